@@ -1,0 +1,289 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names the part it pins. A plausible slip anywhere in the oracle
+(a dropped bias, a swapped gate/up half, a wrong scale index, a transposed
+operand, softmax over the wrong set, an unstable permutation) fails one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codecs, oracle
+from sparse_moe_layer_fp32_amd import inputs as gen
+from tests import handworked
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------ P1: e4m3 decode
+def test_e4m3_decode_format_points():
+    fx = json.load(open(os.path.join(GOLD, "e4m3_points.json")))
+    for code, val in fx["points"].items():
+        got = codecs.E4M3_TABLE[int(code, 16)]
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    for code in fx["nan_codes"]:
+        assert np.isnan(codecs.E4M3_TABLE[int(code, 16)])
+    assert np.sum(np.isnan(codecs.E4M3_TABLE)) == 2
+
+
+def test_e4m3_decode_matches_torch_float8():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(codecs.E4M3_TABLE, ref)
+
+
+# ------------------------------------------------------------------ P2: RNE encoder
+def _brute_encode(v):
+    """Nearest finite e4m3 value by exhaustive search; ties to the even code."""
+    finite = [c for c in range(256) if not np.isnan(codecs.E4M3_TABLE[c])]
+    best = None
+    for c in finite:
+        err = abs(codecs.E4M3_TABLE[c] - v)
+        key = (err, c & 1)                      # tie -> even mantissa (lowest code bit 0)
+        if best is None or key < best[0]:
+            best = (key, c)
+    c = best[1]
+    if codecs.E4M3_TABLE[c] == 0:               # keep the sign of zero
+        c = 0x80 if math.copysign(1, v) < 0 else 0x00
+    return c
+
+
+def test_e4m3_encoder_exhaustive_midpoints():
+    pos = codecs.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    pts = np.concatenate([pos, mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+                          np.nextafter(mids.astype(np.float32), np.float32(1e9)), [448.0]])
+    pts = np.concatenate([pts, -pts]).astype(np.float32)
+    got = codecs.e4m3_encode_rne(pts)
+    want = np.array([_brute_encode(float(v)) for v in pts], np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_e4m3_encoder_random_vs_brute_and_torch():
+    rng = np.random.default_rng(5)
+    v = np.concatenate([rng.uniform(-448, 448, 2000), rng.normal(0, 1e-2, 2000),
+                        rng.normal(0, 1, 2000)]).astype(np.float32)
+    got = codecs.e4m3_encode_rne(v)
+    want = np.array([_brute_encode(float(a)) for a in v[:1500]], np.uint8)
+    np.testing.assert_array_equal(got[:1500], want)
+    tq = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(got, tq)
+
+
+def test_e4m3_encoder_saturates_and_nan():
+    got = codecs.e4m3_encode_rne(np.array([460.0, -1e6, np.nan], np.float32))
+    assert list(got) == [0x7E, 0xFE, 0x7F]
+
+
+# ------------------------------------------------------------------ P3: router logits
+def test_router_logits_vs_python_loops():
+    rng = np.random.default_rng(1)
+    T, d, E = 3, 7, 5
+    x = gen.to_bf16_bits(rng.normal(size=(T, d)).astype(np.float32))
+    W = rng.normal(size=(d, E)).astype(np.float32)
+    b = rng.normal(size=E).astype(np.float32)
+    got = oracle.router_logits(x, W, b)
+    xf = gen.bf16_bits_to_f32(x)
+    for t in range(T):
+        for e in range(E):
+            s = math.fsum(float(xf[t, i]) * float(W[i, e]) for i in range(d)) + float(b[e])
+            assert abs(got[t, e] - s) <= 1e-14 * (1 + abs(s))
+
+
+# ------------------------------------------------------------------ P4: top-k
+def test_topk_is_the_k_largest_set_in_descending_order():
+    rng = np.random.default_rng(2)
+    L = rng.normal(size=(200, 12))
+    L[0, :] = 1.0                                # all ties -> lowest indices
+    for k in (1, 3, 12):
+        idx = oracle.topk_select(L, k)
+        for t in range(L.shape[0]):
+            S = set(idx[t].tolist())
+            rest = [e for e in range(12) if e not in S]
+            assert len(S) == k
+            if rest:
+                assert min(L[t, list(S)]) >= max(L[t, rest])
+            assert all(L[t, idx[t, j]] >= L[t, idx[t, j + 1]] for j in range(k - 1))
+        assert list(idx[0]) == list(range(k))
+
+
+# ------------------------------------------------------------------ P5: gate weights
+def test_gate_weights_closed_forms():
+    rng = np.random.default_rng(3)
+    L = rng.normal(scale=3, size=(100, 8))
+    w1 = oracle.gate_weights(L, oracle.topk_select(L, 1))
+    assert np.all(w1 == 1.0)
+    idx2 = oracle.topk_select(L, 2)
+    w2 = oracle.gate_weights(L, idx2)
+    l1 = np.take_along_axis(L, idx2, 1)
+    logistic = 1.0 / (1.0 + np.exp(l1[:, 1] - l1[:, 0]))
+    np.testing.assert_allclose(w2[:, 0], logistic, rtol=1e-14)
+    idx4 = oracle.topk_select(L, 4)
+    w4 = oracle.gate_weights(L, idx4)
+    assert np.max(np.abs(w4.sum(1) - 1)) <= 1e-15
+    assert np.all(np.diff(w4, axis=1) <= 0)       # ordered like the logits
+    # softmax over the selected logits only: shifting an unselected logit changes nothing
+    L2 = L.copy()
+    for t in range(100):
+        e = [x for x in range(8) if x not in idx4[t]][0]
+        L2[t, e] -= 5.0
+    np.testing.assert_array_equal(oracle.gate_weights(L2, idx4), w4)
+
+
+# ------------------------------------------------------------------ P6: permutation
+@pytest.mark.parametrize("T,E,k", [(1, 4, 2), (37, 8, 3), (300, 64, 8), (5, 3, 3)])
+def test_permutation_invariants(T, E, k):
+    rng = np.random.default_rng(T * E + k)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    counts, offsets, row_of, row_token = oracle.permutation(idx, E)
+    np.testing.assert_array_equal(counts, np.bincount(idx.ravel(), minlength=E))
+    assert offsets[0] == 0 and np.all(np.diff(offsets) == counts) and offsets[-1] == T * k
+    assert sorted(row_of.ravel().tolist()) == list(range(T * k))     # bijection
+    for t in range(T):
+        for j in range(k):
+            r = row_of[t, j]
+            e = idx[t, j]
+            assert offsets[e] <= r < offsets[e + 1]
+            assert row_token[r] == t
+    for e in range(E):                                                 # stable in token order
+        toks = row_token[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(toks) > 0)
+
+
+# ------------------------------------------------------------------ P7: activation quantisation
+def test_quantize_groups_properties():
+    rng = np.random.default_rng(4)
+    v = (rng.normal(size=(40, 512)) * rng.uniform(0.01, 10, size=(40, 1))).astype(np.float32)
+    v[3, 128:256] = 0.0                                  # an all-zero group
+    q, s = oracle.quantize_groups(v)
+    assert s.dtype == np.float32 and s.shape == (40, 4)
+    assert s[3, 1] == 1.0 and np.all(q[3, 128:256] == 0)
+    vals = codecs.e4m3_decode(q)
+    assert np.all(np.abs(vals) <= 448)
+    g = v.reshape(40, 4, 128)
+    am = np.abs(g).argmax(axis=2)
+    for r in range(40):
+        for c in range(4):
+            if r == 3 and c == 1:
+                continue
+            a = g[r, c, am[r, c]]
+            assert vals.reshape(40, 4, 128)[r, c, am[r, c]] == math.copysign(448, a)
+    deq = oracle.dequant_groups(q, s)
+    # error at most half an e4m3 spacing (relative 2^-4 for normals, 2^-10 * s absolute below)
+    err = np.abs(deq - v)
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, np.repeat(s, 128, axis=1) * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-6))
+    q2, s2 = oracle.quantize_groups(deq.astype(np.float32))
+    np.testing.assert_array_equal(codecs.e4m3_decode(q2) * np.repeat(s2, 128, 1), deq)
+
+
+def test_quantize_groups_vs_torch_cast():
+    """Special case reducing to a library routine: scale by fl32(amax/448), then
+    PyTorch's float8_e4m3fn cast (round-to-nearest-even)."""
+    rng = np.random.default_rng(6)
+    v = rng.normal(size=(64, 384)).astype(np.float32)
+    q, s = oracle.quantize_groups(v)
+    t = torch.from_numpy(v).view(64, 3, 128)
+    ts = t.abs().amax(dim=2, keepdim=True) / 448.0
+    tq = (t / ts).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).reshape(64, 384)
+    np.testing.assert_array_equal(q, tq.numpy())
+    np.testing.assert_array_equal(s, ts.squeeze(2).numpy())
+
+
+# ------------------------------------------------------------------ P8: k=1, E=1 -> dense biased SwiGLU MLP
+def _torch_quant(v32):
+    n, K = v32.shape
+    g = v32.view(n, K // 128, 128)
+    am = g.abs().amax(dim=2, keepdim=True)
+    s = torch.where(am > 0, am / 448.0, torch.ones_like(am))
+    q = (g / s).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q * s.double()).view(n, K)
+
+
+def _torch_weight(codes, scales):
+    K, N = codes.shape
+    w = torch.from_numpy(codes).view(torch.float8_e4m3fn).double()
+    s = torch.from_numpy(scales).double().repeat_interleave(128, 0).repeat_interleave(128, 1)
+    return w * s
+
+
+def test_single_expert_reduces_to_dense_swiglu_mlp():
+    layer = gen.custom_layer(256, 384, 1, 1, d_real=200, layer_id=201)
+    inp = gen.make_inputs(layer, T=24)
+    res = oracle.forward(inp)
+    bf = lambda b: torch.from_numpy(gen.bf16_bits_to_f32(b)).double()
+    x = bf(inp["x"]).float()
+    f = inp["f"]
+    P = _torch_quant(x) @ _torch_weight(inp["W_gateup"][0], inp["S_gateup"][0]) + bf(inp["b_gateup"][0])
+    h = torch.nn.functional.silu(P[:, :f]) * P[:, f:]
+    dense = _torch_quant(h.float()) @ _torch_weight(inp["W_down"][0], inp["S_down"][0]) + bf(inp["b_down"][0])
+    np.testing.assert_allclose(res["out64"], dense.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P9: sparse routing vs all-experts brute force
+@pytest.mark.parametrize("T,d,f,E,k", [(8, 128, 128, 4, 2), (64, 256, 256, 8, 2), (9, 256, 128, 6, 6)])
+def test_sparse_block_equals_all_experts_brute_force(T, d, f, E, k):
+    layer = gen.custom_layer(d, f, E, k, layer_id=300 + E)
+    inp = gen.make_inputs(layer, T=T)
+    res = oracle.forward(inp)
+    xf = gen.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    L = xf @ inp["W_router"].astype(np.float64) + inp["b_router"].astype(np.float64)
+    xdeq = oracle.dequant_groups(*oracle.quantize_groups(xf.astype(np.float32)))
+    out = np.zeros((T, d))
+    for t in range(T):
+        for e in range(E):
+            rank = sum(1 for e2 in range(E) if L[t, e2] > L[t, e] or (L[t, e2] == L[t, e] and e2 < e))
+            if rank >= k:
+                continue
+            sel = [e2 for e2 in range(E)
+                   if sum(1 for e3 in range(E) if L[t, e3] > L[t, e2] or (L[t, e3] == L[t, e2] and e3 < e2)) < k]
+            w = math.exp(L[t, e]) / sum(math.exp(L[t, e2]) for e2 in sel)
+            Y = oracle.expert_mlp(xdeq[t:t + 1], inp["W_gateup"][e], inp["S_gateup"][e], inp["b_gateup"][e],
+                                  inp["W_down"][e], inp["S_down"][e], inp["b_down"][e])
+            out[t] += w * Y[0]
+    np.testing.assert_allclose(res["out64"], out, rtol=1e-12, atol=1e-12 * np.abs(out).max())
+
+
+# ------------------------------------------------------------------ P10: padding
+def test_padded_columns_are_exactly_zero():
+    layer = gen.custom_layer(384, 256, 6, 2, d_real=300, layer_id=401)
+    inp = gen.make_inputs(layer, T=20)
+    res = oracle.forward(inp)
+    assert np.all(res["out64"][:, 300:] == 0.0)
+    assert np.abs(res["out64"][:, :300]).min() > 0
+
+
+# ------------------------------------------------------------------ P11: token independence
+def test_token_independence():
+    inp = gen.make_inputs("c0")
+    full = oracle.forward(inp)["out64"]
+    sub = [5, 0, 63, 17]
+    part = oracle.forward(inp, tokens=sub)["out64"]
+    np.testing.assert_allclose(part, full[sub], rtol=1e-13, atol=1e-13)
+    perm = np.random.default_rng(7).permutation(inp["T"])
+    inp2 = dict(inp, x=inp["x"][perm])
+    np.testing.assert_allclose(oracle.forward(inp2)["out64"], full[perm], rtol=1e-13, atol=1e-13)
+    inp3 = dict(inp, x=inp["x"][:10], T=10)
+    np.testing.assert_allclose(oracle.forward(inp3)["out64"], full[:10], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ hand-worked block (closed forms)
+@pytest.mark.parametrize("k", [1, 2])
+def test_handworked_block(k):
+    inp = handworked.build(k)
+    res = oracle.forward(inp)
+    want = handworked.expected(k)
+    assert list(res["idx"][0]) == ([0] if k == 1 else [0, 1])
+    np.testing.assert_allclose(res["out64"][0], want, rtol=0, atol=1e-6 * np.abs(want).max())
+    assert res["xq"][0, 0] == 0x7E and res["xq"][0, 1] == 0x76 and res["xs"][0, 0] == 2.0 ** -7
+
+
+# ------------------------------------------------------------------ SwiGLU form
+def test_silu_vs_torch():
+    z = np.linspace(-60, 60, 2001)
+    np.testing.assert_allclose(oracle.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
+                               rtol=1e-15, atol=1e-300)
