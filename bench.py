@@ -1,0 +1,190 @@
+"""Benchmark of the sparse MoE block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1]
+
+A step is one whole forward (router + top-k + softmax + x quantisation,
+routing scan and placement, gate/up grouped FP8 GEMM with SwiGLU and h
+quantisation, down grouped FP8 GEMM, weighted combine) over one batch of
+seeded synthetic input already resident in HBM.  The default workload is the
+decode-shaped gpt-oss-20b-like layer (T=64 tokens, d=2944, f=2944, E=32,
+k=4).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
+GEMM (its duration measured with HIP events inside the timed region, on the
+stream it runs on) and the CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sparse_moe_layer_fp32_amd as moe  # noqa: E402
+from sparse_moe_layer_fp32_amd import inputs as gen  # noqa: E402
+
+METRIC = "MoE-layer tokens/s + % of FP8 MFMA peak (prefill) / % HBM BW (decode)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gateup_algorithmic(inp, counts):
+    """Algorithmic HBM bytes and FP8 flops of one gate/up GEMM launch.
+
+    Bytes: every touched expert's gate/up weights (e4m3 codes, fp32 block
+    scales, bf16 bias) once, the quantised activations of every token once
+    (codes + scales), and the h codes + scales of every routed row once.
+    Flops: 2 * rows * d * 2f."""
+    T, d, f, k = inp["T"], inp["d"], inp["f"], inp["k"]
+    R = T * k
+    touched = int(np.count_nonzero(counts))
+    w = touched * (d * 2 * f + 4 * (d // 128) * (2 * f // 128) + 2 * 2 * f)
+    a = T * d + 4 * T * (d // 128)
+    h = R * f + 4 * R * (f // 128)
+    return dict(bytes=w + a + h, flops=2.0 * R * d * 2 * f, touched=touched)
+
+
+def down_algorithmic(inp, counts):
+    T, d, f, k = inp["T"], inp["d"], inp["f"], inp["k"]
+    R = T * k
+    touched = int(np.count_nonzero(counts))
+    w = touched * (f * d + 4 * (f // 128) * (d // 128) + 2 * d)
+    return dict(bytes=w + R * f + 4 * R * (f // 128) + 4 * R * d, flops=2.0 * R * f * d)
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the workload's tokens."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import oracle as orc
+    T = inp["T"]
+    n = min(T, 64)
+    toks = np.arange(n)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        orc.forward(inp, tokens=toks)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s or reps >= 3:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{reps} x oracle.forward on the first {n} of {T} tokens (routing of all "
+                      f"{T} tokens, expert math of the sample, fp64 NumPy; {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS))
+    ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the MoE block here is "
+              "built for a single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = gen.CONFIGS[args.workload]
+    log(f"[bench] generating {cfg.name} (T={cfg.T}, d={cfg.layer.d}, f={cfg.layer.f}, "
+        f"E={cfg.layer.E}, k={cfg.layer.k})")
+    inp = gen.make_inputs(cfg.name)
+    dev = torch.device("cuda:0")
+    p = moe.device_inputs(inp, dev)
+    T, d, f, E, k = inp["T"], inp["d"], inp["f"], inp["E"], inp["k"]
+    w_args = (p["W_router"], p["b_router"], k, p["W_gateup"], p["S_gateup"], p["b_gateup"],
+              p["W_down"], p["S_down"], p["b_down"])
+    ws = torch.empty(moe.workspace_bytes(T, d, f, E, k), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    x = p["x"]
+
+    dbg = moe.forward_debug(x, *w_args, path=args.path)
+    torch.cuda.synchronize()
+    counts = np.diff(dbg["offsets"].cpu().numpy())
+    del dbg
+    ga = gateup_algorithmic(inp, counts)
+    da = down_algorithmic(inp, counts)
+
+    def step(ev=None):
+        moe.forward_stages("router", "place", x, *w_args, out, ws, path=args.path)
+        if ev is not None:
+            ev[0].record()
+        moe.forward_stages("gateup", "gateup", x, *w_args, out, ws, path=args.path)
+        if ev is not None:
+            ev[1].record()
+        moe.forward_stages("down", "down", x, *w_args, out, ws, path=args.path)
+        if ev is not None:
+            ev[2].record()
+        moe.forward_stages("combine", "combine", x, *w_args, out, ws, path=args.path)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms = total_ms / args.steps
+    tok_s = T / (ms * 1e-3)
+
+    decode = (args.path == "decode") or (args.path == "auto" and T * k <= 32 * E)
+    if decode:
+        ach = ga["bytes"] / (gate_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = ga["flops"] / (gate_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "grouped_gemm_kernel (gate/up + bias + SwiGLU + h quantisation)"
+    roof["avg_ms"] = round(gate_ms, 5)
+    roof["algorithmic_bytes"] = ga["bytes"]
+    roof["algorithmic_flops"] = ga["flops"]
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.layer.name} {cfg.role} T={T} d={d} "
+                               f"(real {inp['d_real']}) f={f} E={E} k={k}",
+                   "T": T, "d": d, "f": f, "E": E, "k": k, "path": args.path,
+                   "experts_touched": ga["touched"]},
+        "roofline": roof,
+        "stages_ms": {"gateup": round(gate_ms, 5), "down": round(down_ms, 5),
+                      "rest": round(ms - gate_ms - down_ms, 5)},
+        "down_gemm": {"achieved_GBs": round(da["bytes"] / (down_ms * 1e-3) / 1e9, 1),
+                      "achieved_TFLOPs": round(da["flops"] / (down_ms * 1e-3) / 1e12, 1)},
+        "step_tflops": round((ga["flops"] + da["flops"]) / (ms * 1e-3) / 1e12, 2),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,224 @@
+"""Sparse MoE block forward on one MI355X (gfx950): Python binding of the C ABI.
+
+The block (router with bias, top-k, softmax over the selected logits, FP8
+128x128 block-scaled SwiGLU experts with biases, weighted combine) runs in
+HIP kernels of ``libsparse_moe.so``; this module only checks tensors and
+passes device pointers and the current HIP stream (see ``include/moe.h``).
+There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_moe.so")
+
+PATHS = {"auto": 0, "prefill": 1, "decode": 2}
+BLOCK = 128
+MAX_EXPERTS = 256
+MAX_TOPK = 8
+
+SYMBOLS = ("moe_workspace_bytes", "moe_forward", "moe_forward_ex", "moe_forward_stages",
+           "moe_forward_debug", "moe_status_string")
+STAGES = {"router": 0, "scan": 1, "place": 2, "gateup": 3, "down": 4, "combine": 5}
+
+
+class MoeError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"moe status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, U, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    L.moe_workspace_bytes.restype = S
+    L.moe_workspace_bytes.argtypes = [I, I, I, I, I]
+    fwd = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, P, S]
+    L.moe_forward.restype = I
+    L.moe_forward.argtypes = fwd + [P]
+    L.moe_forward_ex.restype = I
+    L.moe_forward_ex.argtypes = fwd + [U, P]
+    L.moe_forward_stages.restype = I
+    L.moe_forward_stages.argtypes = fwd + [U, I, I, P]
+    L.moe_forward_debug.restype = I
+    L.moe_forward_debug.argtypes = fwd + [U, P] + [P] * 10
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_status_string.argtypes = [I]
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, status_string(status))
+
+
+def workspace_bytes(T: int, d: int, f: int, E: int, k: int) -> int:
+    return int(lib().moe_workspace_bytes(T, d, f, E, k))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(t, name, shape, nbytes, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.element_size() != nbytes:
+        raise TypeError(f"{name} has {t.element_size()}-byte elements, expected {nbytes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device, stream, *tensors):
+    """Raw handle of ``stream`` (default: the current stream).  Tensors allocated
+    here on the current stream are recorded on a different target stream so
+    the caching allocator does not reuse them before that stream is done."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    if stream is not None:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
+          out, workspace):
+    T, d = x.shape
+    E = W_router.shape[1]
+    f = W_down.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    _expect(x, "x", (T, d), 2, dev)
+    _expect(W_router, "W_router", (d, E), 4, dev)
+    _expect(b_router, "b_router", (E,), 4, dev)
+    _expect(W_gateup, "W_gateup", (E, d, 2 * f), 1, dev)
+    _expect(S_gateup, "S_gateup", (E, d // BLOCK, 2 * f // BLOCK), 4, dev)
+    _expect(b_gateup, "b_gateup", (E, 2 * f), 2, dev)
+    _expect(W_down, "W_down", (E, f, d), 1, dev)
+    _expect(S_down, "S_down", (E, f // BLOCK, d // BLOCK), 4, dev)
+    _expect(b_down, "b_down", (E, d), 2, dev)
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", (T, d), 2, dev)
+    need = workspace_bytes(T, d, f, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    args = [_ptr(x), _ptr(W_router), _ptr(b_router), int(k), _ptr(W_gateup), _ptr(S_gateup),
+            _ptr(b_gateup), _ptr(W_down), _ptr(S_down), _ptr(b_down), _ptr(out), T, d, f, E,
+            _ptr(workspace), workspace.numel() * workspace.element_size()]
+    return args, out, workspace, (T, d, f, E)
+
+
+def forward(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
+            out=None, workspace=None, path="auto", stream=None):
+    """bf16 [T, d] output of the block; every argument is a device tensor laid
+    out as ``include/moe.h`` states (bf16 tensors may be any 2-byte dtype,
+    e4m3 tensors any 1-byte dtype)."""
+    args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
+                             S_down, b_down, out, workspace)
+    _check(lib().moe_forward_ex(*args, PATHS[path], _stream(x.device, stream, ws, out)))
+    return out
+
+
+def forward_stages(first, last, x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
+                   S_down, b_down, out, workspace, path="auto", stream=None):
+    """Stages ``first``..``last`` (names of ``STAGES`` or ints) of ``forward`` on a
+    caller-kept workspace; all stages must run in order on that workspace."""
+    first = STAGES.get(first, first)
+    last = STAGES.get(last, last)
+    args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
+                             S_down, b_down, out, workspace)
+    _check(lib().moe_forward_stages(*args, PATHS[path], int(first), int(last),
+                                    _stream(x.device, stream, ws, out)))
+    return out
+
+
+def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
+                  path="auto", stream=None):
+    """``forward`` plus the intermediates (routing, permutation, quantised
+    activations and h, per-row expert outputs) as a dict of device tensors."""
+    T, d = x.shape
+    E, f = W_router.shape[1], W_down.shape[1]
+    R = T * k
+    dev = x.device
+    i32, f32, u8 = torch.int32, torch.float32, torch.uint8
+    dbg = dict(topk_idx=torch.empty((T, k), dtype=i32, device=dev),
+               topk_w=torch.empty((T, k), dtype=f32, device=dev),
+               offsets=torch.empty(E + 1, dtype=i32, device=dev),
+               row_token=torch.empty(R, dtype=i32, device=dev),
+               row_of=torch.empty((T, k), dtype=i32, device=dev),
+               xq=torch.empty((T, d), dtype=u8, device=dev),
+               xs=torch.empty((T, d // BLOCK), dtype=f32, device=dev),
+               hq=torch.empty((R, f), dtype=u8, device=dev),
+               hs=torch.empty((R, f // BLOCK), dtype=f32, device=dev),
+               y=torch.empty((R, d), dtype=f32, device=dev))
+    args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
+                             S_down, b_down, None, None)
+    order = ["topk_idx", "topk_w", "offsets", "row_token", "row_of", "xq", "xs", "hq", "hs", "y"]
+    _check(lib().moe_forward_debug(*args, PATHS[path], _stream(dev, stream, ws, out, *dbg.values()),
+                                   *[_ptr(dbg[n]) for n in order]))
+    dbg["out"] = out
+    return dbg
+
+
+def device_inputs(inp: dict, device="cuda"):
+    """Host arrays of ``inputs.make_inputs`` -> device tensors in the C-ABI dtypes."""
+    import numpy as np
+
+    def t(a, dtype):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).to(device)
+
+    return dict(
+        x=t(inp["x"], torch.bfloat16), W_router=t(inp["W_router"], torch.float32),
+        b_router=t(inp["b_router"], torch.float32), k=int(inp["k"]),
+        W_gateup=t(inp["W_gateup"], torch.uint8), S_gateup=t(inp["S_gateup"], torch.float32),
+        b_gateup=t(inp["b_gateup"], torch.bfloat16), W_down=t(inp["W_down"], torch.uint8),
+        S_down=t(inp["S_down"], torch.float32), b_down=t(inp["b_down"], torch.bfloat16))
+
+
+class MoeBlock:
+    """Device-resident layer parameters plus a reusable workspace."""
+
+    def __init__(self, params: dict):
+        self.p = {k: v for k, v in params.items() if k != "x"}
+        self._ws = None
+
+    def workspace(self, T):
+        p = self.p
+        need = workspace_bytes(T, p["W_router"].shape[0], p["W_down"].shape[1],
+                               p["W_router"].shape[1], p["k"])
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=p["W_router"].device)
+        return self._ws
+
+    def __call__(self, x, out=None, path="auto", stream=None):
+        p = self.p
+        return forward(x, p["W_router"], p["b_router"], p["k"], p["W_gateup"], p["S_gateup"],
+                       p["b_gateup"], p["W_down"], p["S_down"], p["b_down"], out=out,
+                       workspace=self.workspace(x.shape[0]), path=path, stream=stream)

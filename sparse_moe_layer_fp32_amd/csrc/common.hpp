@@ -1,0 +1,84 @@
+// Device helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 128;      // quantisation group width and weight block edge
+constexpr float kFp8Max = 448.0f;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ----------------------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __uint_as_float(static_cast<uint32_t>(u) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ----------------------------------------------------------------------------- e4m3
+// Two fp32 values -> two OCP e4m3 bytes (round to nearest even) in the low half
+// of the result. Callers clamp to +-448 first, so no value saturates here.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+
+__device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
+}
+
+// ----------------------------------------------------------------------------- wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// max over the 16 lanes that share lane/16 (the 16 columns of one MFMA row group)
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// ----------------------------------------------------------------------------- byte transpose
+// Four dwords r0..r3 (byte b of r_i = element (i, b)) -> c0..c3 with byte i of
+// c_b = element (i, b).  v_perm_b32 picks result bytes from {S0:S1}; selector
+// values 0-3 address S1, 4-7 address S0.
+__device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t r2, uint32_t r3,
+                                             uint32_t& c0, uint32_t& c1, uint32_t& c2,
+                                             uint32_t& c3) {
+  uint32_t t0 = __builtin_amdgcn_perm(r1, r0, 0x06020400u);  // r0.0 r1.0 r0.2 r1.2
+  uint32_t t1 = __builtin_amdgcn_perm(r1, r0, 0x07030501u);  // r0.1 r1.1 r0.3 r1.3
+  uint32_t t2 = __builtin_amdgcn_perm(r3, r2, 0x06020400u);  // r2.0 r3.0 r2.2 r3.2
+  uint32_t t3 = __builtin_amdgcn_perm(r3, r2, 0x07030501u);  // r2.1 r3.1 r2.3 r3.3
+  c0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  c1 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  c2 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  c3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
+// ----------------------------------------------------------------------------- MFMA
+// D(16x16 fp32) = A(16x128 e4m3) * B(128x16 e4m3) + C.  Lane l holds 32 bytes
+// of A row l%16 and of B column l%16 (the same K slots for both), and
+// returns rows 4*(l/16)+i, i<4, of column l%16.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------- misc
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

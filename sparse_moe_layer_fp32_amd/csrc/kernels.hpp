@@ -1,0 +1,59 @@
+// Host-side launchers of the MoE kernels (one translation unit per kernel family).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int RT_TT = 16;     // tokens per router / placement workgroup
+constexpr int kMaxTopK = 8;
+
+// GEMM tile shapes.  "Gated" is gate/up + bias + SwiGLU + h quantisation,
+// "plain" is down + bias.  Prefill tiles are MFMA-bound, decode tiles stream
+// the weights with few rows.
+struct GemmShape {
+  int bm;       // rows per tile
+  int bnp;      // B columns per tile (gate+up columns for the gated kernel)
+};
+constexpr GemmShape kGatedPrefill{128, 256};
+constexpr GemmShape kGatedDecode{32, 256};
+constexpr GemmShape kPlainPrefill{128, 256};
+constexpr GemmShape kPlainDecode{32, 128};
+
+struct GemmArgs {
+  const uint8_t* A;            // e4m3 activations: x codes [T,K] (gated) or h codes [R,K] (plain)
+  const float* As;             // their scales [rows, K/128]
+  const int32_t* row_token;    // gated: token of each permuted row
+  const uint8_t* B;            // e4m3 weights [E, K, N]
+  const float* Bs;             // block scales [E, K/128, N/128]
+  const uint16_t* bias;        // bf16 [E, N]
+  const int32_t* counts;       // rows per expert [E]
+  const int32_t* offsets;      // first row per expert [E+1]
+  const int32_t* tile_off;     // first tile per expert [E+1] (this kernel's tiling)
+  int K, N, f, n_tiles, E;
+  uint8_t* Hq;                 // gated outputs: h codes [R, f] and scales [R, f/128]
+  float* Hs;
+  float* Y;                    // plain output [R, N]
+};
+
+hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
+                         int k, int32_t* topk_idx, float* topk_w, int32_t* hist, uint8_t* xq,
+                         float* xs, hipStream_t stream);
+
+hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
+                             int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
+                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream);
+
+hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
+                              int k, int32_t* row_of, int32_t* row_token, hipStream_t stream);
+
+hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
+                          int k, uint16_t* out, hipStream_t stream);
+
+// max_tiles bounds the tile count so the grid covers every tile.
+hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream);
+hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream);
+
+}  // namespace moe

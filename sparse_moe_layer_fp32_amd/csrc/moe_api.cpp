@@ -1,0 +1,258 @@
+// C ABI of the MoE block forward: argument checks, workspace carving and the
+// launch sequence on the caller's stream.  No allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.hpp"
+#include "moe.h"
+
+namespace {
+
+using moe::ceil_div;
+
+constexpr int64_t kMaxRows = int64_t(1) << 28;  // T*k bound (row indices are int32)
+
+struct Layout {
+  size_t topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, row_of,
+      row_token, xq, xs, hq, hs, y, total;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
+  const int64_t R = T * k, NT = ceil_div((int)T, moe::RT_TT);
+  Layout l{};
+  size_t o = 0;
+  auto put = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  l.topk_idx = put(4 * R);
+  l.topk_w = put(4 * R);
+  l.hist = put(4 * NT * E);
+  l.counts = put(4 * E);
+  l.offsets = put(4 * (E + 1));
+  l.tile_base = put(4 * NT * E);
+  l.tile_off0 = put(4 * (E + 1));
+  l.tile_off1 = put(4 * (E + 1));
+  l.row_of = put(4 * R);
+  l.row_token = put(4 * R);
+  l.xq = put(T * d);
+  l.xs = put(4 * T * (d / moe::kBlock));
+  l.hq = put(R * f);
+  l.hs = put(4 * R * (f / moe::kBlock));
+  l.y = put(4 * R * d);
+  l.total = o;
+  return l;
+}
+
+moe_status check_sizes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k) {
+  if (T < 0 || d <= 0 || f <= 0 || E < 1 || d % MOE_BLOCK || f % MOE_BLOCK) return MOE_ERR_SHAPE;
+  if (k < 1 || k > E || k > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)T * k > kMaxRows || d > (1 << 20) || f > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k) {
+  if (check_sizes(T, d, f, E, k) != MOE_OK) return 0;
+  return make_layout(T, d, f, E, k).total;
+}
+
+const char* moe_status_string(int32_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid shape (T < 0, or d/f not a positive multiple of 128, or E < 1)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported sizes (k outside [1, min(E, 8)], E > 256, or too many rows)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MOE_ERR_HIP: return "a HIP kernel launch failed";
+    case MOE_ERR_FLAGS: return "unknown flags";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_forward_stages(const void* x, const float* W_router, const float* b_router,
+                              int32_t k, const uint8_t* W_gateup, const float* S_gateup,
+                              const void* b_gateup, const uint8_t* W_down, const float* S_down,
+                              const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
+                              int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
+                              int32_t first_stage, int32_t last_stage, void* stream_) {
+  const moe_status sz = check_sizes(T, d, f, E, k);
+  if (sz != MOE_OK) return sz;
+  if (flags > MOE_PATH_DECODE) return MOE_ERR_FLAGS;
+  if (first_stage < 0 || last_stage >= MOE_NUM_STAGES || first_stage > last_stage)
+    return MOE_ERR_FLAGS;
+  if (T == 0) return MOE_OK;
+  const void* ptrs[] = {x, W_router, b_router, W_gateup, S_gateup, b_gateup,
+                        W_down, S_down, b_down, out, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr) return MOE_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  const Layout l = make_layout(T, d, f, E, k);
+  if (workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  auto at = [&](size_t off) { return ws + off; };
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(at(l.topk_idx));
+  float* topk_w = reinterpret_cast<float*>(at(l.topk_w));
+  int32_t* hist = reinterpret_cast<int32_t*>(at(l.hist));
+  int32_t* counts = reinterpret_cast<int32_t*>(at(l.counts));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(l.offsets));
+  int32_t* tile_base = reinterpret_cast<int32_t*>(at(l.tile_base));
+  int32_t* tile_off0 = reinterpret_cast<int32_t*>(at(l.tile_off0));
+  int32_t* tile_off1 = reinterpret_cast<int32_t*>(at(l.tile_off1));
+  int32_t* row_of = reinterpret_cast<int32_t*>(at(l.row_of));
+  int32_t* row_token = reinterpret_cast<int32_t*>(at(l.row_token));
+  uint8_t* xq = at(l.xq);
+  float* xs = reinterpret_cast<float*>(at(l.xs));
+  uint8_t* hq = at(l.hq);
+  float* hs = reinterpret_cast<float*>(at(l.hs));
+  float* y = reinterpret_cast<float*>(at(l.y));
+
+  const int R = T * k;
+  const int NT = ceil_div(T, moe::RT_TT);
+  bool decode;
+  if (flags == MOE_PATH_AUTO) decode = (int64_t)R <= 32 * (int64_t)E;
+  else decode = flags == MOE_PATH_DECODE;
+  const moe::GemmShape gs = decode ? moe::kGatedDecode : moe::kGatedPrefill;
+  const moe::GemmShape ps = decode ? moe::kPlainDecode : moe::kPlainPrefill;
+  const int nt_g = f / moe::kBlock;
+  const int nt_p = ceil_div(d, ps.bnp);
+  const int nz = E < R ? E : R;  // experts that can hold rows
+  const int max_g = (ceil_div(R, gs.bm) + nz) * nt_g;
+  const int max_p = (ceil_div(R, ps.bm) + nz) * nt_p;
+
+  for (int stage = first_stage; stage <= last_stage; ++stage) {
+    hipError_t err = hipSuccess;
+    switch (stage) {
+      case MOE_STAGE_ROUTER:
+        err = moe::launch_router(static_cast<const uint16_t*>(x), W_router, b_router, T, d, E, k,
+                                 topk_idx, topk_w, hist, xq, xs, stream);
+        break;
+      case MOE_STAGE_SCAN:
+        err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
+                                     tile_base, tile_off0, tile_off1, stream);
+        break;
+      case MOE_STAGE_PLACE:
+        err = moe::launch_route_place(topk_idx, tile_base, T, E, k, row_of, row_token, stream);
+        break;
+      case MOE_STAGE_GATEUP: {
+        moe::GemmArgs g{};
+        g.A = xq;
+        g.As = xs;
+        g.row_token = row_token;
+        g.B = W_gateup;
+        g.Bs = S_gateup;
+        g.bias = static_cast<const uint16_t*>(b_gateup);
+        g.counts = counts;
+        g.offsets = offsets;
+        g.tile_off = tile_off0;
+        g.K = d;
+        g.N = 2 * f;
+        g.f = f;
+        g.n_tiles = nt_g;
+        g.E = E;
+        g.Hq = hq;
+        g.Hs = hs;
+        err = moe::launch_gemm_gated(g, decode, max_g, stream);
+        break;
+      }
+      case MOE_STAGE_DOWN: {
+        moe::GemmArgs p{};
+        p.A = hq;
+        p.As = hs;
+        p.B = W_down;
+        p.Bs = S_down;
+        p.bias = static_cast<const uint16_t*>(b_down);
+        p.counts = counts;
+        p.offsets = offsets;
+        p.tile_off = tile_off1;
+        p.K = f;
+        p.N = d;
+        p.f = f;
+        p.n_tiles = nt_p;
+        p.E = E;
+        p.Y = y;
+        err = moe::launch_gemm_plain(p, decode, max_p, stream);
+        break;
+      }
+      case MOE_STAGE_COMBINE:
+        err = moe::launch_combine(y, row_of, topk_w, T, d, k, static_cast<uint16_t*>(out), stream);
+        break;
+    }
+    if (err != hipSuccess) return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_router, int32_t k,
+                          const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
+                          const uint8_t* W_down, const float* S_down, const void* b_down,
+                          void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
+  return moe_forward_stages(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
+                            b_down, out, T, d, f, E, workspace, workspace_bytes, flags, 0,
+                            MOE_NUM_STAGES - 1, stream);
+}
+
+moe_status moe_forward(const void* x, const float* W_router, const float* b_router, int32_t k,
+                       const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
+                       const uint8_t* W_down, const float* S_down, const void* b_down, void* out,
+                       int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return moe_forward_ex(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
+                        b_down, out, T, d, f, E, workspace, workspace_bytes, MOE_PATH_AUTO, stream);
+}
+
+moe_status moe_forward_debug(const void* x, const float* W_router, const float* b_router,
+                             int32_t k, const uint8_t* W_gateup, const float* S_gateup,
+                             const void* b_gateup, const uint8_t* W_down, const float* S_down,
+                             const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
+                             int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream_, int32_t* topk_idx, float* topk_w, int32_t* offsets,
+                             int32_t* row_token, int32_t* row_of, uint8_t* xq, float* xs,
+                             uint8_t* hq, float* hs, float* y) {
+  const moe_status st =
+      moe_forward_ex(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
+                     b_down, out, T, d, f, E, workspace, workspace_bytes, flags, stream_);
+  if (st != MOE_OK || T == 0) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const Layout l = make_layout(T, d, f, E, k);
+  const uint8_t* ws = static_cast<const uint8_t*>(workspace);
+  const size_t R = (size_t)T * k;
+  struct Copy {
+    void* dst;
+    size_t off, bytes;
+  } copies[] = {
+      {topk_idx, l.topk_idx, 4 * R},
+      {topk_w, l.topk_w, 4 * R},
+      {offsets, l.offsets, 4 * ((size_t)E + 1)},
+      {row_token, l.row_token, 4 * R},
+      {row_of, l.row_of, 4 * R},
+      {xq, l.xq, (size_t)T * d},
+      {xs, l.xs, 4 * (size_t)T * (d / MOE_BLOCK)},
+      {hq, l.hq, R * f},
+      {hs, l.hs, 4 * R * (f / MOE_BLOCK)},
+      {y, l.y, 4 * R * d},
+  };
+  for (const Copy& c : copies) {
+    if (c.dst == nullptr) continue;
+    if (hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Routing metadata (expert histogram -> prefix scan -> stable permutation and
+// GEMM tile tables) and the weighted combine.
+//
+// "GPT-OSS on day 0", section "MoE": the dispatcher selects the tokens routed
+// to each expert and the combine is a weighted accumulation of the expert
+// outputs.  "Hosting Qwen on Blackwell", section "Expert Parallel": dispatch
+// aggregates the routing information and stages tokens into the buffer the
+// MoE GEMM reads; combine first accumulates locally.  On one GPU that is a
+// counting sort of the (token, slot) pairs by expert, stable in token order,
+// and a gather-sum over the k rows of each token in slot order.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+// Exclusive scan of n <= 256 ints in LDS by wave 0 (4 per lane); returns the total.
+__device__ int wave0_exclusive_scan(int* s, int n) {
+  const int lane = threadIdx.x & 63;
+  int v[4], run = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane * 4 + q;
+    v[q] = i < n ? s[i] : 0;
+    run += v[q];
+  }
+  int incl = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int pre = incl - run;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane * 4 + q;
+    if (i < n) s[i] = pre;
+    pre += v[q];
+  }
+  return __shfl(incl, 63);
+}
+
+// One workgroup.  hist[nt][E] holds the expert counts of every router tile.
+__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist, int nt,
+                                                          int E, int bm0, int ntile0, int bm1,
+                                                          int ntile1, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ tile_base,
+                                                          int32_t* __restrict__ tile_off0,
+                                                          int32_t* __restrict__ tile_off1) {
+  __shared__ int spart[1024];
+  __shared__ int scnt[256], soff[256], st0[256], st1[256];
+  const int tid = threadIdx.x;
+  int EP = 1;
+  while (EP < E) EP <<= 1;
+  const int P = 1024 / EP;               // threads per expert
+  const int e = tid % EP, p = tid / EP;
+  const int ch = ceil_div(nt, P);
+  const int lo = min(nt, p * ch), hi = min(nt, lo + ch);
+  int s = 0;
+  if (e < E)
+    for (int tl = lo; tl < hi; ++tl) s += hist[(size_t)tl * E + e];
+  spart[tid] = s;
+  __syncthreads();
+  if (p == 0 && e < E) {                 // exclusive scan over this expert's chunks
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = spart[q * EP + e];
+      spart[q * EP + e] = run;
+      run += v;
+    }
+    scnt[e] = run;
+  }
+  __syncthreads();
+  if (tid < E) {
+    const int c = scnt[tid];
+    counts[tid] = c;
+    soff[tid] = c;
+    st0[tid] = ceil_div(c, bm0) * ntile0;
+    st1[tid] = ceil_div(c, bm1) * ntile1;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int tot = wave0_exclusive_scan(soff, E);
+    const int t0 = wave0_exclusive_scan(st0, E);
+    const int t1 = wave0_exclusive_scan(st1, E);
+    if (tid == 0) {
+      offsets[E] = tot;
+      tile_off0[E] = t0;
+      tile_off1[E] = t1;
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+    offsets[tid] = soff[tid];
+    tile_off0[tid] = st0[tid];
+    tile_off1[tid] = st1[tid];
+  }
+  if (e < E) {                           // absolute first row of every (tile, expert)
+    int run = soff[e] + spart[tid];
+    for (int tl = lo; tl < hi; ++tl) {
+      tile_base[(size_t)tl * E + e] = run;
+      run += hist[(size_t)tl * E + e];
+    }
+  }
+}
+
+// One workgroup per router tile: rank of every (token, slot) pair among the
+// earlier pairs of the tile with the same expert (a token never picks an
+// expert twice, so this is the token order).
+__global__ __launch_bounds__(128) void route_place_kernel(const int32_t* __restrict__ topk_idx,
+                                                          const int32_t* __restrict__ tile_base,
+                                                          int T, int E, int k,
+                                                          int32_t* __restrict__ row_of,
+                                                          int32_t* __restrict__ row_token) {
+  __shared__ int se[RT_TT * kMaxTopK];
+  const int tl = blockIdx.x, t0 = tl * RT_TT;
+  const int n = min(RT_TT, T - t0) * k;
+  const int p = threadIdx.x;
+  if (p < n) se[p] = topk_idx[(size_t)t0 * k + p];
+  __syncthreads();
+  if (p < n) {
+    const int e = se[p];
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += (se[q] == e);
+    const int row = tile_base[(size_t)tl * E + e] + rank;
+    row_of[(size_t)t0 * k + p] = row;
+    row_token[row] = t0 + p / k;
+  }
+}
+
+// out[t, :] = bf16( sum_j w[t,j] * Y[row_of[t,j], :] ), fp32 in slot order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
+                                                      const int32_t* __restrict__ row_of,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int d, int k, uint16_t* __restrict__ out) {
+  const int t = blockIdx.x;
+  int rows[kMaxTopK];
+  float ws[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
+    ws[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
+  }
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 acc = *reinterpret_cast<const float4*>(Y + (size_t)rows[0] * d + c);
+    acc.x *= ws[0];
+    acc.y *= ws[0];
+    acc.z *= ws[0];
+    acc.w *= ws[0];
+#pragma unroll
+    for (int j = 1; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const float4 y = *reinterpret_cast<const float4*>(Y + (size_t)rows[j] * d + c);
+        acc.x = fmaf(ws[j], y.x, acc.x);
+        acc.y = fmaf(ws[j], y.y, acc.y);
+        acc.z = fmaf(ws[j], y.z, acc.z);
+        acc.w = fmaf(ws[j], y.w, acc.w);
+      }
+    }
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+    *reinterpret_cast<uint2*>(out + (size_t)t * d + c) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
+                             int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
+                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream) {
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, ntiles, E, bm0, nt0,
+                     bm1, nt1, counts, offsets, tile_base, tile_off0, tile_off1);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
+                              int k, int32_t* row_of, int32_t* row_token, hipStream_t stream) {
+  hipLaunchKernelGGL(route_place_kernel, dim3(ceil_div(T, RT_TT)), dim3(128), 0, stream, topk_idx,
+                     tile_base, T, E, k, row_of, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
+                          int k, uint16_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, Y, row_of, topk_w, T, d, k,
+                     out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

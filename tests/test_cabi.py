@@ -1,0 +1,90 @@
+"""The C-ABI library loads, exports what include/moe.h declares, and rejects bad
+arguments on the host before touching the GPU (CPU only: no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_moe_layer_fp32_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(moe.SYMBOLS), names
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS):
+        assert moe.status_string(s) and moe.status_string(s) != "unknown status"
+    assert moe.status_string(-99) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert moe.workspace_bytes(64, 256, 256, 8, 2) > 64 * 256 * (1 + 2 * 4)
+    assert moe.workspace_bytes(64, 200, 256, 8, 2) == 0        # d not a multiple of 128
+    assert moe.workspace_bytes(64, 256, 256, 8, 9) == 0        # k > 8
+    assert moe.workspace_bytes(64, 256, 256, 300, 2) == 0      # E > 256
+    assert moe.workspace_bytes(0, 256, 256, 8, 2) > 0
+    a = moe.workspace_bytes(100, 256, 384, 8, 2)
+    b = moe.workspace_bytes(200, 256, 384, 8, 2)
+    assert b > a
+
+
+# fake, 16-byte aligned device addresses: every case below fails validation
+# before any pointer is used, so nothing is dereferenced or launched
+FAKE = 1 << 20
+
+
+def call(T=64, d=256, f=256, E=8, k=2, ws=None, flags=0, null=None, misalign=None, stages=None):
+    ptrs = [FAKE + 4096 * i for i in range(11)]
+    if null is not None:
+        ptrs[null] = None
+    if misalign is not None:
+        ptrs[misalign] += 4
+    if ws is None:
+        ws = moe.workspace_bytes(T, d, f, E, k)
+    x, Wr, br, Wgu, Sgu, bgu, Wdn, Sdn, bdn, out, wsp = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    args = [x, Wr, br, k, Wgu, Sgu, bgu, Wdn, Sdn, bdn, out, T, d, f, E, wsp, ws]
+    if stages is not None:
+        return moe.lib().moe_forward_stages(*args, flags, stages[0], stages[1], None)
+    return moe.lib().moe_forward_ex(*args, flags, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=200), ERR_SHAPE), (dict(f=100), ERR_SHAPE), (dict(T=-1), ERR_SHAPE), (dict(E=0), ERR_SHAPE),
+    (dict(d=0), ERR_SHAPE), (dict(k=0), ERR_UNSUP), (dict(k=9, E=16), ERR_UNSUP),
+    (dict(k=5, E=4), ERR_UNSUP), (dict(E=257), ERR_UNSUP), (dict(T=1 << 27, k=4), ERR_UNSUP),
+    (dict(flags=3), ERR_FLAGS), (dict(ws=100), ERR_WS), (dict(null=0), ERR_NULL),
+    (dict(null=9), ERR_NULL), (dict(null=10), ERR_NULL), (dict(misalign=3), ERR_ALIGN),
+    (dict(misalign=0), ERR_ALIGN), (dict(stages=(3, 2)), ERR_FLAGS), (dict(stages=(0, 6)), ERR_FLAGS),
+    (dict(stages=(-1, 2)), ERR_FLAGS),
+])
+def test_argument_errors(kw, want):
+    assert call(**kw) == want
+
+
+def test_empty_batch_is_a_noop():
+    assert call(T=0, null=0) == OK          # x may be NULL when T == 0
+    assert call(T=0, null=9) == OK          # out may be NULL when T == 0
+
+
+def test_workspace_size_formula_matches_header_estimate():
+    T, d, f, E, k = 4096, 4096, 1536, 128, 8
+    est = T * (d + k * (f + 4 * d + 8))
+    got = moe.workspace_bytes(T, d, f, E, k)
+    assert 0.9 * est < got < 1.2 * est

@@ -1,0 +1,148 @@
+"""HIP path vs the CPU oracle, element by element, through the C ABI (GPU only).
+
+Small cases run the oracle on every token and cover both GEMM paths (large
+row tiles and small row tiles), ragged expert tails, padded hidden sizes,
+column tails, k = 1, k = E and E = 256, k = 8.  Full-size workloads check the
+routing, permutation and x quantisation on every token and the expert rows
+and outputs on a seeded sample of tokens, in the launch configuration the
+benchmark times.  Gates are those of ``tests/parity.py``.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_layer_fp32_amd as moe
+from sparse_moe_layer_fp32_amd import inputs as gen
+from tests import handworked, parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_debug(inp, path):
+    p = moe.device_inputs(inp)
+    dbg = moe.forward_debug(p["x"], p["W_router"], p["b_router"], p["k"], p["W_gateup"],
+                            p["S_gateup"], p["b_gateup"], p["W_down"], p["S_down"], p["b_down"],
+                            path=path)
+    torch.cuda.synchronize()
+    return dbg
+
+
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+@pytest.mark.parametrize("k", [1, 2])
+def test_handworked_block(k, path):
+    inp = handworked.build(k)
+    _say(f"[handworked] k={k} path={path}")
+    dbg = run_debug(inp, path)
+    g = parity.bf16_to_f64(dbg["out"])[0]
+    want = handworked.expected(k)
+    # bf16 output of a hand-derived value: within one bf16 half-spacing (2^-9 relative) + h rounding
+    np.testing.assert_allclose(g, want, rtol=2.0 ** -8, atol=1e-6)
+    assert sorted(dbg["topk_idx"].cpu().numpy()[0].tolist()) == ([0] if k == 1 else [0, 1])
+    xq = dbg["xq"].cpu().numpy()[0]
+    assert xq[0] == 0x7E and xq[1] == 0x76 and np.all(xq[2:] == 0)
+    assert dbg["xs"].cpu().numpy()[0, 0] == 2.0 ** -7
+
+
+SMALL = [
+    # (T, d, d_real, f, E, k)
+    (64, 256, 256, 256, 8, 2),          # the tiny config
+    (1, 128, 128, 128, 2, 1),           # one token
+    (37, 384, 300, 256, 6, 3),          # ragged T, padded hidden size
+    (1000, 256, 256, 256, 4, 2),        # ~500 rows per expert: several row tiles + tails
+    (77, 128, 128, 128, 256, 8),        # E = 256, k = 8
+    (50, 256, 256, 128, 5, 5),          # k = E (every expert)
+    (130, 640, 640, 384, 3, 1),         # k = 1, down-projection column tail (640 = 2.5 x 256)
+    (513, 384, 384, 512, 7, 3),         # odd expert count, T not a multiple of 16
+]
+
+
+@pytest.mark.parametrize("path", ["prefill", "decode"])
+@pytest.mark.parametrize("shape", SMALL, ids=[f"T{s[0]}-d{s[1]}-f{s[3]}-E{s[4]}-k{s[5]}" for s in SMALL])
+def test_small_shapes_vs_oracle(shape, path):
+    T, d, dr, f, E, k = shape
+    layer = gen.custom_layer(d, f, E, k, d_real=dr, layer_id=1000 + d + f + E + k)
+    inp = gen.make_inputs(layer, T=T)
+    _say(f"[small] shape={shape} path={path}")
+    dbg = run_debug(inp, path)
+    ref = parity.oracle_ref(inp)
+    parity.check_routing(dbg, ref, T, k)
+    parity.check_xquant(dbg, ref["xq"], ref["xs"])
+    nflip, ncodes = parity.check_h_decisions(dbg, ref)
+    worst = parity.check_down_stage(dbg, ref, inp, dr)
+    parity.check_combine_stage(dbg)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, dr)
+    assert np.all(g[:, dr:] == 0), "padded output columns must be exactly zero"
+    _say(f"   out {m}\n   h decisions differing from the oracle: {nflip}/{ncodes}; "
+         f"down-stage err/bound {worst:.3f}")
+
+
+def test_deterministic_bits():
+    layer = gen.custom_layer(256, 256, 8, 2, layer_id=2000)
+    inp = gen.make_inputs(layer, T=700)
+    p = moe.device_inputs(inp)
+    args = (p["x"], p["W_router"], p["b_router"], p["k"], p["W_gateup"], p["S_gateup"],
+            p["b_gateup"], p["W_down"], p["S_down"], p["b_down"])
+    for path in ("prefill", "decode"):
+        a = moe.forward(*args, path=path).clone()
+        b = moe.forward(*args, path=path).clone()
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), path
+
+
+def test_empty_batch_and_stage_split():
+    layer = gen.custom_layer(256, 256, 8, 2, layer_id=2001)
+    inp = gen.make_inputs(layer, T=40)
+    p = moe.device_inputs(inp)
+    args = (p["W_router"], p["b_router"], p["k"], p["W_gateup"], p["S_gateup"], p["b_gateup"],
+            p["W_down"], p["S_down"], p["b_down"])
+    empty = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    assert moe.forward(empty, *args).shape == (0, 256)
+    whole = moe.forward(p["x"], *args)
+    ws = torch.empty(moe.workspace_bytes(40, 256, 256, 8, 2), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(whole)
+    moe.forward_stages("router", "place", p["x"], *args, out, ws)
+    moe.forward_stages("gateup", "gateup", p["x"], *args, out, ws)
+    moe.forward_stages("down", "combine", p["x"], *args, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int16), out.view(torch.int16))
+
+
+FULL = ["c1", "c2", "c3", "c4a", "c4b"]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", FULL)
+def test_full_size_sampled(cfg):
+    """Full-size workload in the benchmark's launch configuration (auto path)."""
+    c = gen.CONFIGS[cfg]
+    _say(f"[full] {cfg}: generating inputs T={c.T} d={c.layer.d} f={c.layer.f} E={c.layer.E} k={c.layer.k}")
+    inp = gen.make_inputs(cfg)
+    T, k, dr = inp["T"], inp["k"], inp["d_real"]
+    _say(f"[full] {cfg}: running the HIP path")
+    dbg = run_debug(inp, "auto")
+    _say(f"[full] {cfg}: oracle routing + x quantisation on all {T} tokens")
+    r = parity.orc.route(inp)
+    parity.check_routing(dbg, r, T, k)
+    x32 = gen.bf16_bits_to_f32(inp["x"])
+    xq, xs = parity.orc.quantize_groups(x32)
+    parity.check_xquant(dbg, xq, xs)
+    rng = np.random.default_rng(12345)
+    sample = np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(T, 160), replace=False)]))
+    _say(f"[full] {cfg}: oracle expert math on {len(sample)} sampled tokens")
+    ref = parity.oracle_ref(inp, tokens=sample)
+    nflip, ncodes = parity.check_h_decisions(dbg, ref)
+    worst = parity.check_down_stage(dbg, ref, inp, dr)
+    parity.check_combine_stage(dbg, sample)
+    g = parity.bf16_to_f64(dbg["out"])[sample]
+    m = parity.check_end_to_end(g, dbg, ref, inp, dr)
+    assert m["gate"] == "literal", f"{cfg}: the literal north-star gates must hold on the configs: {m}"
+    assert np.all(g[:, dr:] == 0)
+    _say(f"[full] {cfg}: out {m}\n   h decisions differing from the oracle: {nflip}/{ncodes}; "
+         f"down-stage err/bound {worst:.3f}")
