@@ -60,7 +60,8 @@ typedef enum {
   MOE_ERR_NULL = -1,        /* a required pointer is NULL                         */
   MOE_ERR_SHAPE = -2,       /* T < 0, d or f not a positive multiple of 128, E < 1 */
   MOE_ERR_UNSUPPORTED = -3, /* k < 1, k > E, k > MOE_MAX_TOPK, E > MOE_MAX_EXPERTS,
-                               or sizes whose element counts overflow int32        */
+                               d or f > MOE_MAX_HIDDEN, or tensors of 2^31 bytes
+                               or more (T*d, T*k*f, d*2f, scales)                 */
   MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_bytes */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
   MOE_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError)           */
@@ -70,6 +71,7 @@ typedef enum {
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 8
 #define MOE_BLOCK 128
+#define MOE_MAX_HIDDEN 8192 /* d and f: at most 64 blocks of 128 */
 
 /* Path selection for the expert GEMMs (argument `flags`). */
 #define MOE_PATH_AUTO 0u    /* pick by the mean rows per expert, T*k/E           */

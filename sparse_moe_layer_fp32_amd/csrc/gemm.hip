@@ -289,6 +289,291 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill kernel: direct global->LDS loads into a 3-stage ring.
+//
+// Tile 128 rows x 256 B columns, K block 128, 4 waves (2 x 2) of 64 x 128.
+// Per stage: A [128][128] e4m3 with the 16-byte segments of row r stored at
+// position seg ^ ((r >> 1) & 7); B [128 K][256 N] in its global K x N
+// orientation with the 16-byte segments of K row kr at seg ^ fb(kr); the A row
+// scales [128] fp32.  Loads are buffer_load ... lds (lane i of a load writes
+// bytes [16i, 16i+16) of a 1 KB LDS chunk; rows outside the tile or columns
+// outside N read offsets past the buffer end and land as zeros).  The B
+// operand of the MFMA is read with ds_read_b64_tr_b8: in each group of 16
+// lanes, lanes 2j and 2j+1 address the two 8-byte halves of one 16-column
+// segment of K row j, and lane i receives column i of those 8 rows.
+constexpr int DMA_STAGES = 3;
+constexpr int DMA_BM = 128;
+constexpr int DMA_BNP = 256;
+constexpr int DMA_SA = DMA_BM * kBlock;              // 16 KB
+constexpr int DMA_SB = kBlock * DMA_BNP;             // 32 KB
+constexpr int DMA_STAGE = DMA_SA + DMA_SB + 1024;      // + A row scales (and a spare 512 B)
+constexpr int DMA_STAGE_ALLOC = DMA_STAGE;
+static_assert(DMA_STAGE_ALLOC >= 48 * (DMA_BNP + 4) * 4, "a stage also holds 48 accumulator rows");
+constexpr uint32_t kOob = 0x80000000u;               // buffer offset that reads as zero
+constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_b(int kr) { return (kr & 7) | (((kr >> 5) & 1) << 3); }
+
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0f70 | 0); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0f70 | 13); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+  }
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
+  constexpr int BM = DMA_BM, BNP = DMA_BNP;
+  constexpr int MB = 4, NB = 8;  // 16x16 blocks per wave: 64 rows x 128 columns
+  // The three ring stages are distinct LDS objects: the compiler's wait
+  // analysis tells loads into one object from reads of another, so the
+  // next stages stay in flight while a stage is read.  After the K loop they
+  // hold the accumulator tile (48 padded rows each).
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE_ALLOC];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE_ALLOC];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE_ALLOC];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
+  // wave (wm, wn): rows 64*wm.., tile columns 128*wn..  (gated: wn = 0 gate, wn = 1 up)
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
+
+  // ---- which tile (XCD-contiguous slice of the tile table)
+  const int total = g.tile_off[g.E];
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  if (slot >= chunk) return;
+  const int L = xcd * chunk + slot;
+  if (L >= total) return;
+  int lo = 0, hi = g.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (g.tile_off[mid] <= L) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int cnt = g.counts[e];
+  const int mt = ceil_div(cnt, BM);
+  const int local = L - g.tile_off[e];
+  const int ng = local / (mt * GN);
+  const int rem = local - ng * mt * GN;
+  const int gw = min(GN, g.n_tiles - ng * GN);
+  const int m = rem / gw, nt = ng * GN + rem % gw;
+  const int row0 = g.offsets[e] + m * BM;
+  const int valid = min(BM, cnt - m * BM);
+  const int n0 = nt * (GATED ? kBlock : BNP);
+
+  // global column of 16-column segment s of the tile (segments 0-7 gate, 8-15 up)
+  auto seg_col = [&](int s) -> int {
+    if (GATED) return s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8);
+    return n0 + 16 * s;
+  };
+
+  // ---- buffer resources and per-lane load offsets (fixed for the tile)
+  const __amdgpu_buffer_rsrc_t rA =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, g.A_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rAs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, g.As_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(g.B + (size_t)e * K * N), (short)0, K * N, kRsrcWord3);
+  uint32_t aoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = wave * 4 + q;               // 1 KB chunk = rows 8c..8c+7
+    const int r = 8 * c + (lane >> 3);
+    const int sgm = (lane & 7) ^ swz_a(r);
+    aoff[q] = kOob;
+    if (r < valid) {
+      const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
+      aoff[q] = (uint32_t)arow * (uint32_t)K + 16u * sgm;
+    }
+  }
+  uint32_t soff = kOob;  // A scales: waves 0, 1 load rows 64w + lane; waves 2, 3 load zeros
+  if (wave < 2) {                               // into the spare half (same count per wave)
+    const int r = 64 * wave + lane;
+    if (r < valid) {
+      const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
+      soff = (uint32_t)arow * (uint32_t)nkb * 4u;
+    }
+  }
+  // B: lane -> K row kr = 4c + lane/16 of chunk c, segment (lane & 15) ^ swz_b(kr);
+  // swz_b(kr) only depends on lane (kr & 7 = 4(c & 1) + lane/16, kr >> 5 = c >> 3),
+  // so the column of each chunk is a function of (lane, c & 1, c >> 3)
+  const int b_kr0 = lane >> 4;
+  auto boff_of = [&](int c) -> uint32_t {
+    const int kr = 4 * c + b_kr0;
+    const int gc = seg_col((lane & 15) ^ swz_b(kr));
+    return gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
+  };
+
+  // Every call issues the same 13 loads per wave, also past the last K block
+  // (they then read offsets past the buffers and land as zeros in a stage no
+  // one reads): unconditional issue keeps the in-flight count the same on
+  // every path, so the compiler's waits stay exact.
+  auto issue = [&](uint8_t* base, int kb) {
+    const bool live = kb < nkb;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t o = (aoff[q] == kOob || !live) ? kOob : aoff[q] + (uint32_t)kb * kBlock;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (wave * 4 + q) * 1024), 16, o,
+                                               0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t bo = boff_of(wave * 8 + q);
+      const uint32_t o = (bo == kOob || !live) ? kOob : bo + (uint32_t)kb * kBlock * (uint32_t)N;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rB, (lds_void*)(base + DMA_SA + (wave * 8 + q) * 1024), 16, o, 0, 0, 0);
+    }
+    {
+      const uint32_t o = (soff == kOob || !live) ? kOob : soff + 4u * kb;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rAs, (lds_void*)(base + DMA_SA + DMA_SB + wave * 256), 4, o, 0, 0, 0);
+    }
+  };
+
+  // ---- per-lane LDS read offsets (stage-relative)
+  const int gq = lane >> 4, l16 = lane & 15;
+  // A: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
+  const int a_row = (wm * 64 + l16) * kBlock;
+  const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
+  const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
+  // B: transposing reads of K rows 32gq + 8r + l16/2, half l16 & 1 of segment cs
+  const int b_row = (32 * gq + (l16 >> 1)) * BNP + 8 * (l16 & 1);
+  const int b_swz = (l16 >> 1) | ((gq & 1) << 3);
+  const int b_base = 16 * ((8 * wn) ^ b_swz);  // segment 8wn + nb sits at b_base ^ 16nb
+  const int s_row = (wm * 64 + 4 * gq) * 4;
+
+  // weight scales of this wave's 128-column block for every K block: lane kb
+  // holds block kb (K <= 64 blocks); the loop reads them with v_readlane
+  const int sblk = seg_col(8 * wn) / kBlock;
+  const float bs_lane =
+      (lane < nkb && sblk < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk] : 0.f;
+
+  v4f acc[MB][NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int gc = seg_col(8 * wn + nb) + l16;
+    const float bv = gc < N ? bf16_to_f32(g.bias[(size_t)e * N + gc]) : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = v4f{bv, bv, bv, bv};
+  }
+
+  auto compute = [&](const uint8_t* base, int kb) {
+    const uint8_t* sA = base;
+    const uint8_t* sB = base + DMA_SA;
+    const float* sAs = reinterpret_cast<const float*>(base + DMA_SA + DMA_SB);
+    const float sb = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_lane), kb));
+    v8i af[MB];
+    v4f sc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const v4i lo4 = *reinterpret_cast<const v4i*>(sA + a_row + mb * 16 * kBlock + a_pos0);
+      const v4i hi4 = *reinterpret_cast<const v4i*>(sA + a_row + mb * 16 * kBlock + a_pos1);
+      af[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      sc[mb] = *reinterpret_cast<const v4f*>(reinterpret_cast<const uint8_t*>(sAs) + s_row +
+                                             mb * 64) * sb;
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      v8i bf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(sB + b_row + r * 8 * BNP + (b_base ^ (16 * nb))));
+        bf[2 * r] = t[0];
+        bf[2 * r + 1] = t[1];
+      }
+      v4f pn[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        pn[mb] = mfma_fp8_16x16x128(af[mb], bf, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(pn[mb][i], sc[mb][i], acc[mb][nb][i]);
+    }
+  };
+
+  // Ring synchronisation: wait for this wave's loads of stage kb (the next
+  // stage's loads may stay in flight), then a bare s_barrier.  A __syncthreads
+  // fence would also wait for the in-flight stage.  The empty asm statements
+  // keep the compiler from moving LDS accesses across the barrier.
+  auto wait_stage = [&](int) {
+    wait_vmcnt(13);  // this wave's 13 loads of the next stage stay in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  issue(st0, 0);
+  issue(st1, 1);
+  for (int kb = 0; kb < nkb; kb += 3) {
+    wait_stage(kb);
+    issue(st2, kb + 2);
+    compute(st0, kb);
+    if (kb + 1 >= nkb) break;
+    wait_stage(kb + 1);
+    issue(st0, kb + 3);
+    compute(st1, kb + 1);
+    if (kb + 2 >= nkb) break;
+    wait_stage(kb + 2);
+    issue(st1, kb + 4);
+    compute(st2, kb + 2);
+  }
+  wait_vmcnt(0);  // the loads past the last K block land before LDS is reused
+
+  __syncthreads();  // every wave is done with the ring
+  // accumulator tile -> LDS, row-major [BM][BNP] fp32 with a 4-float row pad,
+  // rows 0-47 in st0, 48-95 in st1, 96-127 in st2
+  constexpr int CP = BNP + 4;
+  auto crow = [&](int r) -> float* {
+    uint8_t* b = r < 48 ? st0 : (r < 96 ? st1 : st2);
+    return reinterpret_cast<float*>(b) + (r % 48) * CP;
+  };
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* rowp = crow(wm * 64 + mb * 16 + 4 * gq + i);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) rowp[wn * 128 + nb * 16 + l16] = acc[mb][nb][i];
+    }
+  __syncthreads();
+  if constexpr (GATED) {
+    // h = silu(gate) * up and its 1x128 e4m3 quantisation, one row per wave step:
+    // lane c holds h columns 2c, 2c+1 of the tile's 128
+    for (int r = wave; r < valid; r += 4) {
+      const float* rowp = crow(r);
+      const float2 gv = *reinterpret_cast<const float2*>(rowp + 2 * lane);
+      const float2 uv = *reinterpret_cast<const float2*>(rowp + 128 + 2 * lane);
+      const float h0 = gv.x / (1.0f + expf(-gv.x)) * uv.x;
+      const float h1 = gv.y / (1.0f + expf(-gv.y)) * uv.y;
+      const float amax = wave_max(fmaxf(fabsf(h0), fabsf(h1)));
+      const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+      const float q0 = fminf(fmaxf(h0 / s, -kFp8Max), kFp8Max);
+      const float q1 = fminf(fmaxf(h1 / s, -kFp8Max), kFp8Max);
+      reinterpret_cast<uint16_t*>(g.Hq + (size_t)(row0 + r) * g.f + n0)[lane] =
+          static_cast<uint16_t>(f32x2_to_e4m3(q0, q1));
+      if (lane == 0) g.Hs[(size_t)(row0 + r) * (g.f / kBlock) + nt] = s;
+    }
+  } else {
+    // Y rows: 256 columns = 64 lanes x 4
+    const int gc = n0 + 4 * lane;
+    if (gc < N)
+      for (int r = wave; r < valid; r += 4)
+        *reinterpret_cast<float4*>(g.Y + (size_t)(row0 + r) * N + gc) =
+            *reinterpret_cast<const float4*>(crow(r) + 4 * lane);
+  }
+}
+
 int grid_for(int max_tiles) { return 8 * ceil_div(max_tiles, 8); }
 
 }  // namespace
@@ -300,8 +585,7 @@ hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kGatedDecode.bm, kGatedDecode.bnp, 1, 4, true>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<kGatedPrefill.bm, kGatedPrefill.bnp, 2, 2, true>),
-                       grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -312,8 +596,7 @@ hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kPlainDecode.bm, kPlainDecode.bnp, 1, 4, false>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<kPlainPrefill.bm, kPlainPrefill.bnp, 2, 2, false>),
-                       grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 
 namespace moe {
 
-constexpr int RT_TT = 16;     // tokens per router / placement workgroup
+constexpr int RT_TT = 64;     // tokens per router / placement workgroup (histogram tile)
 constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 256;
 
 // GEMM tile shapes.  "Gated" is gate/up + bias + SwiGLU + h quantisation,
 // "plain" is down + bias.  Prefill tiles are MFMA-bound, decode tiles stream
@@ -33,14 +34,19 @@ struct GemmArgs {
   const int32_t* offsets;      // first row per expert [E+1]
   const int32_t* tile_off;     // first tile per expert [E+1] (this kernel's tiling)
   int K, N, f, n_tiles, E;
+  int A_bytes, As_bytes;       // sizes of A and As (buffer bounds; reads past them give 0)
   uint8_t* Hq;                 // gated outputs: h codes [R, f] and scales [R, f/128]
   float* Hs;
   float* Y;                    // plain output [R, N]
 };
 
+// K splits of the router for T tokens (1: top-k fused into the router kernel;
+// >1: partial logits [splits][T][E] fp32 in `partial`, then a top-k kernel).
+int router_splits(int T, int d);
+
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
-                         int k, int32_t* topk_idx, float* topk_w, int32_t* hist, uint8_t* xq,
-                         float* xs, hipStream_t stream);
+                         int k, float* partial, int32_t* topk_idx, float* topk_w, int32_t* hist,
+                         uint8_t* xq, float* xs, hipStream_t stream);
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,

@@ -13,9 +13,10 @@ namespace {
 using moe::ceil_div;
 
 constexpr int64_t kMaxRows = int64_t(1) << 28;  // T*k bound (row indices are int32)
+constexpr int64_t kMaxBuffer = int64_t(1) << 31;
 
 struct Layout {
-  size_t topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, row_of,
+  size_t partial, topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, row_of,
       row_token, xq, xs, hq, hs, y, total;
 };
 
@@ -30,6 +31,8 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
     o = align256(o + bytes);
     return at;
   };
+  const int64_t ns = moe::router_splits((int)T, (int)d);
+  l.partial = put(ns > 1 ? 4 * ns * T * E : 0);
   l.topk_idx = put(4 * R);
   l.topk_w = put(4 * R);
   l.hist = put(4 * NT * E);
@@ -52,7 +55,14 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
 moe_status check_sizes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k) {
   if (T < 0 || d <= 0 || f <= 0 || E < 1 || d % MOE_BLOCK || f % MOE_BLOCK) return MOE_ERR_SHAPE;
   if (k < 1 || k > E || k > MOE_MAX_TOPK || E > MOE_MAX_EXPERTS) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)T * k > kMaxRows || d > (1 << 20) || f > (1 << 20)) return MOE_ERR_UNSUPPORTED;
+  // the GEMMs keep one weight scale per K block in one lane: at most 64 blocks
+  if ((int64_t)T * k > kMaxRows || d > 64 * MOE_BLOCK || f > 64 * MOE_BLOCK)
+    return MOE_ERR_UNSUPPORTED;
+  // buffer offsets of the GEMM loads are 32-bit and must stay below 2^31
+  const int64_t R = (int64_t)T * k;
+  if ((int64_t)T * d >= kMaxBuffer || R * f >= kMaxBuffer || 2 * (int64_t)d * f >= kMaxBuffer ||
+      4 * R * (d / MOE_BLOCK + f / MOE_BLOCK) >= kMaxBuffer)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -105,6 +115,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   auto at = [&](size_t off) { return ws + off; };
+  float* partial = reinterpret_cast<float*>(at(l.partial));
   int32_t* topk_idx = reinterpret_cast<int32_t*>(at(l.topk_idx));
   float* topk_w = reinterpret_cast<float*>(at(l.topk_w));
   int32_t* hist = reinterpret_cast<int32_t*>(at(l.hist));
@@ -139,7 +150,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
     switch (stage) {
       case MOE_STAGE_ROUTER:
         err = moe::launch_router(static_cast<const uint16_t*>(x), W_router, b_router, T, d, E, k,
-                                 topk_idx, topk_w, hist, xq, xs, stream);
+                                 partial, topk_idx, topk_w, hist, xq, xs, stream);
         break;
       case MOE_STAGE_SCAN:
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
@@ -166,6 +177,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.E = E;
         g.Hq = hq;
         g.Hs = hs;
+        g.A_bytes = (int)((int64_t)T * d);
+        g.As_bytes = (int)(4 * (int64_t)T * (d / moe::kBlock));
         err = moe::launch_gemm_gated(g, decode, max_g, stream);
         break;
       }
@@ -185,6 +198,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.n_tiles = nt_p;
         p.E = E;
         p.Y = y;
+        p.A_bytes = (int)((int64_t)R * f);
+        p.As_bytes = (int)(4 * (int64_t)R * (f / moe::kBlock));
         err = moe::launch_gemm_plain(p, decode, max_p, stream);
         break;
       }

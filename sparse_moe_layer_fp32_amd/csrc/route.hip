@@ -109,7 +109,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
 // One workgroup per router tile: rank of every (token, slot) pair among the
 // earlier pairs of the tile with the same expert (a token never picks an
 // expert twice, so this is the token order).
-__global__ __launch_bounds__(128) void route_place_kernel(const int32_t* __restrict__ topk_idx,
+__global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_kernel(const int32_t* __restrict__ topk_idx,
                                                           const int32_t* __restrict__ tile_base,
                                                           int T, int E, int k,
                                                           int32_t* __restrict__ row_of,
@@ -178,7 +178,7 @@ hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, in
 
 hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
                               int k, int32_t* row_of, int32_t* row_token, hipStream_t stream) {
-  hipLaunchKernelGGL(route_place_kernel, dim3(ceil_div(T, RT_TT)), dim3(128), 0, stream, topk_idx,
+  hipLaunchKernelGGL(route_place_kernel, dim3(ceil_div(T, RT_TT)), dim3(RT_TT * kMaxTopK), 0, stream, topk_idx,
                      tile_base, T, E, k, row_of, row_token);
   return hipGetLastError();
 }

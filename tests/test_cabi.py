@@ -69,6 +69,7 @@ def call(T=64, d=256, f=256, E=8, k=2, ws=None, flags=0, null=None, misalign=Non
     (dict(d=200), ERR_SHAPE), (dict(f=100), ERR_SHAPE), (dict(T=-1), ERR_SHAPE), (dict(E=0), ERR_SHAPE),
     (dict(d=0), ERR_SHAPE), (dict(k=0), ERR_UNSUP), (dict(k=9, E=16), ERR_UNSUP),
     (dict(k=5, E=4), ERR_UNSUP), (dict(E=257), ERR_UNSUP), (dict(T=1 << 27, k=4), ERR_UNSUP),
+    (dict(d=8320), ERR_UNSUP), (dict(f=8320), ERR_UNSUP), (dict(T=1 << 20, d=4096, k=1), ERR_UNSUP),
     (dict(flags=3), ERR_FLAGS), (dict(ws=100), ERR_WS), (dict(null=0), ERR_NULL),
     (dict(null=9), ERR_NULL), (dict(null=10), ERR_NULL), (dict(misalign=3), ERR_ALIGN),
     (dict(misalign=0), ERR_ALIGN), (dict(stages=(3, 2)), ERR_FLAGS), (dict(stages=(0, 6)), ERR_FLAGS),
