@@ -290,26 +290,35 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: direct global->LDS loads into a 3-stage ring.
+// Prefill kernel: direct global->LDS loads into a 3-stage ring, 8 waves.
 //
-// Tile 128 rows x 256 B columns, K block 128, 4 waves (2 x 2) of 64 x 128.
-// Per stage: A [128][128] e4m3 with the 16-byte segments of row r stored at
-// position seg ^ ((r >> 1) & 7); B [128 K][256 N] in its global K x N
-// orientation with the 16-byte segments of K row kr at seg ^ fb(kr); the A row
-// scales [128] fp32.  Loads are buffer_load ... lds (lane i of a load writes
-// bytes [16i, 16i+16) of a 1 KB LDS chunk; rows outside the tile or columns
-// outside N read offsets past the buffer end and land as zeros).  The B
-// operand of the MFMA is read with ds_read_b64_tr_b8: in each group of 16
+// Tile 128 rows x 256 B columns, K block 128.  Per stage: A [128][128] e4m3
+// with the 16-byte segments of row r stored at position seg ^ ((r >> 1) & 7);
+// B [128 K][256 N] in its global K x N orientation with the 16-byte segments
+// of K row kr at seg ^ swz_b(kr); the A row scales of the stage's K block.
+// Loads are buffer_load ... lds: lane i of a load writes bytes [s*i, s*i+s)
+// of the LDS destination; rows outside the tile or columns outside N read
+// offsets past the buffer end and land as zeros.
+//
+// Eight waves (two per SIMD, so one wave's LDS waits and barrier hide under
+// the other's MFMAs) in a 2 x 4 grid each own 64 rows x 64 columns.  The
+// weights are the first MFMA operand and the activations the second, so a
+// lane's four outputs are four consecutive columns of one row: the row scale
+// is one scalar per lane and the epilogue writes whole dwords / float4s.
+// The weight operand is read with ds_read_b64_tr_b8: in each group of 16
 // lanes, lanes 2j and 2j+1 address the two 8-byte halves of one 16-column
 // segment of K row j, and lane i receives column i of those 8 rows.
-constexpr int DMA_STAGES = 3;
+// Gated tiles hold 128 gate and the matching 128 up columns; wave column
+// wn owns h columns 32wn..32wn+31 as two gate and two up blocks, so SwiGLU
+// and the per-row h quantisation run on registers.
 constexpr int DMA_BM = 128;
 constexpr int DMA_BNP = 256;
+constexpr int DMA_WAVES = 8;
 constexpr int DMA_SA = DMA_BM * kBlock;              // 16 KB
 constexpr int DMA_SB = kBlock * DMA_BNP;             // 32 KB
-constexpr int DMA_STAGE = DMA_SA + DMA_SB + 1024;      // + A row scales (and a spare 512 B)
-constexpr int DMA_STAGE_ALLOC = DMA_STAGE;
-static_assert(DMA_STAGE_ALLOC >= 48 * (DMA_BNP + 4) * 4, "a stage also holds 48 accumulator rows");
+constexpr int DMA_SS = DMA_WAVES * 256;              // row scales: waves 0, 1; the others load zeros
+constexpr int DMA_STAGE = DMA_SA + DMA_SB + DMA_SS;  // 50 KB; three stages = 150 KB
+constexpr int DMA_LOADS = 2 + 4 + 1;                 // per wave and stage: A, B, scales
 constexpr uint32_t kOob = 0x80000000u;               // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
 
@@ -322,27 +331,25 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0f70 | 0); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0f70 | 13); break;
+    case DMA_LOADS: __builtin_amdgcn_s_waitcnt(0x0f70 | DMA_LOADS); break;
     default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
   }
 }
 
 template <bool GATED>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
+__global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int BM = DMA_BM, BNP = DMA_BNP;
-  constexpr int MB = 4, NB = 8;  // 16x16 blocks per wave: 64 rows x 128 columns
+  constexpr int MB = 4, NB = 4;  // 16x16 blocks per wave: 64 rows x 64 columns
   // The three ring stages are distinct LDS objects: the compiler's wait
   // analysis tells loads into one object from reads of another, so the
-  // next stages stay in flight while a stage is read.  After the K loop they
-  // hold the accumulator tile (48 padded rows each).
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE_ALLOC];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE_ALLOC];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE_ALLOC];
+  // next stages stay in flight while a stage is read.
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
-  // wave (wm, wn): rows 64*wm.., tile columns 128*wn..  (gated: wn = 0 gate, wn = 1 up)
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
 
   // ---- which tile (XCD-contiguous slice of the tile table)
@@ -382,11 +389,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
       __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, g.As_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(g.B + (size_t)e * K * N), (short)0, K * N, kRsrcWord3);
-  uint32_t aoff[4];
+  // A: 1 KB chunk c = rows 8c..8c+7; wave w loads chunks 2w, 2w+1
+  uint32_t aoff[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = wave * 4 + q;               // 1 KB chunk = rows 8c..8c+7
-    const int r = 8 * c + (lane >> 3);
+  for (int q = 0; q < 2; ++q) {
+    const int r = 8 * (2 * wave + q) + (lane >> 3);
     const int sgm = (lane & 7) ^ swz_a(r);
     aoff[q] = kOob;
     if (r < valid) {
@@ -394,42 +401,45 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
       aoff[q] = (uint32_t)arow * (uint32_t)K + 16u * sgm;
     }
   }
-  uint32_t soff = kOob;  // A scales: waves 0, 1 load rows 64w + lane; waves 2, 3 load zeros
-  if (wave < 2) {                               // into the spare half (same count per wave)
-    const int r = 64 * wave + lane;
+  // A row scales: waves 0, 1 fill 64 rows each in the order [row % 16][row / 16],
+  // so that one 16-byte read returns the four row blocks of a lane; waves 2-7
+  // load zeros into the spare space (same load count on every wave)
+  uint32_t soff = kOob;
+  if (wave < 2) {
+    const int r = 64 * wave + 16 * (lane & 3) + (lane >> 2);
     if (r < valid) {
       const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
       soff = (uint32_t)arow * (uint32_t)nkb * 4u;
     }
   }
-  // B: lane -> K row kr = 4c + lane/16 of chunk c, segment (lane & 15) ^ swz_b(kr);
-  // swz_b(kr) only depends on lane (kr & 7 = 4(c & 1) + lane/16, kr >> 5 = c >> 3),
-  // so the column of each chunk is a function of (lane, c & 1, c >> 3)
-  const int b_kr0 = lane >> 4;
-  auto boff_of = [&](int c) -> uint32_t {
-    const int kr = 4 * c + b_kr0;
+  // B: 1 KB chunk c = K rows 4c..4c+3; wave w loads chunks 4w..4w+3; lane ->
+  // K row 4c + lane/16, the 16 bytes of segment (lane & 15) ^ swz_b(kr)
+  uint32_t boff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int kr = 4 * (4 * wave + q) + (lane >> 4);
     const int gc = seg_col((lane & 15) ^ swz_b(kr));
-    return gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
-  };
+    boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
+  }
 
-  // Every call issues the same 13 loads per wave, also past the last K block
+  // Every call issues the same loads per wave, also past the last K block
   // (they then read offsets past the buffers and land as zeros in a stage no
   // one reads): unconditional issue keeps the in-flight count the same on
   // every path, so the compiler's waits stay exact.
   auto issue = [&](uint8_t* base, int kb) {
     const bool live = kb < nkb;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       const uint32_t o = (aoff[q] == kOob || !live) ? kOob : aoff[q] + (uint32_t)kb * kBlock;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (wave * 4 + q) * 1024), 16, o,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (2 * wave + q) * 1024), 16, o,
                                                0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t bo = boff_of(wave * 8 + q);
-      const uint32_t o = (bo == kOob || !live) ? kOob : bo + (uint32_t)kb * kBlock * (uint32_t)N;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t o =
+          (boff[q] == kOob || !live) ? kOob : boff[q] + (uint32_t)kb * kBlock * (uint32_t)N;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rB, (lds_void*)(base + DMA_SA + (wave * 8 + q) * 1024), 16, o, 0, 0, 0);
+          rB, (lds_void*)(base + DMA_SA + (4 * wave + q) * 1024), 16, o, 0, 0, 0);
     }
     {
       const uint32_t o = (soff == kOob || !live) ? kOob : soff + 4u * kb;
@@ -440,65 +450,79 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
 
   // ---- per-lane LDS read offsets (stage-relative)
   const int gq = lane >> 4, l16 = lane & 15;
-  // A: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
+  // activations: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
   const int a_row = (wm * 64 + l16) * kBlock;
   const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
   const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
-  // B: transposing reads of K rows 32gq + 8r + l16/2, half l16 & 1 of segment cs
+  // weights: transposing reads of K rows 32gq + 8r + l16/2, half l16 & 1 of a segment
   const int b_row = (32 * gq + (l16 >> 1)) * BNP + 8 * (l16 & 1);
   const int b_swz = (l16 >> 1) | ((gq & 1) << 3);
-  const int b_base = 16 * ((8 * wn) ^ b_swz);  // segment 8wn + nb sits at b_base ^ 16nb
-  const int s_row = (wm * 64 + 4 * gq) * 4;
+  // tile segment of column block nb: gated 2wn + nb (gate) and 8 + 2wn + nb - 2 (up),
+  // plain 4wn + nb; stored at segment ^ b_swz
+  const int b_base = 16 * ((GATED ? 2 * wn : 4 * wn) ^ b_swz);
+  auto b_seg = [&](int nb) -> int { return GATED ? ((nb & 1) | ((nb >> 1) << 3)) : nb; };
+  const int s_pos = (wm * 64 + 4 * l16) * 4;
 
-  // weight scales of this wave's 128-column block for every K block: lane kb
-  // holds block kb (K <= 64 blocks); the loop reads them with v_readlane
-  const int sblk = seg_col(8 * wn) / kBlock;
-  const float bs_lane =
-      (lane < nkb && sblk < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk] : 0.f;
+  // weight scales of every K block (lane kb holds block kb; K <= 64 blocks),
+  // read in the loop with v_readlane: plain waves use one 128-column block,
+  // gated waves one gate block and one up block
+  const int sblk0 = seg_col(GATED ? 0 : 4 * wn) / kBlock;
+  const int sblk1 = GATED ? seg_col(8) / kBlock : sblk0;
+  const float bs0_lane =
+      (lane < nkb && sblk0 < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk0] : 0.f;
+  const float bs1_lane =
+      (GATED && lane < nkb && sblk1 < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk1] : 0.f;
 
-  v4f acc[MB][NB];
+  // accumulators start from the bias: block nb, lane -> columns 4gq..4gq+3 of the block
+  float acc[MB][NB][4];  // scalars, not vectors: no register-quad constraint in the loop
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int gc = seg_col(8 * wn + nb) + l16;
-    const float bv = gc < N ? bf16_to_f32(g.bias[(size_t)e * N + gc]) : 0.f;
+    const int gc = seg_col((GATED ? 2 * wn : 4 * wn) + b_seg(nb)) + 4 * gq;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = v4f{bv, bv, bv, bv};
+    for (int i = 0; i < 4; ++i) {
+      const float bv = gc + i < N ? bf16_to_f32(g.bias[(size_t)e * N + gc + i]) : 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[mb][nb][i] = bv;
+    }
   }
 
   auto compute = [&](const uint8_t* base, int kb) {
     const uint8_t* sA = base;
     const uint8_t* sB = base + DMA_SA;
-    const float* sAs = reinterpret_cast<const float*>(base + DMA_SA + DMA_SB);
-    const float sb = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs_lane), kb));
-    v8i af[MB];
-    v4f sc[MB];
+    const float sb0 = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs0_lane), kb));
+    const float sb1 = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                            __builtin_bit_cast(int, bs1_lane), kb))
+                            : sb0;
+    const v4f sa = *reinterpret_cast<const v4f*>(base + DMA_SA + DMA_SB + s_pos);
+    v8i xf[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const v4i lo4 = *reinterpret_cast<const v4i*>(sA + a_row + mb * 16 * kBlock + a_pos0);
       const v4i hi4 = *reinterpret_cast<const v4i*>(sA + a_row + mb * 16 * kBlock + a_pos1);
-      af[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      sc[mb] = *reinterpret_cast<const v4f*>(reinterpret_cast<const uint8_t*>(sAs) + s_row +
-                                             mb * 64) * sb;
+      xf[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      v8i bf;
+      v8i wf;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(sB + b_row + r * 8 * BNP + (b_base ^ (16 * nb))));
-        bf[2 * r] = t[0];
-        bf[2 * r + 1] = t[1];
+            (__attribute__((address_space(3))) v2i*)(sB + b_row + r * 8 * BNP +
+                                                     (b_base ^ (16 * b_seg(nb)))));
+        wf[2 * r] = t[0];
+        wf[2 * r + 1] = t[1];
       }
+      const float sb = (GATED && nb >= 2) ? sb1 : sb0;
       v4f pn[MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        pn[mb] = mfma_fp8_16x16x128(af[mb], bf, v4f{0.f, 0.f, 0.f, 0.f});
+      for (int mb = 0; mb < MB; ++mb) pn[mb] = mfma_fp8_16x16x128(wf, xf[mb], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb) {
+        const float s = sa[mb] * sb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(pn[mb][i], sc[mb][i], acc[mb][nb][i]);
+        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(pn[mb][i], s, acc[mb][nb][i]);
+      }
     }
   };
 
@@ -506,8 +530,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
   // stage's loads may stay in flight), then a bare s_barrier.  A __syncthreads
   // fence would also wait for the in-flight stage.  The empty asm statements
   // keep the compiler from moving LDS accesses across the barrier.
-  auto wait_stage = [&](int) {
-    wait_vmcnt(13);  // this wave's 13 loads of the next stage stay in flight
+  auto wait_stage = [&]() {
+    wait_vmcnt(DMA_LOADS);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -516,61 +540,76 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
   issue(st0, 0);
   issue(st1, 1);
   for (int kb = 0; kb < nkb; kb += 3) {
-    wait_stage(kb);
+    wait_stage();
     issue(st2, kb + 2);
     compute(st0, kb);
     if (kb + 1 >= nkb) break;
-    wait_stage(kb + 1);
+    wait_stage();
     issue(st0, kb + 3);
     compute(st1, kb + 1);
     if (kb + 2 >= nkb) break;
-    wait_stage(kb + 2);
+    wait_stage();
     issue(st1, kb + 4);
     compute(st2, kb + 2);
   }
   wait_vmcnt(0);  // the loads past the last K block land before LDS is reused
 
-  __syncthreads();  // every wave is done with the ring
-  // accumulator tile -> LDS, row-major [BM][BNP] fp32 with a 4-float row pad,
-  // rows 0-47 in st0, 48-95 in st1, 96-127 in st2
-  constexpr int CP = BNP + 4;
-  auto crow = [&](int r) -> float* {
-    uint8_t* b = r < 48 ? st0 : (r < 96 ? st1 : st2);
-    return reinterpret_cast<float*>(b) + (r % 48) * CP;
-  };
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float* rowp = crow(wm * 64 + mb * 16 + 4 * gq + i);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) rowp[wn * 128 + nb * 16 + l16] = acc[mb][nb][i];
-    }
-  __syncthreads();
+  // lane -> rows 64wm + 16mb + l16, columns (of block nb) 4gq..4gq+3
   if constexpr (GATED) {
-    // h = silu(gate) * up and its 1x128 e4m3 quantisation, one row per wave step:
-    // lane c holds h columns 2c, 2c+1 of the tile's 128
-    for (int r = wave; r < valid; r += 4) {
-      const float* rowp = crow(r);
-      const float2 gv = *reinterpret_cast<const float2*>(rowp + 2 * lane);
-      const float2 uv = *reinterpret_cast<const float2*>(rowp + 128 + 2 * lane);
-      const float h0 = gv.x / (1.0f + expf(-gv.x)) * uv.x;
-      const float h1 = gv.y / (1.0f + expf(-gv.y)) * uv.y;
-      const float amax = wave_max(fmaxf(fabsf(h0), fabsf(h1)));
+    // h = silu(gate) * up on registers: h column 32wn + 16j + 4gq + i
+    float h[MB][2][4];
+    float pmax[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float gv = acc[mb][j][i], uv = acc[mb][2 + j][i];
+          h[mb][j][i] = gv / (1.0f + expf(-gv)) * uv;
+          mx = fmaxf(mx, fabsf(h[mb][j][i]));
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    // row maxima over the four wave columns through LDS: smax[wn][row]
+    __syncthreads();  // every wave is done with the ring
+    float* smax = reinterpret_cast<float*>(st0);
+    if (gq == 0)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * 64 + 16 * mb + l16] = pmax[mb];
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = wm * 64 + 16 * mb + l16;
+      const float amax = fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
       const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-      const float q0 = fminf(fmaxf(h0 / s, -kFp8Max), kFp8Max);
-      const float q1 = fminf(fmaxf(h1 / s, -kFp8Max), kFp8Max);
-      reinterpret_cast<uint16_t*>(g.Hq + (size_t)(row0 + r) * g.f + n0)[lane] =
-          static_cast<uint16_t>(f32x2_to_e4m3(q0, q1));
-      if (lane == 0) g.Hs[(size_t)(row0 + r) * (g.f / kBlock) + nt] = s;
+      if (r < valid) {
+        uint8_t* hrow = g.Hq + (size_t)(row0 + r) * g.f + n0 + 32 * wn + 4 * gq;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] / s, -kFp8Max), kFp8Max);
+          *reinterpret_cast<uint32_t*>(hrow + 16 * j) = f32x4_to_e4m3(q[0], q[1], q[2], q[3]);
+        }
+        if (wn == 0 && gq == 0) g.Hs[(size_t)(row0 + r) * (g.f / kBlock) + nt] = s;
+      }
     }
   } else {
-    // Y rows: 256 columns = 64 lanes x 4
-    const int gc = n0 + 4 * lane;
-    if (gc < N)
-      for (int r = wave; r < valid; r += 4)
-        *reinterpret_cast<float4*>(g.Y + (size_t)(row0 + r) * N + gc) =
-            *reinterpret_cast<const float4*>(crow(r) + 4 * lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int gc = n0 + 64 * wn + 16 * nb + 4 * gq;
+      if (gc < N)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * 64 + 16 * mb + l16;
+          if (r < valid)
+            *reinterpret_cast<v4f*>(g.Y + (size_t)(row0 + r) * N + gc) =
+                v4f{acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]};
+        }
+    }
   }
 }
 
@@ -585,7 +624,7 @@ hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kGatedDecode.bm, kGatedDecode.bnp, 1, 4, true>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), grid, dim3(DMA_WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -596,7 +635,7 @@ hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kPlainDecode.bm, kPlainDecode.bnp, 1, 4, false>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), grid, dim3(DMA_WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 
