@@ -19,6 +19,8 @@
 // product of the row's activation scale and the block's weight scale.
 // Tiles are taken from a device-side table (expert, row block, column block),
 // grouped so that tiles sharing weights run together on one XCD (L2).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,7 +30,7 @@ namespace {
 
 constexpr int KP = 144;      // LDS pitch (bytes) of a staged row/column: 128 + 16
 constexpr int B_COLQ = 16;   // extra bytes after every 16 staged B columns (bank spread)
-constexpr int GN = 4;        // column tiles per group in the tile order
+constexpr int GN = kTileGroup;  // column tiles per group in the tile order
 
 template <int BM, int BNP, int WAVES_M, int WAVES_N, bool GATED>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
@@ -290,15 +292,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// Prefill kernel: direct global->LDS loads into a 3-stage ring, 8 waves.
+// Prefill kernel: persistent, direct global->LDS loads into a 3-stage ring,
+// 8 waves.
 //
 // Tile 128 rows x 256 B columns, K block 128.  Per stage: A [128][128] e4m3
-// with the 16-byte segments of row r stored at position seg ^ ((r >> 1) & 7);
+// with the 16-byte segments of row r stored at position seg ^ (r & 7);
 // B [128 K][256 N] in its global K x N orientation with the 16-byte segments
-// of K row kr at seg ^ swz_b(kr); the A row scales of the stage's K block.
-// Loads are buffer_load ... lds: lane i of a load writes bytes [s*i, s*i+s)
-// of the LDS destination; rows outside the tile or columns outside N read
-// offsets past the buffer end and land as zeros.
+// of K row kr at seg ^ swz_b(kr); a 2 KB side area where wave w's load lands
+// at 256w: the A row scales of the K block (waves 0, 1), the tile's bias
+// (waves 2, 3), the two weight-block scales of the K block (wave 4, lanes
+// 0-1) and zeros (waves 5-7).  Loads are buffer_load ... lds: lane i of a
+// load writes bytes [s*i, s*i+s) of the LDS destination; rows outside the
+// tile or columns outside N read offsets past the buffer end and land as
+// zeros.
 //
 // Eight waves (two per SIMD, so one wave's LDS waits and barrier hide under
 // the other's MFMAs) in a 2 x 4 grid each own 64 rows x 64 columns.  The
@@ -311,145 +317,222 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 // Gated tiles hold 128 gate and the matching 128 up columns; wave column
 // wn owns h columns 32wn..32wn+31 as two gate and two up blocks, so SwiGLU
 // and the per-row h quantisation run on registers.
+//
+// Persistent: one workgroup per CU walks the tiles L = lo + slot + i * nslots
+// of its XCD's contiguous slice of the tile list with one continuous K-block
+// stream, so the next tile's first stages load while the current tile ends.
+// Inside that stream the only vector-memory operations are the stage loads,
+// the row-token loads of the gated kernel and the epilogue stores, all with a
+// fixed count per wave; tile descriptors come through the scalar cache and
+// bias and weight scales through the stages.  So every wait is a vmcnt the
+// kernel states itself, and nothing drains the ring at a tile boundary.
 constexpr int DMA_BM = 128;
 constexpr int DMA_BNP = 256;
 constexpr int DMA_WAVES = 8;
 constexpr int DMA_SA = DMA_BM * kBlock;              // 16 KB
 constexpr int DMA_SB = kBlock * DMA_BNP;             // 32 KB
-constexpr int DMA_SS = DMA_WAVES * 256;              // row scales: waves 0, 1; the others load zeros
+constexpr int DMA_SS = DMA_WAVES * 256;              // side area: wave w's load lands at 256w
 constexpr int DMA_STAGE = DMA_SA + DMA_SB + DMA_SS;  // 50 KB; three stages = 150 KB
-constexpr int DMA_LOADS = 2 + 4 + 1;                 // per wave and stage: A, B, scales
+constexpr int DMA_LOADS = 2 + 4 + 1;                 // per wave and stage: A, B, side
+constexpr int SIDE_AS = 0, SIDE_BIAS = 512, SIDE_BS = 1024;
 constexpr uint32_t kOob = 0x80000000u;               // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(4))) int32_t const_i32;
 
-__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
+// A row r keeps its 16-byte segment s at position s ^ (r & 7): the 8 rows that
+// one 128-byte LDS cycle of a ds_read_b128 serves sit in 8 distinct positions.
+__device__ __forceinline__ int swz_a(int r) { return r & 7; }
 __device__ __forceinline__ int swz_b(int kr) { return (kr & 7) | (((kr >> 5) & 1) << 3); }
 
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0f70 | 0); break;
-    case DMA_LOADS: __builtin_amdgcn_s_waitcnt(0x0f70 | DMA_LOADS); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
-  }
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Raw buffer resource (gfx9: base, stride 0, byte size, raw-buffer word 3) in SGPRs.
+__device__ __forceinline__ v4i dma_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// Global -> LDS loads (buffer_load ... lds): lane i writes bytes [s*i, s*i+s)
+// at LDS address `lds` (uniform); offsets past the resource size read zeros.
+// Written as inline asm so that the compiler does not track them: its wait
+// analysis cannot tell the ring stages apart across the persistent loop and
+// would wait for every load in flight before each LDS read.  The kernel's own
+// s_waitcnt + s_barrier pairs order these loads against the reads; a wait
+// the compiler adds for its own memory operations only waits longer.  M0 is
+// restored.
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc)
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<uintptr_t>(p))));
+}
+
+// One output tile: {expert, first row, rows, column tile} from the tile list.
+struct DmaTile {
+  int e, row0, valid, nt;
+};
+
+__device__ __forceinline__ DmaTile dma_tile(const GemmArgs& g, int L) {
+  const const_i32* v = (const const_i32*)g.tiles + 4 * L;  // uniform: scalar loads
+  return DmaTile{v[0], v[1], v[2], v[3]};
 }
 
 template <bool GATED>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
   constexpr int BM = DMA_BM, BNP = DMA_BNP;
-  constexpr int MB = 4, NB = 4;  // 16x16 blocks per wave: 64 rows x 64 columns
-  // The three ring stages are distinct LDS objects: the compiler's wait
-  // analysis tells loads into one object from reads of another, so the
-  // next stages stay in flight while a stage is read.
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];
+  constexpr int MB = 4, NB = 4;                     // 16x16 blocks per wave: 64 rows x 64 columns
+  constexpr int RT = GATED ? 1 : 0;                 // row-token loads per cursor move
+  constexpr int ST = GATED ? 4 * 3 : 4 * 4;         // epilogue stores per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];  // the three ring stages
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE];
+  __shared__ float smax[GATED ? 4 * BM : 1];        // gated epilogue: row maxima per wave column
+  __shared__ int32_t rtok[GATED ? 2 : 1][GATED ? DMA_WAVES * 64 : 1];  // row tokens, 2 tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int wm = wave >> 2, wn = wave & 3;
+  const int gq = lane >> 4, l16 = lane & 15;
   const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
 
-  // ---- which tile (XCD-contiguous slice of the tile table)
-  const int total = g.tile_off[g.E];
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  // ---- this workgroup's tiles: L = lo + slot + i * nslots < hi
+  const int total = ((const const_i32*)g.tile_off)[g.E];
+  const int nslots = gridDim.x >> 3;
   const int chunk = (total + 7) >> 3;
-  if (slot >= chunk) return;
-  const int L = xcd * chunk + slot;
-  if (L >= total) return;
-  int lo = 0, hi = g.E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_off[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int cnt = g.counts[e];
-  const int mt = ceil_div(cnt, BM);
-  const int local = L - g.tile_off[e];
-  const int ng = local / (mt * GN);
-  const int rem = local - ng * mt * GN;
-  const int gw = min(GN, g.n_tiles - ng * GN);
-  const int m = rem / gw, nt = ng * GN + rem % gw;
-  const int row0 = g.offsets[e] + m * BM;
-  const int valid = min(BM, cnt - m * BM);
-  const int n0 = nt * (GATED ? kBlock : BNP);
+  const int lo = (blockIdx.x & 7) * chunk;
+  const int hi = min(total, lo + chunk);
+  const int L0 = lo + (blockIdx.x >> 3);
+  if (L0 >= hi) return;
 
-  // global column of 16-column segment s of the tile (segments 0-7 gate, 8-15 up)
-  auto seg_col = [&](int s) -> int {
-    if (GATED) return s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8);
-    return n0 + 16 * s;
+  const v4i rA = dma_rsrc(g.A, g.A_bytes);
+  // side-area load of this wave: A row scales, bias, weight-block scales or zeros
+  const v4i rSide = wave < 2   ? dma_rsrc(g.As, g.As_bytes)
+                    : wave < 4 ? dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N)
+                               : dma_rsrc(g.Bs, 4u * (uint32_t)g.E * nkb * nsb);
+  const int side_step = wave < 2 ? 4 : (wave == 4 ? 4 * nsb : 0);  // bytes per K block
+
+  // ---- load cursor: tile tl (index Ll), K block kbl; the next tile prefetched
+  int Ll = L0, kbl = 0, rb = 0;
+  int Lln = Ll + nslots;
+  DmaTile tl = dma_tile(g, Ll), tln = tl;
+  if (Lln < hi) tln = dma_tile(g, Lln);
+  uint32_t aoff[2], boff[4], soff;
+  auto no_loads = [&]() {
+    aoff[0] = aoff[1] = soff = kOob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) boff[q] = kOob;
   };
 
-  // ---- buffer resources and per-lane load offsets (fixed for the tile)
-  const __amdgpu_buffer_rsrc_t rA =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, g.A_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rAs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)g.As, (short)0, g.As_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(g.B + (size_t)e * K * N), (short)0, K * N, kRsrcWord3);
-  // A: 1 KB chunk c = rows 8c..8c+7; wave w loads chunks 2w, 2w+1
-  uint32_t aoff[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 8 * (2 * wave + q) + (lane >> 3);
-    const int sgm = (lane & 7) ^ swz_a(r);
-    aoff[q] = kOob;
-    if (r < valid) {
-      const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
-      aoff[q] = (uint32_t)arow * (uint32_t)K + 16u * sgm;
+  // gated: tokens of the tile's 128 rows -> rtok[buf] (waves 0, 1; the
+  // others load zeros into their own slots)
+  auto rt_load = [&](const DmaTile& t, bool live, int buf) {
+    if constexpr (GATED) {
+      const int r = 64 * wave + lane;
+      const uint32_t o = (live && wave < 2 && r < t.valid) ? 4u * (uint32_t)(t.row0 + r) : kOob;
+      dma4(dma_rsrc(g.row_token, g.rows_bytes), lds_addr(&rtok[buf][64 * wave]), o);
     }
-  }
-  // A row scales: waves 0, 1 fill 64 rows each in the order [row % 16][row / 16],
-  // so that one 16-byte read returns the four row blocks of a lane; waves 2-7
-  // load zeros into the spare space (same load count on every wave)
-  uint32_t soff = kOob;
-  if (wave < 2) {
-    const int r = 64 * wave + 16 * (lane & 3) + (lane >> 2);
-    if (r < valid) {
-      const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
-      soff = (uint32_t)arow * (uint32_t)nkb * 4u;
-    }
-  }
-  // B: 1 KB chunk c = K rows 4c..4c+3; wave w loads chunks 4w..4w+3; lane ->
-  // K row 4c + lane/16, the 16 bytes of segment (lane & 15) ^ swz_b(kr)
-  uint32_t boff[4];
+  };
+  // per-lane load offsets of tile t (row tokens in rtok[buf] for the gated kernel);
+  // loads that must read zeros get an offset past the buffer, which stays past
+  // it when the K-block stride is added
+  v4i rB;
+  auto setup = [&](const DmaTile& t, int buf) {
+    const int n0 = t.nt * (GATED ? kBlock : BNP);
+    rB = dma_rsrc(g.B + (size_t)t.e * K * N, (uint32_t)K * (uint32_t)N);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int kr = 4 * (4 * wave + q) + (lane >> 4);
-    const int gc = seg_col((lane & 15) ^ swz_b(kr));
-    boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
-  }
-
-  // Every call issues the same loads per wave, also past the last K block
-  // (they then read offsets past the buffers and land as zeros in a stage no
-  // one reads): unconditional issue keeps the in-flight count the same on
-  // every path, so the compiler's waits stay exact.
-  auto issue = [&](uint8_t* base, int kb) {
-    const bool live = kb < nkb;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t o = (aoff[q] == kOob || !live) ? kOob : aoff[q] + (uint32_t)kb * kBlock;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)(base + (2 * wave + q) * 1024), 16, o,
-                                               0, 0, 0);
+    for (int q = 0; q < 2; ++q) {  // A: 1 KB chunk c = rows 8c..8c+7; wave w: chunks 2w, 2w+1
+      const int r = 8 * (2 * wave + q) + (lane >> 3);
+      const int sgm = (lane & 7) ^ swz_a(r);
+      aoff[q] = kOob;
+      if (r < t.valid) aoff[q] = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)K + 16u * sgm;
     }
+    // B: 1 KB chunk c = K rows 4c..4c+3; wave w: chunks 4w..4w+3; lane -> K row
+    // 4c + lane/16, the 16 bytes of segment (lane & 15) ^ swz_b(kr)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t o =
-          (boff[q] == kOob || !live) ? kOob : boff[q] + (uint32_t)kb * kBlock * (uint32_t)N;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rB, (lds_void*)(base + DMA_SA + (4 * wave + q) * 1024), 16, o, 0, 0, 0);
+      const int kr = 4 * (4 * wave + q) + (lane >> 4);
+      const int s = (lane & 15) ^ swz_b(kr);
+      const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
+      boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
     }
-    {
-      const uint32_t o = (soff == kOob || !live) ? kOob : soff + 4u * kb;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rAs, (lds_void*)(base + DMA_SA + DMA_SB + wave * 256), 4, o, 0, 0, 0);
+    soff = kOob;
+    if (wave < 2) {  // A row scales in the order [row % 16][row / 16] of each 64-row half
+      const int r = 64 * wave + 16 * (lane & 3) + (lane >> 2);
+      if (r < t.valid) soff = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)nkb * 4u;
+    } else if (wave < 4) {  // bias: 128 columns (bf16 pairs) per wave
+      const int c = (GATED ? (wave == 2 ? n0 : g.f + n0) : n0 + 128 * (wave - 2)) + 2 * lane;
+      if (c < N) soff = 2u * ((uint32_t)t.e * (uint32_t)N + (uint32_t)c);
+    } else if (wave == 4 && lane < 2) {  // the two weight-block scales of the K block
+      const int sb = GATED ? (lane == 0 ? n0 : g.f + n0) / kBlock : n0 / kBlock + lane;
+      if (sb < nsb) soff = 4u * ((uint32_t)t.e * (uint32_t)nkb * (uint32_t)nsb + (uint32_t)sb);
     }
+  };
+
+  // Every call issues the same loads per wave, also past the last tile (they
+  // then read offsets past the buffers and land as zeros in a stage no one
+  // reads): the in-flight count is the same on every path.
+  auto issue = [&](uint8_t* base) {
+    const uint32_t sbase = lds_addr(base);
+    const uint32_t ka = (uint32_t)kbl * kBlock, kb = ka * (uint32_t)N;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(rA, sbase + (2 * wave + q) * 1024, aoff[q] + ka);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(rB, sbase + DMA_SA + (4 * wave + q) * 1024, boff[q] + kb);
+    dma4(rSide, sbase + DMA_SA + DMA_SB + 256 * wave, soff + (uint32_t)(kbl * side_step));
+    ++kbl;
+  };
+  // After a tile's last K block has been issued the cursor moves to its next
+  // tile, whose row tokens were loaded one move earlier; returns the number
+  // of loads it issued.
+  auto advance = [&]() -> int {
+    if (kbl < nkb) return 0;
+    kbl = 0;
+    Ll = Lln;
+    tl = tln;
+    rb ^= 1;
+    Lln += nslots;
+    if (Lln < hi) tln = dma_tile(g, Lln);
+    if (nkb == 1) {  // the row tokens were loaded one K block ago: wait for them
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    if (Ll < hi) setup(tl, rb);
+    else no_loads();
+    // the previous readers of rtok[rb ^ 1] are past a ring barrier
+    rt_load(tln, Lln < hi, rb ^ 1);
+    return RT;
   };
 
   // ---- per-lane LDS read offsets (stage-relative)
-  const int gq = lane >> 4, l16 = lane & 15;
   // activations: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
   const int a_row = (wm * 64 + l16) * kBlock;
   const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
@@ -461,40 +544,38 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // plain 4wn + nb; stored at segment ^ b_swz
   const int b_base = 16 * ((GATED ? 2 * wn : 4 * wn) ^ b_swz);
   auto b_seg = [&](int nb) -> int { return GATED ? ((nb & 1) | ((nb >> 1) << 3)) : nb; };
-  const int s_pos = (wm * 64 + 4 * l16) * 4;
+  const int s_pos = DMA_SA + DMA_SB + SIDE_AS + (wm * 64 + 4 * l16) * 4;
+  // bias of block nb: 4 bf16 at columns 4gq.. of the block
+  auto bias_pos = [&](int nb) -> int {
+    return DMA_SA + DMA_SB + SIDE_BIAS +
+           2 * (GATED ? (nb < 2 ? 32 * wn + 16 * nb : 128 + 32 * wn + 16 * (nb - 2))
+                      : 64 * wn + 16 * nb) + 8 * gq;
+  };
 
-  // weight scales of every K block (lane kb holds block kb; K <= 64 blocks),
-  // read in the loop with v_readlane: plain waves use one 128-column block,
-  // gated waves one gate block and one up block
-  const int sblk0 = seg_col(GATED ? 0 : 4 * wn) / kBlock;
-  const int sblk1 = GATED ? seg_col(8) / kBlock : sblk0;
-  const float bs0_lane =
-      (lane < nkb && sblk0 < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk0] : 0.f;
-  const float bs1_lane =
-      (GATED && lane < nkb && sblk1 < nsb) ? g.Bs[((size_t)e * nkb + lane) * nsb + sblk1] : 0.f;
-
-  // accumulators start from the bias: block nb, lane -> columns 4gq..4gq+3 of the block
+  // ---- compute side: tile tc, K block kbc; the next tile prefetched
+  DmaTile tc = tl, tcn = tln;
+  int Lcn = Lln, kbc = 0;
   float acc[MB][NB][4];  // scalars, not vectors: no register-quad constraint in the loop
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int gc = seg_col((GATED ? 2 * wn : 4 * wn) + b_seg(nb)) + 4 * gq;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float bv = gc + i < N ? bf16_to_f32(g.bias[(size_t)e * N + gc + i]) : 0.f;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) acc[mb][nb][i] = bv;
-    }
-  }
 
-  auto compute = [&](const uint8_t* base, int kb) {
+  auto compute = [&](const uint8_t* base) {
     const uint8_t* sA = base;
     const uint8_t* sB = base + DMA_SA;
-    const float sb0 = __builtin_bit_cast(
-        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bs0_lane), kb));
-    const float sb1 = GATED ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                            __builtin_bit_cast(int, bs1_lane), kb))
-                            : sb0;
-    const v4f sa = *reinterpret_cast<const v4f*>(base + DMA_SA + DMA_SB + s_pos);
+    const float* sbs = reinterpret_cast<const float*>(base + DMA_SA + DMA_SB + SIDE_BS);
+    const float sb0 = sbs[GATED ? 0 : (wn >> 1)];
+    const float sb1 = GATED ? sbs[1] : sb0;
+    if (kbc == 0) {  // accumulators start from the bias
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint2 w = *reinterpret_cast<const uint2*>(base + bias_pos(nb));
+        const float bv[4] = {bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
+                             bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) acc[mb][nb][i] = bv[i];
+      }
+    }
+    const v4f sa = *reinterpret_cast<const v4f*>(base + s_pos);
     v8i xf[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -526,94 +607,155 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     }
   };
 
-  // Ring synchronisation: wait for this wave's loads of stage kb (the next
-  // stage's loads may stay in flight), then a bare s_barrier.  A __syncthreads
-  // fence would also wait for the in-flight stage.  The empty asm statements
-  // keep the compiler from moving LDS accesses across the barrier.
-  auto wait_stage = [&]() {
-    wait_vmcnt(DMA_LOADS);
+  // lane -> rows 64wm + 16mb + l16, columns (of block nb) 4gq..4gq+3.  Every
+  // wave issues ST stores whatever the tile's shape (rows past the tile and
+  // columns past N go to offsets past the buffers, which drops them).
+  auto epilogue = [&](const DmaTile& t) {
+    const int n0 = t.nt * (GATED ? kBlock : BNP);
+    if constexpr (GATED) {
+      // h = silu(gate) * up on registers: h column 32wn + 16j + 4gq + i
+      float h[MB][2][4];
+      float pmax[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[mb][j][i], uv = acc[mb][2 + j][i];
+            // silu with the hardware exp2 and reciprocal (relative error ~1e-7,
+            // far below the e4m3 spacing h is rounded to)
+            const float ex = __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f);
+            h[mb][j][i] = gv * __builtin_amdgcn_rcpf(1.0f + ex) * uv;
+            mx = fmaxf(mx, fabsf(h[mb][j][i]));
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      // row maxima over the four wave columns through LDS.  The previous
+      // tile's readers are past at least one ring barrier; a bare s_barrier
+      // (no memory fence) leaves the next tile's stage loads in flight.
+      if (gq == 0)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * 64 + 16 * mb + l16] = pmax[mb];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const __amdgpu_buffer_rsrc_t rH =
+          __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rHs =
+          __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = wm * 64 + 16 * mb + l16;
+        const float amax =
+            fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
+        const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+        const float inv = 1.0f / s;
+        const bool ok = r < t.valid;
+        const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] * inv, -kFp8Max), kFp8Max);
+          __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
+                                                ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+        }
+        const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
+                                              (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rY =
+          __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, g.out_bytes, kRsrcWord3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int gc = n0 + 64 * wn + 16 * nb + 4 * gq;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * 64 + 16 * mb + l16;
+          const uint32_t o = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)N + (uint32_t)gc);
+          const v4u d = v4u{__builtin_bit_cast(uint32_t, acc[mb][nb][0]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][1]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][2]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, rY, (r < t.valid && gc < N) ? (int)o : (int)kOob,
+                                                 0, 0);
+        }
+      }
+    }
+  };
+
+  // Ring synchronisation: wait for this wave's loads of the stage about to be
+  // read.  Younger than them are the next stage's 7 loads and `pend` more
+  // operations (row tokens, epilogue stores), which may stay in flight.
+  // Then a bare s_barrier (a __syncthreads fence would wait for everything).
+  auto wait_stage = [&](int pend) {
+    if (pend == 0) wait_vmcnt<DMA_LOADS>();
+    else if (pend == RT) wait_vmcnt<DMA_LOADS + RT>();
+    else if (pend == ST) wait_vmcnt<DMA_LOADS + ST>();
+    else if (pend == RT + ST) wait_vmcnt<DMA_LOADS + RT + ST>();
+    else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
-  issue(st0, 0);
-  issue(st1, 1);
-  for (int kb = 0; kb < nkb; kb += 3) {
-    wait_stage();
-    issue(st2, kb + 2);
-    compute(st0, kb);
-    if (kb + 1 >= nkb) break;
-    wait_stage();
-    issue(st0, kb + 3);
-    compute(st1, kb + 1);
-    if (kb + 2 >= nkb) break;
-    wait_stage();
-    issue(st1, kb + 4);
-    compute(st2, kb + 2);
-  }
-  wait_vmcnt(0);  // the loads past the last K block land before LDS is reused
-
-  // lane -> rows 64wm + 16mb + l16, columns (of block nb) 4gq..4gq+3
+  // ---- prologue: row tokens of the first two tiles, offsets of the first
+  rt_load(tl, true, 0);
+  rt_load(tln, Lln < hi, 1);
   if constexpr (GATED) {
-    // h = silu(gate) * up on registers: h column 32wn + 16j + 4gq + i
-    float h[MB][2][4];
-    float pmax[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      float mx = 0.f;
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = acc[mb][j][i], uv = acc[mb][2 + j][i];
-          h[mb][j][i] = gv / (1.0f + expf(-gv)) * uv;
-          mx = fmaxf(mx, fabsf(h[mb][j][i]));
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
-    }
-    // row maxima over the four wave columns through LDS: smax[wn][row]
-    __syncthreads();  // every wave is done with the ring
-    float* smax = reinterpret_cast<float*>(st0);
-    if (gq == 0)
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * 64 + 16 * mb + l16] = pmax[mb];
+    wait_vmcnt<0>();
     __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = wm * 64 + 16 * mb + l16;
-      const float amax = fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
-      const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-      if (r < valid) {
-        uint8_t* hrow = g.Hq + (size_t)(row0 + r) * g.f + n0 + 32 * wn + 4 * gq;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float q[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] / s, -kFp8Max), kFp8Max);
-          *reinterpret_cast<uint32_t*>(hrow + 16 * j) = f32x4_to_e4m3(q[0], q[1], q[2], q[3]);
-        }
-        if (wn == 0 && gq == 0) g.Hs[(size_t)(row0 + r) * (g.f / kBlock) + nt] = s;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int gc = n0 + 64 * wn + 16 * nb + 4 * gq;
-      if (gc < N)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int r = wm * 64 + 16 * mb + l16;
-          if (r < valid)
-            *reinterpret_cast<v4f*>(g.Y + (size_t)(row0 + r) * N + gc) =
-                v4f{acc[mb][nb][0], acc[mb][nb][1], acc[mb][nb][2], acc[mb][nb][3]};
-        }
-    }
   }
+  setup(tl, 0);
+
+  // One K block; returns false after the workgroup's last tile.
+  int pend = 0;
+  auto step = [&](const uint8_t* cur, uint8_t* next2) -> bool {
+    wait_stage(pend);
+    issue(next2);
+    compute(cur);
+    pend = advance();
+    if (++kbc < nkb) return true;
+    epilogue(tc);
+    pend += ST;
+    if (Lcn >= hi) return false;
+    kbc = 0;
+    tc = tcn;
+    Lcn += nslots;
+    if (Lcn < hi) tcn = dma_tile(g, Lcn);
+    return true;
+  };
+
+  issue(st0);
+  pend = advance();
+  issue(st1);
+  pend = advance();
+  while (step(st0, st2) && step(st1, st0) && step(st2, st1)) {
+  }
+  wait_vmcnt<0>();  // the loads past the last tile land before the workgroup ends
 }
 
 int grid_for(int max_tiles) { return 8 * ceil_div(max_tiles, 8); }
+
+// Persistent prefill grid: one workgroup per CU (a multiple of 8, one slice
+// per XCD), fewer when the tile list cannot fill them.
+int grid_persistent(int max_tiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = 8 * ceil_div(n, 8);
+  }
+  return std::min(cus[dev], grid_for(max_tiles));
+}
 
 }  // namespace
 
@@ -624,7 +766,8 @@ hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kGatedDecode.bm, kGatedDecode.bnp, 1, 4, true>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), grid, dim3(DMA_WAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(grid_persistent(max_tiles)),
+                       dim3(DMA_WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -635,7 +778,8 @@ hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipS
     hipLaunchKernelGGL((grouped_gemm_kernel<kPlainDecode.bm, kPlainDecode.bnp, 1, 4, false>), grid,
                        dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), grid, dim3(DMA_WAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), dim3(grid_persistent(max_tiles)),
+                       dim3(DMA_WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 

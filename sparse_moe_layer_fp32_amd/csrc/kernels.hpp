@@ -8,6 +8,7 @@
 namespace moe {
 
 constexpr int RT_TT = 64;     // tokens per router / placement workgroup (histogram tile)
+constexpr int kTileGroup = 4; // column tiles per group in a GEMM's tile order
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 256;
 
@@ -33,8 +34,11 @@ struct GemmArgs {
   const int32_t* counts;       // rows per expert [E]
   const int32_t* offsets;      // first row per expert [E+1]
   const int32_t* tile_off;     // first tile per expert [E+1] (this kernel's tiling)
+  const int32_t* tiles;        // prefill: tile list [tiles][4] = {expert, first row, rows, column tile}
   int K, N, f, n_tiles, E;
   int A_bytes, As_bytes;       // sizes of A and As (buffer bounds; reads past them give 0)
+  int rows_bytes;              // 4 * R: size of row_token
+  int out_bytes, out2_bytes;   // gated: sizes of Hq and Hs; plain: size of Y
   uint8_t* Hq;                 // gated outputs: h codes [R, f] and scales [R, f/128]
   float* Hs;
   float* Y;                    // plain output [R, N]
@@ -51,6 +55,12 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, in
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
                              int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream);
+
+// Tile list of one grouped GEMM from its per-expert tile offsets (row blocks
+// of bm rows, n_tiles column tiles, grouped kTileGroup column tiles at a time).
+hipError_t launch_tile_table(const int32_t* tile_off, const int32_t* counts, const int32_t* offsets,
+                             int E, int bm, int n_tiles, int max_tiles, int32_t* tiles,
+                             hipStream_t stream);
 
 hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
                               int k, int32_t* row_of, int32_t* row_token, hipStream_t stream);

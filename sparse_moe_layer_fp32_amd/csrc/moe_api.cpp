@@ -16,8 +16,8 @@ constexpr int64_t kMaxRows = int64_t(1) << 28;  // T*k bound (row indices are in
 constexpr int64_t kMaxBuffer = int64_t(1) << 31;
 
 struct Layout {
-  size_t partial, topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, row_of,
-      row_token, xq, xs, hq, hs, y, total;
+  size_t partial, topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, tiles0,
+      tiles1, row_of, row_token, xq, xs, hq, hs, y, total;
 };
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -41,6 +41,10 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
   l.tile_base = put(4 * NT * E);
   l.tile_off0 = put(4 * (E + 1));
   l.tile_off1 = put(4 * (E + 1));
+  // prefill tile lists (row blocks of the prefill tile height)
+  const int64_t mtiles = ceil_div((int)R, moe::kGatedPrefill.bm) + (E < R ? E : R);
+  l.tiles0 = put(16 * mtiles * (f / moe::kBlock));
+  l.tiles1 = put(16 * mtiles * ceil_div((int)d, moe::kPlainPrefill.bnp));
   l.row_of = put(4 * R);
   l.row_token = put(4 * R);
   l.xq = put(T * d);
@@ -124,6 +128,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   int32_t* tile_base = reinterpret_cast<int32_t*>(at(l.tile_base));
   int32_t* tile_off0 = reinterpret_cast<int32_t*>(at(l.tile_off0));
   int32_t* tile_off1 = reinterpret_cast<int32_t*>(at(l.tile_off1));
+  int32_t* tiles0 = reinterpret_cast<int32_t*>(at(l.tiles0));
+  int32_t* tiles1 = reinterpret_cast<int32_t*>(at(l.tiles1));
   int32_t* row_of = reinterpret_cast<int32_t*>(at(l.row_of));
   int32_t* row_token = reinterpret_cast<int32_t*>(at(l.row_token));
   uint8_t* xq = at(l.xq);
@@ -155,6 +161,12 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
       case MOE_STAGE_SCAN:
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
                                      tile_base, tile_off0, tile_off1, stream);
+        if (err == hipSuccess && !decode)
+          err = moe::launch_tile_table(tile_off0, counts, offsets, E, gs.bm, nt_g, max_g, tiles0,
+                                       stream);
+        if (err == hipSuccess && !decode)
+          err = moe::launch_tile_table(tile_off1, counts, offsets, E, ps.bm, nt_p, max_p, tiles1,
+                                       stream);
         break;
       case MOE_STAGE_PLACE:
         err = moe::launch_route_place(topk_idx, tile_base, T, E, k, row_of, row_token, stream);
@@ -170,6 +182,10 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.counts = counts;
         g.offsets = offsets;
         g.tile_off = tile_off0;
+        g.tiles = tiles0;
+        g.rows_bytes = (int)(4 * (int64_t)R);
+        g.out_bytes = (int)((int64_t)R * f);
+        g.out2_bytes = (int)(4 * (int64_t)R * (f / moe::kBlock));
         g.K = d;
         g.N = 2 * f;
         g.f = f;
@@ -192,6 +208,9 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.counts = counts;
         p.offsets = offsets;
         p.tile_off = tile_off1;
+        p.tiles = tiles1;
+        p.rows_bytes = (int)(4 * (int64_t)R);
+        p.out_bytes = (int)(4 * (int64_t)R * d);
         p.K = f;
         p.N = d;
         p.f = f;

@@ -8,6 +8,8 @@
 // MoE GEMM reads; combine first accumulates locally.  On one GPU that is a
 // counting sort of the (token, slot) pairs by expert, stable in token order,
 // and a gather-sum over the k rows of each token in slot order.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -130,6 +132,33 @@ __global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_kernel(const int
   }
 }
 
+// Entry L of the tile list: the expert whose tiles hold L (binary search of
+// the tile offsets), then inside the expert the order (column group of
+// kTileGroup tiles, row block, column tile), so that consecutive tiles share
+// one slice of the expert's weights.
+__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ tile_off,
+                                                        const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets, int E,
+                                                        int bm, int n_tiles, int max_tiles,
+                                                        int4* __restrict__ tiles) {
+  const int total = min(tile_off[E], max_tiles);
+  for (int L = blockIdx.x * 256 + threadIdx.x; L < total; L += gridDim.x * 256) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_off[mid] <= L) lo = mid; else hi = mid;
+    }
+    const int cnt = counts[lo];
+    const int mt = ceil_div(cnt, bm);
+    const int local = L - tile_off[lo];
+    const int ng = local / (mt * kTileGroup);
+    const int rem = local - ng * mt * kTileGroup;
+    const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
+    const int m = rem / gw;
+    tiles[L] = make_int4(lo, offsets[lo] + m * bm, min(bm, cnt - m * bm), ng * kTileGroup + rem % gw);
+  }
+}
+
 // out[t, :] = bf16( sum_j w[t,j] * Y[row_of[t,j], :] ), fp32 in slot order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ row_of,
@@ -180,6 +209,16 @@ hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base,
                               int k, int32_t* row_of, int32_t* row_token, hipStream_t stream) {
   hipLaunchKernelGGL(route_place_kernel, dim3(ceil_div(T, RT_TT)), dim3(RT_TT * kMaxTopK), 0, stream, topk_idx,
                      tile_base, T, E, k, row_of, row_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_table(const int32_t* tile_off, const int32_t* counts, const int32_t* offsets,
+                             int E, int bm, int n_tiles, int max_tiles, int32_t* tiles,
+                             hipStream_t stream) {
+  if (max_tiles <= 0) return hipSuccess;
+  const int grid = std::min(1024, ceil_div(max_tiles, 256));
+  hipLaunchKernelGGL(tile_table_kernel, dim3(grid), dim3(256), 0, stream, tile_off, counts, offsets,
+                     E, bm, n_tiles, max_tiles, reinterpret_cast<int4*>(tiles));
   return hipGetLastError();
 }
 
