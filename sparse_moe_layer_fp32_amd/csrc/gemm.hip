@@ -326,14 +326,27 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
 // fixed count per wave; tile descriptors come through the scalar cache and
 // bias and weight scales through the stages.  So every wait is a vmcnt the
 // kernel states itself, and nothing drains the ring at a tile boundary.
-constexpr int DMA_BM = 128;
-constexpr int DMA_BNP = 256;
 constexpr int DMA_WAVES = 8;
-constexpr int DMA_SA = DMA_BM * kBlock;              // 16 KB
-constexpr int DMA_SB = kBlock * DMA_BNP;             // 32 KB
 constexpr int DMA_SS = DMA_WAVES * 256;              // side area: wave w's load lands at 256w
-constexpr int DMA_STAGE = DMA_SA + DMA_SB + DMA_SS;  // 50 KB; three stages = 150 KB
-constexpr int DMA_LOADS = 2 + 4 + 1;                 // per wave and stage: A, B, side
+// Tiles: 128 rows (prefill: waves of 64 rows) or 32 rows (decode, bound by
+// streaming the weights: waves of 16 rows), by 256 B columns (waves of 64)
+// or, for the decode down projection, 128 (waves of 32).  A stage is
+// A [BM][128], B [128][BNP] and the side area: 50 KB for prefill.
+template <int BM, int BNP>
+struct DmaShape {
+  static constexpr int MB = BM / 32;                 // 16-row blocks per wave
+  static constexpr int NB = BNP / 64;                // 16-column blocks per wave
+  static constexpr int SA = BM * kBlock;
+  static constexpr int SB = kBlock * BNP;
+  static constexpr int STAGE = SA + SB + DMA_SS;
+  static constexpr int A_PER = BM >= 64 ? BM / 64 : 1;        // A chunks (1 KB) per loading wave
+  static constexpr int A_WAVES = BM / 8 / A_PER;              // waves that load A
+  static constexpr int B_PER = BNP / 64;                      // B chunks per wave
+  static constexpr int SEGS = BNP / 16;                       // 16-byte segments per K row
+  static constexpr int LOADS_MIN = (A_WAVES == DMA_WAVES ? A_PER : 0) + B_PER + 1;  // fewest per wave
+  static_assert(BM == 32 || BM == 128, "row tile");
+  static_assert(BNP == 128 || BNP == 256, "column tile");
+};
 constexpr int SIDE_AS = 0, SIDE_BIAS = 512, SIDE_BS = 1024;
 constexpr uint32_t kOob = 0x80000000u;               // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
@@ -343,7 +356,10 @@ typedef __attribute__((address_space(4))) int32_t const_i32;
 // A row r keeps its 16-byte segment s at position s ^ (r & 7): the 8 rows that
 // one 128-byte LDS cycle of a ds_read_b128 serves sit in 8 distinct positions.
 __device__ __forceinline__ int swz_a(int r) { return r & 7; }
-__device__ __forceinline__ int swz_b(int kr) { return (kr & 7) | (((kr >> 5) & 1) << 3); }
+template <int SEGS>
+__device__ __forceinline__ int swz_b(int kr) {
+  return SEGS == 16 ? (kr & 7) | (((kr >> 5) & 1) << 3) : (kr & 7);
+}
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
 template <int N>
@@ -404,12 +420,15 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& g, int L) {
   return DmaTile{v[0], v[1], v[2], v[3]};
 }
 
-template <bool GATED>
+template <bool GATED, int BM, int BNP>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
-  constexpr int BM = DMA_BM, BNP = DMA_BNP;
-  constexpr int MB = 4, NB = 4;                     // 16x16 blocks per wave: 64 rows x 64 columns
+  using S = DmaShape<BM, BNP>;
+  static_assert(!GATED || BNP == 256, "gated tiles: 128 gate + 128 up columns");
+  constexpr int DMA_SA = S::SA, DMA_SB = S::SB, DMA_STAGE = S::STAGE;
+  constexpr int MB = S::MB, NB = S::NB;             // 16x16 blocks per wave
+  constexpr int WR = 16 * MB;                       // rows per wave
   constexpr int RT = GATED ? 1 : 0;                 // row-token loads per cursor move
-  constexpr int ST = GATED ? 4 * 3 : 4 * 4;         // epilogue stores per wave
+  constexpr int ST = GATED ? MB * 3 : MB * NB;      // epilogue stores per wave
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];  // the three ring stages
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE];
@@ -443,11 +462,11 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   int Lln = Ll + nslots;
   DmaTile tl = dma_tile(g, Ll), tln = tl;
   if (Lln < hi) tln = dma_tile(g, Lln);
-  uint32_t aoff[2], boff[4], soff;
+  uint32_t aoff[S::A_PER], boff[S::B_PER], soff;
   auto no_loads = [&]() {
-    aoff[0] = aoff[1] = soff = kOob;
+    aoff[0] = aoff[S::A_PER - 1] = soff = kOob;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) boff[q] = kOob;
+    for (int q = 0; q < S::B_PER; ++q) boff[q] = kOob;
   };
 
   // gated: tokens of the tile's 128 rows -> rtok[buf] (waves 0, 1; the
@@ -467,18 +486,18 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     const int n0 = t.nt * (GATED ? kBlock : BNP);
     rB = dma_rsrc(g.B + (size_t)t.e * K * N, (uint32_t)K * (uint32_t)N);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {  // A: 1 KB chunk c = rows 8c..8c+7; wave w: chunks 2w, 2w+1
-      const int r = 8 * (2 * wave + q) + (lane >> 3);
+    for (int q = 0; q < S::A_PER; ++q) {  // A: 1 KB chunk c = rows 8c..8c+7; wave w: A_PER chunks
+      const int r = 8 * (S::A_PER * wave + q) + (lane >> 3);
       const int sgm = (lane & 7) ^ swz_a(r);
       aoff[q] = kOob;
       if (r < t.valid) aoff[q] = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)K + 16u * sgm;
     }
-    // B: 1 KB chunk c = K rows 4c..4c+3; wave w: chunks 4w..4w+3; lane -> K row
-    // 4c + lane/16, the 16 bytes of segment (lane & 15) ^ swz_b(kr)
+    // B: 1 KB chunk c = K rows (1024 / BNP) c..; wave w: chunks B_PER w..; lane ->
+    // K row of the chunk lane / SEGS, the 16 bytes of segment (lane % SEGS) ^ swz_b(kr)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int kr = 4 * (4 * wave + q) + (lane >> 4);
-      const int s = (lane & 15) ^ swz_b(kr);
+    for (int q = 0; q < S::B_PER; ++q) {
+      const int kr = (1024 / BNP) * (S::B_PER * wave + q) + lane / S::SEGS;
+      const int s = (lane % S::SEGS) ^ swz_b<S::SEGS>(kr);
       const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
       boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
     }
@@ -501,10 +520,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   auto issue = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
     const uint32_t ka = (uint32_t)kbl * kBlock, kb = ka * (uint32_t)N;
+    if (S::A_WAVES == DMA_WAVES || wave < S::A_WAVES)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) dma16(rA, sbase + (2 * wave + q) * 1024, aoff[q] + ka);
+      for (int q = 0; q < S::A_PER; ++q)
+        dma16(rA, sbase + (S::A_PER * wave + q) * 1024, aoff[q] + ka);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma16(rB, sbase + DMA_SA + (4 * wave + q) * 1024, boff[q] + kb);
+    for (int q = 0; q < S::B_PER; ++q)
+      dma16(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
     dma4(rSide, sbase + DMA_SA + DMA_SB + 256 * wave, soff + (uint32_t)(kbl * side_step));
     ++kbl;
   };
@@ -534,22 +556,23 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 
   // ---- per-lane LDS read offsets (stage-relative)
   // activations: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
-  const int a_row = (wm * 64 + l16) * kBlock;
+  const int a_row = (wm * WR + l16) * kBlock;
   const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
   const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
   // weights: transposing reads of K rows 32gq + 8r + l16/2, half l16 & 1 of a segment
   const int b_row = (32 * gq + (l16 >> 1)) * BNP + 8 * (l16 & 1);
-  const int b_swz = (l16 >> 1) | ((gq & 1) << 3);
+  const int b_swz = swz_b<S::SEGS>(32 * gq + (l16 >> 1));  // the same for the 4 reads
   // tile segment of column block nb: gated 2wn + nb (gate) and 8 + 2wn + nb - 2 (up),
-  // plain 4wn + nb; stored at segment ^ b_swz
-  const int b_base = 16 * ((GATED ? 2 * wn : 4 * wn) ^ b_swz);
+  // plain NB wn + nb; stored at segment ^ b_swz
+  const int b_base = 16 * ((GATED ? 2 * wn : NB * wn) ^ b_swz);
   auto b_seg = [&](int nb) -> int { return GATED ? ((nb & 1) | ((nb >> 1) << 3)) : nb; };
-  const int s_pos = DMA_SA + DMA_SB + SIDE_AS + (wm * 64 + 4 * l16) * 4;
+  // row scale of row r at float 64 (r / 64) + 4 (r % 16) + (r % 64) / 16
+  const int s_pos = DMA_SA + DMA_SB + SIDE_AS + (MB == 4 ? (wm * 64 + 4 * l16) : (4 * l16 + wm)) * 4;
   // bias of block nb: 4 bf16 at columns 4gq.. of the block
   auto bias_pos = [&](int nb) -> int {
     return DMA_SA + DMA_SB + SIDE_BIAS +
            2 * (GATED ? (nb < 2 ? 32 * wn + 16 * nb : 128 + 32 * wn + 16 * (nb - 2))
-                      : 64 * wn + 16 * nb) + 8 * gq;
+                      : 16 * NB * wn + 16 * nb) + 8 * gq;
   };
 
   // ---- compute side: tile tc, K block kbc; the next tile prefetched
@@ -561,7 +584,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     const uint8_t* sA = base;
     const uint8_t* sB = base + DMA_SA;
     const float* sbs = reinterpret_cast<const float*>(base + DMA_SA + DMA_SB + SIDE_BS);
-    const float sb0 = sbs[GATED ? 0 : (wn >> 1)];
+    const float sb0 = sbs[(GATED || BNP == 128) ? 0 : (wn >> 1)];
     const float sb1 = GATED ? sbs[1] : sb0;
     if (kbc == 0) {  // accumulators start from the bias
 #pragma unroll
@@ -575,7 +598,9 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
           for (int mb = 0; mb < MB; ++mb) acc[mb][nb][i] = bv[i];
       }
     }
-    const v4f sa = *reinterpret_cast<const v4f*>(base + s_pos);
+    v4f sa;
+    if constexpr (MB == 4) sa = *reinterpret_cast<const v4f*>(base + s_pos);
+    else sa[0] = *reinterpret_cast<const float*>(base + s_pos);
     v8i xf[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -638,7 +663,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
       // (no memory fence) leaves the next tile's stage loads in flight.
       if (gq == 0)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * 64 + 16 * mb + l16] = pmax[mb];
+        for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * WR + 16 * mb + l16] = pmax[mb];
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -649,7 +674,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
           __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int r = wm * 64 + 16 * mb + l16;
+        const int r = wm * WR + 16 * mb + l16;
         const float amax =
             fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
         const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
@@ -673,10 +698,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
           __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, g.out_bytes, kRsrcWord3);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int gc = n0 + 64 * wn + 16 * nb + 4 * gq;
+        const int gc = n0 + 16 * NB * wn + 16 * nb + 4 * gq;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int r = wm * 64 + 16 * mb + l16;
+          const int r = wm * WR + 16 * mb + l16;
           const uint32_t o = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)N + (uint32_t)gc);
           const v4u d = v4u{__builtin_bit_cast(uint32_t, acc[mb][nb][0]),
                             __builtin_bit_cast(uint32_t, acc[mb][nb][1]),
@@ -694,10 +719,11 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // operations (row tokens, epilogue stores), which may stay in flight.
   // Then a bare s_barrier (a __syncthreads fence would wait for everything).
   auto wait_stage = [&](int pend) {
-    if (pend == 0) wait_vmcnt<DMA_LOADS>();
-    else if (pend == RT) wait_vmcnt<DMA_LOADS + RT>();
-    else if (pend == ST) wait_vmcnt<DMA_LOADS + ST>();
-    else if (pend == RT + ST) wait_vmcnt<DMA_LOADS + RT + ST>();
+    constexpr int NL = S::LOADS_MIN;  // waves that issue more wait for a little more
+    if (pend == 0) wait_vmcnt<NL>();
+    else if (pend == RT) wait_vmcnt<NL + RT>();
+    else if (pend == ST) wait_vmcnt<NL + ST>();
+    else if (pend == RT + ST) wait_vmcnt<NL + RT + ST>();
     else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -761,25 +787,21 @@ int grid_persistent(int max_tiles) {
 
 hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
-  const dim3 grid(grid_for(max_tiles));
+  const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   if (decode)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kGatedDecode.bm, kGatedDecode.bnp, 1, 4, true>), grid,
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, kGatedDecode.bm, kGatedDecode.bnp>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true>), dim3(grid_persistent(max_tiles)),
-                       dim3(DMA_WAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, kGatedPrefill.bm, kGatedPrefill.bnp>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
-  const dim3 grid(grid_for(max_tiles));
+  const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   if (decode)
-    hipLaunchKernelGGL((grouped_gemm_kernel<kPlainDecode.bm, kPlainDecode.bnp, 1, 4, false>), grid,
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, kPlainDecode.bm, kPlainDecode.bnp>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false>), dim3(grid_persistent(max_tiles)),
-                       dim3(DMA_WAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, kPlainPrefill.bm, kPlainPrefill.bnp>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -41,10 +41,10 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
   l.tile_base = put(4 * NT * E);
   l.tile_off0 = put(4 * (E + 1));
   l.tile_off1 = put(4 * (E + 1));
-  // prefill tile lists (row blocks of the prefill tile height)
-  const int64_t mtiles = ceil_div((int)R, moe::kGatedPrefill.bm) + (E < R ? E : R);
+  // tile lists, sized for the shorter (decode) row tiles
+  const int64_t mtiles = ceil_div((int)R, moe::kGatedDecode.bm) + (E < R ? E : R);
   l.tiles0 = put(16 * mtiles * (f / moe::kBlock));
-  l.tiles1 = put(16 * mtiles * ceil_div((int)d, moe::kPlainPrefill.bnp));
+  l.tiles1 = put(16 * mtiles * ceil_div((int)d, moe::kPlainDecode.bnp));
   l.row_of = put(4 * R);
   l.row_token = put(4 * R);
   l.xq = put(T * d);
@@ -161,10 +161,10 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
       case MOE_STAGE_SCAN:
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
                                      tile_base, tile_off0, tile_off1, stream);
-        if (err == hipSuccess && !decode)
+        if (err == hipSuccess)
           err = moe::launch_tile_table(tile_off0, counts, offsets, E, gs.bm, nt_g, max_g, tiles0,
                                        stream);
-        if (err == hipSuccess && !decode)
+        if (err == hipSuccess)
           err = moe::launch_tile_table(tile_off1, counts, offsets, E, ps.bm, nt_p, max_p, tiles1,
                                        stream);
         break;
