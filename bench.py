@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS))
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the steps, one device-to-device copy of this many MiB "
+                         "(a kernel of known traffic for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the MoE block here is "
@@ -111,6 +114,16 @@ def main():
     ws = torch.empty(moe.workspace_bytes(T, d, f, E, k), dtype=torch.uint8, device=dev)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     x = p["x"]
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {n} bytes")
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dbg = moe.forward_debug(x, *w_args, path=args.path)
     torch.cuda.synchronize()

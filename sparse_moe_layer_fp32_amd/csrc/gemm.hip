@@ -28,269 +28,6 @@ namespace moe {
 
 namespace {
 
-constexpr int KP = 144;      // LDS pitch (bytes) of a staged row/column: 128 + 16
-constexpr int B_COLQ = 16;   // extra bytes after every 16 staged B columns (bank spread)
-constexpr int GN = kTileGroup;  // column tiles per group in the tile order
-
-template <int BM, int BNP, int WAVES_M, int WAVES_N, bool GATED>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs g) {
-  constexpr int WM = BM / WAVES_M;
-  constexpr int WN = BNP / WAVES_N;
-  constexpr int MB = WM / 16;
-  constexpr int NB = WN / 16;
-  constexpr int A_LOADS = BM * 8 / 256;
-  constexpr int B_GROUPS = BNP / 16;
-  constexpr int KR = 128 * B_GROUPS / 256;
-  constexpr int SA_BYTES = BM * KP;
-  constexpr int SB_BYTES = BNP * KP + B_GROUPS * B_COLQ;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves");
-  static_assert(KR == 4 || KR == 8, "B staging rows");
-  static_assert(A_LOADS >= 1, "A staging");
-  static_assert(!GATED || BNP == 256, "gated tile = 128 gate + 128 up columns");
-  static_assert(GATED || WN <= 128, "one weight-scale block per wave");
-  static_assert(!GATED || NB % 2 == 0, "gate/up pairs");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SA_BYTES + SB_BYTES + BM * 4];
-  uint8_t* sA = smem;
-  uint8_t* sB = smem + SA_BYTES;
-  float* sAs = reinterpret_cast<float*>(smem + SA_BYTES + SB_BYTES);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
-
-  // ---- which tile: XCD-contiguous slice of the tile table
-  const int total = g.tile_off[g.E];
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  if (slot >= chunk) return;
-  const int L = xcd * chunk + slot;
-  if (L >= total) return;
-  int lo = 0, hi = g.E;  // tile_off[lo] <= L < tile_off[hi]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (g.tile_off[mid] <= L) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int cnt = g.counts[e];
-  const int mt = ceil_div(cnt, BM);
-  const int local = L - g.tile_off[e];
-  const int ng = local / (mt * GN);
-  const int rem = local - ng * mt * GN;
-  const int gw = min(GN, g.n_tiles - ng * GN);
-  const int m = rem / gw, nt = ng * GN + rem % gw;
-  const int row0 = g.offsets[e] + m * BM;
-  const int valid = min(BM, cnt - m * BM);
-  const int n0 = nt * (GATED ? kBlock : BNP);  // gated: first h column; plain: first column
-
-  // global column of tile column p
-  auto gcol_of = [&](int p) -> int {
-    if (GATED) return p < BNP / 2 ? n0 + p : g.f + n0 + (p - BNP / 2);
-    return n0 + p;
-  };
-
-  // ---- staging sources (fixed for the tile)
-  const uint8_t* a_src[A_LOADS];
-  int a_lds[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int idx = tid + 256 * i, r = idx >> 3, seg = idx & 7;
-    a_lds[i] = r * KP + seg * 16;
-    a_src[i] = nullptr;
-    if (r < valid) {
-      const int arow = GATED ? g.row_token[row0 + r] : row0 + r;
-      a_src[i] = g.A + (size_t)arow * K + seg * 16;
-    }
-  }
-  const float* as_src = nullptr;
-  if (tid < valid) {
-    const int arow = GATED ? g.row_token[row0 + tid] : row0 + tid;
-    as_src = g.As + (size_t)arow * nkb;
-  }
-  const int bgrp = tid % B_GROUPS, kgrp = tid / B_GROUPS;
-  const int bgcol = gcol_of(bgrp * 16);
-  const uint8_t* b_src =
-      bgcol < N ? g.B + (size_t)e * K * N + (size_t)(kgrp * KR) * N + bgcol : nullptr;
-  const int b_lds = bgrp * 16 * KP + bgrp * B_COLQ + kgrp * KR;
-
-  uint4 ra[A_LOADS];
-  uint4 rb[KR];
-  float ras = 0.f;
-  auto stage_load = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + kb * kBlock)
-                       : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int r = 0; r < KR; ++r)
-      rb[r] = b_src ? *reinterpret_cast<const uint4*>(b_src + (size_t)(kb * kBlock + r) * N)
-                    : make_uint4(0u, 0u, 0u, 0u);
-    ras = as_src ? as_src[kb] : 0.f;
-  };
-  auto stage_store = [&]() {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(sA + a_lds[i]) = ra[i];
-    if (tid < BM) sAs[tid] = ras;
-    // KR rows x 16 columns (bytes) -> 16 columns x KR rows
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t w0 = q == 0 ? rb[0].x : q == 1 ? rb[0].y : q == 2 ? rb[0].z : rb[0].w;
-      const uint32_t w1 = q == 0 ? rb[1].x : q == 1 ? rb[1].y : q == 2 ? rb[1].z : rb[1].w;
-      const uint32_t w2 = q == 0 ? rb[2].x : q == 1 ? rb[2].y : q == 2 ? rb[2].z : rb[2].w;
-      const uint32_t w3 = q == 0 ? rb[3].x : q == 1 ? rb[3].y : q == 2 ? rb[3].z : rb[3].w;
-      uint32_t c0, c1, c2, c3;
-      transpose4x4(w0, w1, w2, w3, c0, c1, c2, c3);
-      if constexpr (KR == 8) {
-        const uint32_t w4 = q == 0 ? rb[4].x : q == 1 ? rb[4].y : q == 2 ? rb[4].z : rb[4].w;
-        const uint32_t w5 = q == 0 ? rb[5].x : q == 1 ? rb[5].y : q == 2 ? rb[5].z : rb[5].w;
-        const uint32_t w6 = q == 0 ? rb[6].x : q == 1 ? rb[6].y : q == 2 ? rb[6].z : rb[6].w;
-        const uint32_t w7 = q == 0 ? rb[7].x : q == 1 ? rb[7].y : q == 2 ? rb[7].z : rb[7].w;
-        uint32_t d0, d1, d2, d3;
-        transpose4x4(w4, w5, w6, w7, d0, d1, d2, d3);
-        *reinterpret_cast<uint2*>(sB + b_lds + (4 * q + 0) * KP) = make_uint2(c0, d0);
-        *reinterpret_cast<uint2*>(sB + b_lds + (4 * q + 1) * KP) = make_uint2(c1, d1);
-        *reinterpret_cast<uint2*>(sB + b_lds + (4 * q + 2) * KP) = make_uint2(c2, d2);
-        *reinterpret_cast<uint2*>(sB + b_lds + (4 * q + 3) * KP) = make_uint2(c3, d3);
-      } else {
-        *reinterpret_cast<uint32_t*>(sB + b_lds + (4 * q + 0) * KP) = c0;
-        *reinterpret_cast<uint32_t*>(sB + b_lds + (4 * q + 1) * KP) = c1;
-        *reinterpret_cast<uint32_t*>(sB + b_lds + (4 * q + 2) * KP) = c2;
-        *reinterpret_cast<uint32_t*>(sB + b_lds + (4 * q + 3) * KP) = c3;
-      }
-    }
-  };
-
-  // ---- wave's column blocks (tile columns) and their weight-scale block
-  auto colbase = [&](int nb) -> int {
-    if (GATED)
-      return nb < NB / 2 ? wn * (WN / 2) + nb * 16 : BNP / 2 + wn * (WN / 2) + (nb - NB / 2) * 16;
-    return wn * WN + nb * 16;
-  };
-  // scale-block column index for the gate (0) and up (1) halves, or the plain block
-  int sblk[2];
-  sblk[0] = gcol_of(colbase(0)) / kBlock;
-  sblk[1] = GATED ? gcol_of(colbase(NB / 2)) / kBlock : sblk[0];
-  const float* bs_e = g.Bs + (size_t)e * nkb * nsb;
-
-  // ---- accumulators start at the bias (once per output tile)
-  v4f acc[MB][NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int gc = gcol_of(colbase(nb) + (lane & 15));
-    const float bv = gc < N ? bf16_to_f32(g.bias[(size_t)e * N + gc]) : 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) acc[mb][nb] = v4f{bv, bv, bv, bv};
-  }
-
-  stage_load(0);
-  for (int kb = 0; kb < nkb; ++kb) {
-    __syncthreads();
-    stage_store();
-    __syncthreads();
-    if (kb + 1 < nkb) stage_load(kb + 1);
-
-    const float sb0 = sblk[0] < nsb ? bs_e[(size_t)kb * nsb + sblk[0]] : 0.f;
-    const float sb1 = sblk[1] < nsb ? bs_e[(size_t)kb * nsb + sblk[1]] : 0.f;
-    v8i af[MB];
-    v4f rs0[MB], rs1[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int r = wm * WM + mb * 16;
-      const uint8_t* pa = sA + (r + (lane & 15)) * KP + 32 * (lane >> 4);
-      const v4i lo4 = *reinterpret_cast<const v4i*>(pa);
-      const v4i hi4 = *reinterpret_cast<const v4i*>(pa + 16);
-      af[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      const v4f rsv = *reinterpret_cast<const v4f*>(sAs + r + 4 * (lane >> 4));
-      rs0[mb] = rsv * sb0;
-      rs1[mb] = rsv * sb1;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int cb = colbase(nb);
-      const uint8_t* pb = sB + (cb + (lane & 15)) * KP + (cb >> 4) * B_COLQ + 32 * (lane >> 4);
-      const v4i lo4 = *reinterpret_cast<const v4i*>(pb);
-      const v4i hi4 = *reinterpret_cast<const v4i*>(pb + 16);
-      const v8i bf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const v4f p = mfma_fp8_16x16x128(af[mb], bf, v4f{0.f, 0.f, 0.f, 0.f});
-        const v4f sc = (GATED && nb >= NB / 2) ? rs1[mb] : rs0[mb];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(p[i], sc[i], acc[mb][nb][i]);
-      }
-    }
-  }
-
-  if constexpr (GATED) {
-    // ---- SwiGLU, then per-row 1x128 e4m3 quantisation of h over the tile's
-    // 128 h columns (spread over WAVES_N waves)
-    constexpr int NH = NB / 2;
-    float* sRed = reinterpret_cast<float*>(sB);           // [WAVES_N][BM] row maxima
-    uint8_t* sQ = sA;                                      // [BM][128] h codes
-    float h[MB][NH][4];
-    float rmax[MB][4];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float mx = 0.f;
-#pragma unroll
-        for (int nb = 0; nb < NH; ++nb) {
-          const float gv = acc[mb][nb][i], uv = acc[mb][nb + NH][i];
-          const float hv = gv / (1.0f + expf(-gv)) * uv;
-          h[mb][nb][i] = hv;
-          mx = fmaxf(mx, fabsf(hv));
-        }
-        rmax[mb][i] = max16(mx);
-      }
-    __syncthreads();  // all waves are done with sA / sB
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sRed[wn * BM + wm * WM + mb * 16 + 4 * (lane >> 4) + i] = rmax[mb][i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wm * WM + mb * 16 + 4 * (lane >> 4) + i;
-        float amax = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES_N; ++w) amax = fmaxf(amax, sRed[w * BM + r]);
-        const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-#pragma unroll
-        for (int nb = 0; nb < NH; ++nb) {
-          const float y = fminf(fmaxf(h[mb][nb][i] / s, -kFp8Max), kFp8Max);
-          sQ[r * kBlock + wn * (WN / 2) + nb * 16 + (lane & 15)] =
-              static_cast<uint8_t>(f32x2_to_e4m3(y, 0.f) & 0xffu);
-        }
-        if (wn == 0 && (lane & 15) == 0 && r < valid)
-          g.Hs[(size_t)(row0 + r) * (g.f / kBlock) + nt] = s;
-      }
-    __syncthreads();
-    for (int idx = tid; idx < BM * 8; idx += 256) {
-      const int r = idx >> 3, seg = idx & 7;
-      if (r < valid)
-        *reinterpret_cast<uint4*>(g.Hq + (size_t)(row0 + r) * g.f + n0 + seg * 16) =
-            *reinterpret_cast<const uint4*>(sQ + r * kBlock + seg * 16);
-    }
-  } else {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int gc = gcol_of(colbase(nb) + (lane & 15));
-        if (gc >= N) continue;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * WM + mb * 16 + 4 * (lane >> 4) + i;
-          if (r < valid) g.Y[(size_t)(row0 + r) * N + gc] = acc[mb][nb][i];
-        }
-      }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Prefill kernel: persistent, direct global->LDS loads into a 3-stage ring,
 // 8 waves.
@@ -353,9 +90,12 @@ constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
 
 typedef __attribute__((address_space(4))) int32_t const_i32;
 
-// A row r keeps its 16-byte segment s at position s ^ (r & 7): the 8 rows that
-// one 128-byte LDS cycle of a ds_read_b128 serves sit in 8 distinct positions.
-__device__ __forceinline__ int swz_a(int r) { return r & 7; }
+// A row r keeps its 16-byte segment s at position s ^ swz_a(r), with the
+// XOR key built from row bits 2, 0, 1 (in that order).  The fragment reads
+// (16 rows x 2 segments per lane group) then run without LDS bank conflicts;
+// measured on gfx950 with the SQ_LDS_BANK_CONFLICT counter, where the keys
+// r & 7 and (r >> 1) & 7 cost one extra cycle per read cycle.
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 2) & 1) | ((r & 3) << 1); }
 template <int SEGS>
 __device__ __forceinline__ int swz_b(int kr) {
   return SEGS == 16 ? (kr & 7) | (((kr >> 5) & 1) << 3) : (kr & 7);
@@ -404,6 +144,26 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff) {
       : "=&s"(saved)
       : "s"(lds), "v"(voff), "s"(rsrc)
       : "memory");
+}
+// The same loads without a memory clobber, for loads into a stage that no
+// LDS access of the current step touches: the compiler may then move LDS
+// reads across them.  They stay ordered with the ring's fenced barriers and
+// with every other volatile asm.
+__device__ __forceinline__ void dma16n(v4i rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc));
+}
+__device__ __forceinline__ void dma4n(v4i rsrc, uint32_t lds, uint32_t voff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc));
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
@@ -766,6 +526,413 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   wait_vmcnt<0>();  // the loads past the last tile land before the workgroup ends
 }
 
+// ---------------------------------------------------------------------------
+// Wide prefill kernel: 192 x 256 tiles, 8 waves of 96 x 64, weights three K
+// blocks deep and activations two.
+//
+// A wave owning 96 rows x 64 columns reads 28 fragments from LDS per 24 MFMAs
+// (the 64 x 64 waves of the kernel above read 24 per 16), which keeps the
+// LDS read rate below the FP8 MFMA rate with room for the stage writes.  The
+// promotion of each 128-deep MFMA result (4 FMAs per lane) is issued two
+// MFMAs after it, so the VALU work of one wave runs under the MFMAs of the
+// other wave on its SIMD.
+//
+// LDS: activation stages A [192][128] (segment s of row r at s ^ swz_a(r))
+// with a 2 KB side area each, two deep; weight stages B [128 K][256 N]
+// (segment s of K row kr at s ^ swz_b<16>(kr)), three deep, so a weight
+// slice is requested two K blocks before it is read: the tiles that share a
+// slice all request it at about the same time, and the first of them waits
+// for HBM.  Side area: [0, 1 KB) the A row scales of the K block, row
+// 96 wm + 16 mb + l16 at float 128 wm + 8 l16 + mb (waves 0-3); [1 KB,
+// 1.5 KB) the tile's 256 bias values (waves 4, 5); [1.5 KB, +8) the two
+// weight-block scales of the K block (wave 6).  The bias is added in the
+// epilogue (the accumulator initialisation, reordered; equal up to fp32
+// rounding).
+//
+// Rows: waves wm = 0 / 1 own tile rows 0-95 / 96-191; a wave whose half has
+// no valid row skips its MFMAs, so a ragged tail tile of <= 96 rows costs
+// about half a tile.  Persistent over the tile list; the loads run ahead
+// across tile boundaries (the next tile's first blocks load while the
+// current tile ends).
+constexpr int WM_ROWS = 192, WN_COLS = 256, W_HALF = WM_ROWS / 2;
+constexpr int W_SA = WM_ROWS * kBlock, W_SB = kBlock * WN_COLS, W_SIDE = 2048;
+constexpr int W_ASTAGE = W_SA + W_SIDE;
+constexpr int W_SIDE_BIAS = 1024, W_SIDE_BS = 1536;
+constexpr int W_AQ = W_SA / 1024 / DMA_WAVES;       // A chunks (1 KB) per wave: 3
+constexpr int W_BQ = W_SB / 1024 / DMA_WAVES;       // B chunks per wave: 4
+
+template <bool GATED>
+__global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(GemmArgs g) {
+  constexpr int MB = W_HALF / 16, NB = 4;            // 16 x 16 blocks per wave: 6 x 4
+  constexpr int RT = GATED ? 1 : 0;                  // row-token loads per A-cursor tile move
+  constexpr int ST = GATED ? MB * 3 : MB * NB;       // epilogue stores per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[W_ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[W_ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[W_SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[W_SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb2[W_SB];
+  __shared__ float smax[GATED ? 4 * WM_ROWS : 1];    // row maxima per wave column
+  __shared__ int32_t rtok[GATED ? 2 : 1][GATED ? DMA_WAVES * 64 : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int gq = lane >> 4, l16 = lane & 15;
+  const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
+
+  const int total = ((const const_i32*)g.tile_off)[g.E];
+  const int nslots = gridDim.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int lo = (blockIdx.x & 7) * chunk;
+  const int hi = min(total, lo + chunk);
+  const int L0 = lo + (blockIdx.x >> 3);
+  if (L0 >= hi) return;
+
+  const v4i rA = dma_rsrc(g.A, g.A_bytes);
+  const v4i rSide = wave < 4   ? dma_rsrc(g.As, g.As_bytes)
+                    : wave < 6 ? dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N)
+                               : dma_rsrc(g.Bs, 4u * (uint32_t)g.E * nkb * nsb);
+  const int side_step = wave < 4 ? 4 : (wave == 6 ? 4 * nsb : 0);
+
+  // ---- A cursor (activations + side area, one K block ahead of compute)
+  int La = L0, kba = 0, rb = 0;
+  int Lan = La + nslots;
+  DmaTile ta = dma_tile(g, La), tan = ta;
+  if (Lan < hi) tan = dma_tile(g, Lan);
+  uint32_t aoff[W_AQ], soff;
+  // ---- B cursor (weights, two K blocks ahead of compute)
+  int Lb = L0, kbb = 0;
+  DmaTile tb = ta;
+  uint32_t boff[W_BQ];
+  v4i rB;
+
+  auto rt_load = [&](const DmaTile& t, bool live, int buf) {
+    if constexpr (GATED) {
+      const int r = 64 * wave + lane;
+      const uint32_t o = (live && wave < 3 && r < t.valid) ? 4u * (uint32_t)(t.row0 + r) : kOob;
+      dma4(dma_rsrc(g.row_token, g.rows_bytes), lds_addr(&rtok[buf][64 * wave]), o);
+    }
+  };
+  auto setup_a = [&](const DmaTile& t, int buf) {
+#pragma unroll
+    for (int q = 0; q < W_AQ; ++q) {  // chunk W_AQ wave + q: rows 8 chunk + lane / 8
+      const int r = 8 * (W_AQ * wave + q) + (lane >> 3);
+      const int sgm = (lane & 7) ^ swz_a(r);
+      aoff[q] = kOob;
+      if (r < t.valid)
+        aoff[q] = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)K + 16u * sgm;
+    }
+    const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
+    soff = kOob;
+    if (wave < 4) {  // the scale of row 96 wm + 16 mb + l16 lands at float 128 wm + 8 l16 + mb
+      const int i = 64 * wave + lane;
+      const int mb = i & 7;
+      const int r = W_HALF * (i >> 7) + 16 * mb + ((i >> 3) & 15);
+      if (mb < MB && r < t.valid)
+        soff = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)nkb * 4u;
+    } else if (wave < 6) {  // bias: 128 tile columns (bf16 pairs) per wave
+      const int c = (GATED ? (wave == 4 ? n0 : g.f + n0) : n0 + 128 * (wave - 4)) + 2 * lane;
+      if (c < N) soff = 2u * ((uint32_t)t.e * (uint32_t)N + (uint32_t)c);
+    } else if (wave == 6 && lane < 2) {
+      const int sb = GATED ? (lane == 0 ? n0 : g.f + n0) / kBlock : n0 / kBlock + lane;
+      if (sb < nsb) soff = 4u * ((uint32_t)t.e * (uint32_t)nkb * (uint32_t)nsb + (uint32_t)sb);
+    }
+  };
+  auto setup_b = [&](const DmaTile& t) {
+    const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
+    rB = dma_rsrc(g.B + (size_t)t.e * K * N, (uint32_t)K * (uint32_t)N);
+#pragma unroll
+    for (int q = 0; q < W_BQ; ++q) {  // chunk W_BQ wave + q: K rows 4 chunk + lane / 16
+      const int kr = 4 * (W_BQ * wave + q) + (lane >> 4);
+      const int s = (lane & 15) ^ swz_b<16>(kr);
+      const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
+      boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
+    }
+  };
+  // The loads of one step: A chunks and the side area of block kba into the
+  // next A stage before the compute, B chunks of block kbb into the next B
+  // stage after it.  Issued in one burst after the barrier, the 64 loads of
+  // a step fill the address queues and stall every wave's instruction stream
+  // (MFMAs included) until they drain; two bursts of 32, one at each end of
+  // the compute, do not.  Every load is issued on every path, also past the
+  // last tile (the offsets then point past the buffers and the loads land as
+  // zeros in a stage no one reads), so the in-flight count is the same on
+  // every path.
+  auto issue_a = [&](uint8_t* base) {
+    const uint32_t sbase = lds_addr(base);
+    const uint32_t ka = (uint32_t)kba * kBlock;
+#pragma unroll
+    for (int q = 0; q < W_AQ; ++q) dma16(rA, sbase + (W_AQ * wave + q) * 1024, aoff[q] + ka);
+    dma4(rSide, sbase + W_SA + 256 * wave, soff + (uint32_t)(kba * side_step));
+    ++kba;
+  };
+  auto issue_b = [&](uint8_t* base) {
+    const uint32_t sbase = lds_addr(base);
+    const uint32_t kb = (uint32_t)kbb * kBlock * (uint32_t)N;
+#pragma unroll
+    for (int q = 0; q < W_BQ; ++q) dma16(rB, sbase + (W_BQ * wave + q) * 1024, boff[q] + kb);
+    ++kbb;
+  };
+  // Cursor moves after a tile's last K block has been issued.
+  auto advance_b = [&]() {
+    if (kbb < nkb) return;
+    kbb = 0;
+    Lb += nslots;
+    if (Lb < hi) {
+      tb = dma_tile(g, Lb);
+      setup_b(tb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W_BQ; ++q) boff[q] = kOob;
+    }
+  };
+  auto advance_a = [&]() -> int {
+    if (kba < nkb) return 0;
+    kba = 0;
+    La = Lan;
+    ta = tan;
+    rb ^= 1;
+    Lan += nslots;
+    if (Lan < hi) tan = dma_tile(g, Lan);
+    if (nkb == 1) {  // the row tokens were loaded one K block ago: wait for them
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    if (La < hi) {
+      setup_a(ta, rb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W_AQ; ++q) aoff[q] = kOob;
+      soff = kOob;
+    }
+    // the previous readers of rtok[rb ^ 1] are past a ring barrier
+    rt_load(tan, Lan < hi, rb ^ 1);
+    return RT;
+  };
+
+  // ---- per-lane LDS read offsets
+  const int a_row = (wm * W_HALF + l16) * kBlock;
+  const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
+  const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
+  const int b_row = (32 * gq + (l16 >> 1)) * WN_COLS + 8 * (l16 & 1);
+  const int b_swz = swz_b<16>(32 * gq + (l16 >> 1));
+  // tile B segment of block nb: gated gate 2wn + nb, up 8 + 2wn + nb - 2; plain 4wn + nb
+  auto b_off = [&](int nb) -> int {
+    const int seg = GATED ? (nb < 2 ? 2 * wn + nb : 8 + 2 * wn + nb - 2) : 4 * wn + nb;
+    return b_row + 16 * (seg ^ b_swz);
+  };
+  const int s_pos = W_SA + (wm * 128 + 8 * l16) * 4;
+
+  DmaTile tc = ta;
+  int Lc = L0, kbc = 0;
+  float acc[MB][NB][4];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
+
+  auto compute = [&](const uint8_t* abase, const uint8_t* bbase) {
+    if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
+    const float* sbs = reinterpret_cast<const float*>(abase + W_SA + W_SIDE_BS);
+    const v4f sl = *reinterpret_cast<const v4f*>(abase + s_pos);
+    const v2f sh = *reinterpret_cast<const v2f*>(abase + s_pos + 16);
+    const float sb0 = GATED ? sbs[0] : sbs[wn >> 1];
+    const float sb1 = GATED ? sbs[1] : sb0;
+    v8i wf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(bbase + b_off(nb) + r * 8 * WN_COLS));
+        wf[nb][2 * r] = t[0];
+        wf[nb][2 * r + 1] = t[1];
+      }
+    // MB * NB MFMAs j = 4 mb + nb; the FMAs of MFMA j follow MFMA j + 2
+    v4f pp[MB * NB];
+    v8i xf[MB];
+#pragma unroll
+    for (int j = 0; j < MB * NB + 2; ++j) {
+      if (j < MB * NB) {
+        const int mb = j >> 2, nb = j & 3;
+        if (nb == 0) {
+          const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
+          const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
+          const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
+          xf[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+        pp[j] = mfma_fp8_16x16x128(wf[nb], xf[mb], v4f{0.f, 0.f, 0.f, 0.f});
+      }
+      if (j >= 2) {
+        const int q = j - 2, mb = q >> 2, nb = q & 3;
+        const float sa = mb < 4 ? sl[mb] : sh[mb - 4];
+        const float s = sa * ((GATED && nb >= 2) ? sb1 : sb0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = fmaf(pp[q][i], s, acc[mb][nb][i]);
+      }
+    }
+  };
+
+  // lane -> rows 96 wm + 16 mb + l16, columns 4 gq.. of each 16-column block
+  auto epilogue = [&](const DmaTile& t, const uint8_t* abase) {
+    const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
+    const uint8_t* sbias = abase + W_SA + W_SIDE_BIAS;
+    if constexpr (GATED) {
+      float bg[2][4], bu[2][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint2 wg = *reinterpret_cast<const uint2*>(sbias + 2 * (32 * wn + 16 * j + 4 * gq));
+        const uint2 wu = *reinterpret_cast<const uint2*>(sbias + 2 * (128 + 32 * wn + 16 * j + 4 * gq));
+        bg[j][0] = bf16_to_f32(wg.x & 0xffffu); bg[j][1] = bf16_to_f32(wg.x >> 16);
+        bg[j][2] = bf16_to_f32(wg.y & 0xffffu); bg[j][3] = bf16_to_f32(wg.y >> 16);
+        bu[j][0] = bf16_to_f32(wu.x & 0xffffu); bu[j][1] = bf16_to_f32(wu.x >> 16);
+        bu[j][2] = bf16_to_f32(wu.y & 0xffffu); bu[j][3] = bf16_to_f32(wu.y >> 16);
+      }
+      float pmax[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[mb][j][i] + bg[j][i], uv = acc[mb][2 + j][i] + bu[j][i];
+            // silu with the hardware exp2 and reciprocal (relative error ~1e-7,
+            // far below the e4m3 spacing h is rounded to)
+            const float ex = __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f);
+            const float hv = gv * __builtin_amdgcn_rcpf(1.0f + ex) * uv;
+            acc[mb][j][i] = hv;
+            mx = fmaxf(mx, fabsf(hv));
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      // row maxima over the four wave columns through LDS.  The previous
+      // tile's readers are past at least one ring barrier; a bare s_barrier
+      // (no memory fence) leaves the stage loads in flight.
+      if (gq == 0)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) smax[wn * WM_ROWS + wm * W_HALF + 16 * mb + l16] = pmax[mb];
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const __amdgpu_buffer_rsrc_t rH =
+          __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rHs =
+          __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = wm * W_HALF + 16 * mb + l16;
+        const float amax = fmaxf(fmaxf(smax[r], smax[WM_ROWS + r]),
+                                 fmaxf(smax[2 * WM_ROWS + r], smax[3 * WM_ROWS + r]));
+        const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+        const float inv = 1.0f / s;
+        const bool ok = r < t.valid;
+        const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float q[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[mb][j][i] * inv, -kFp8Max), kFp8Max);
+          __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
+                                                ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+        }
+        const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
+                                              (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rY =
+          __builtin_amdgcn_make_buffer_rsrc(g.Y, (short)0, g.out_bytes, kRsrcWord3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int cl = 64 * wn + 16 * nb + 4 * gq;  // tile column
+        const uint2 wb = *reinterpret_cast<const uint2*>(sbias + 2 * cl);
+        const float b4[4] = {bf16_to_f32(wb.x & 0xffffu), bf16_to_f32(wb.x >> 16),
+                             bf16_to_f32(wb.y & 0xffffu), bf16_to_f32(wb.y >> 16)};
+        const int gc = n0 + cl;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * W_HALF + 16 * mb + l16;
+          const uint32_t o = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)N + (uint32_t)gc);
+          const v4u d = v4u{__builtin_bit_cast(uint32_t, acc[mb][nb][0] + b4[0]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][1] + b4[1]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][2] + b4[2]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][3] + b4[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, rY, (r < t.valid && gc < N) ? (int)o : (int)kOob,
+                                                 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
+  };
+
+  // Ring wait: this wave's loads of the A stage about to be read (and, older,
+  // of the B stage) are done; younger are the next B stage's W_BQ loads and
+  // `pend` row-token loads and epilogue stores.  Then a bare s_barrier.
+  auto wait_stage = [&](int pend) {
+    if (pend == 0) wait_vmcnt<W_BQ>();
+    else if (pend == RT) wait_vmcnt<W_BQ + RT>();
+    else if (pend == ST) wait_vmcnt<W_BQ + ST>();
+    else if (pend == RT + ST) wait_vmcnt<W_BQ + RT + ST>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // ---- prologue: row tokens of the first two tiles, then B of K blocks 0
+  // and 1 and A of K block 0 (the B stages are older than the A stage)
+  rt_load(ta, true, 0);
+  rt_load(tan, Lan < hi, 1);
+  if constexpr (GATED) {
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  setup_a(ta, 0);
+  setup_b(tb);
+  issue_b(sb0);
+  advance_b();
+  int pend = 0;
+  issue_a(sa0);
+  pend = advance_a();
+  issue_b(sb1);
+  advance_b();
+
+  // One K block: compute reads A stage i % 2 and B stage i % 3; loads A of
+  // block i + 1 and B of block i + 2.  Returns false after the last tile.
+  auto step = [&](const uint8_t* ca, uint8_t* na, const uint8_t* cb, uint8_t* nb2) -> bool {
+    wait_stage(pend);
+    issue_a(na);
+    compute(ca, cb);
+    issue_b(nb2);
+    pend = advance_a();
+    advance_b();
+    if (++kbc < nkb) return true;
+    epilogue(tc, ca);
+    pend += ST;
+    Lc += nslots;
+    if (Lc >= hi) return false;
+    kbc = 0;
+    tc = dma_tile(g, Lc);
+    return true;
+  };
+  while (step(sa0, sa1, sb0, sb2) && step(sa1, sa0, sb1, sb0) && step(sa0, sa1, sb2, sb1) &&
+         step(sa1, sa0, sb0, sb2) && step(sa0, sa1, sb1, sb0) && step(sa1, sa0, sb2, sb1)) {
+  }
+  wait_vmcnt<0>();  // the loads past the last tile land before the workgroup ends
+}
+
 int grid_for(int max_tiles) { return 8 * ceil_div(max_tiles, 8); }
 
 // Persistent prefill grid: one workgroup per CU (a multiple of 8, one slice
@@ -788,20 +955,22 @@ int grid_persistent(int max_tiles) {
 hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
+  static_assert(kGatedPrefill.bm == WM_ROWS && kGatedPrefill.bnp == WN_COLS, "wide tile");
   if (decode)
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, kGatedDecode.bm, kGatedDecode.bnp>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, kGatedPrefill.bm, kGatedPrefill.bnp>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(grouped_gemm_wide_kernel<true>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
+  static_assert(kPlainPrefill.bm == WM_ROWS && kPlainPrefill.bnp == WN_COLS, "wide tile");
   if (decode)
     hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, kPlainDecode.bm, kPlainDecode.bnp>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, kPlainPrefill.bm, kPlainPrefill.bnp>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(grouped_gemm_wide_kernel<false>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

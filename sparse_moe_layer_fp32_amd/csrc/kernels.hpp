@@ -19,9 +19,9 @@ struct GemmShape {
   int bm;       // rows per tile
   int bnp;      // B columns per tile (gate+up columns for the gated kernel)
 };
-constexpr GemmShape kGatedPrefill{128, 256};
+constexpr GemmShape kGatedPrefill{192, 256};
 constexpr GemmShape kGatedDecode{32, 256};
-constexpr GemmShape kPlainPrefill{128, 256};
+constexpr GemmShape kPlainPrefill{192, 256};
 constexpr GemmShape kPlainDecode{32, 128};
 
 struct GemmArgs {
