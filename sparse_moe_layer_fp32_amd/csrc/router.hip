@@ -8,23 +8,18 @@
 // token per 128 columns so that every 128-deep K block of the expert GEMMs has
 // one activation scale per row.
 //
-// Design: every wave owns 16 tokens and its own LDS rows (the workgroup
-// barriers only order each wave's LDS writes before its cross-lane reads).
-// Per 128-column group a wave stages its x rows in LDS, quantises them, and
-// accumulates fp32 logits with v_mfma_f32_16x16x4_f32,
-// reading W_router [d, E] straight from memory (16 consecutive experts of one
-// row are 64 contiguous bytes, exactly the B operand of one lane group).  The
-// logits are summed per 128-column group and then across groups (blocked sum).
-// Small batches split the K range over workgroups (partial logits in the
-// workspace, then router_topk_kernel); large batches finish top-k in place.
+// Design: every wave owns 16 tokens.  The logits run on the bf16 matrix
+// cores with each fp32 router weight split into three exact bf16 parts, so
+// they carry fp32 accumulation error only (see router_kernel).  Small
+// batches split the K range over workgroups (partial logits in the
+// workspace, summed in split order by router_finish_kernel); large batches
+// finish top-k in place.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 namespace {
-
-constexpr int XP = kBlock + 4;  // LDS pitch (floats) of a staged x row
 
 __device__ __forceinline__ uint32_t ordered_key(float v) {
   uint32_t u = __float_as_uint(v);
@@ -107,147 +102,181 @@ __device__ void topk_emit(const v4f (&tot)[NBW], const float* __restrict__ br, i
   }
 }
 
-// W_router rows staged per step: a whole 128-row group for E <= 128, half a
-// group for larger E (keeps the LDS slice at <= 64 KB).
-constexpr int wr_rows(int nbw) { return nbw <= 8 ? kBlock : kBlock / 2; }
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// fp32 -> three bf16 parts whose sum is exactly w: each part keeps the top 8
+// significant bits of what the previous parts left (truncation), and a
+// float's 24-bit significand splits into three such pieces.
+__device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t b0 = __float_as_uint(w) & 0xffff0000u;
+  const float r1 = w - __uint_as_float(b0);  // exact
+  const uint32_t b1 = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(b1);  // exact, at most 8 significant bits
+  hi = b0 >> 16;
+  mid = b1 >> 16;
+  lo = __float_as_uint(r2) >> 16;
+}
+
+// W_router rows converted per LDS fill: a whole 128-column group for up to 64
+// experts, fewer rows for more experts (the three planes stay <= 61 KB).
+constexpr int w_fill(int nbw) { return nbw <= 4 ? kBlock : nbw <= 8 ? kBlock / 2 : kBlock / 4; }
 
 // grid = (token tiles of RT_TT, K splits); 4 waves x 16 tokens per workgroup.
-// Per step the workgroup loads one W_router slice [WR_ROWS][16*NBW] into LDS
-// with every load in flight, and prefetches the next slice (and, at a group
-// boundary, the next x rows) into registers while the waves compute.
+//
+// Logits l = x . W_router run on v_mfma_f32_16x16x32_bf16: x is bf16 and each
+// fp32 router weight is split into three bf16 parts (hi + mid + lo, exact),
+// so every product x * part is exact in fp32 and the MFMA sums them in fp32:
+// the logits carry fp32 accumulation error only (summed per 128-column group,
+// then across groups).  The workgroup converts the W_router rows of its K
+// range into three K-contiguous bf16 planes in LDS (the MFMA's B operand);
+// the x fragments (A operand, 8 consecutive bf16 per lane) come straight from
+// memory.  The same registers feed the per-token 1x128 e4m3 quantisation of x.
+// One split: top-k + softmax + tile histogram in place; several: partial
+// logits [split][T][E] for router_finish_kernel.
 template <int NBW>
 __global__ __launch_bounds__(256) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int k, int groups_per_split, float* __restrict__ partial,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist,
     uint8_t* __restrict__ xq, float* __restrict__ xs) {
-  constexpr int EP = NBW * 16;                 // experts padded to 16
-  constexpr int WP = EP + 16;                  // LDS pitch (floats) of a staged W_router row
-  constexpr int WR = wr_rows(NBW);             // rows per step
-  constexpr int STEPS = kBlock / WR;           // steps per 128-column group
-  constexpr int WV = WR * EP / 4 / 256;        // float4 per thread per step
-  static_assert(WR * EP % 1024 == 0, "slice divides over 256 threads");
-  __shared__ float sxw[4][16 * XP];
-  __shared__ __attribute__((aligned(16))) float sw[WR * WP];
+  constexpr int EP = NBW * 16;                   // experts padded to 16
+  constexpr int KC = w_fill(NBW);                // W rows per fill
+  constexpr int PITCH = 2 * KC + 16;             // bytes per expert row of a plane
+  constexpr int UNITS = EP * KC / 8;             // (expert, 8 rows) conversion units
+  constexpr int UPT = (UNITS + 255) / 256;       // units per thread
+  constexpr int FILLS = kBlock / KC;             // fills per group
+  __shared__ __attribute__((aligned(16))) uint8_t wl[3 * EP * PITCH];
   __shared__ int shist[kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
   const int t0 = blockIdx.x * RT_TT + wave * 16;  // this wave's first token
   const int ngroups = d / kBlock;
   const int g0 = blockIdx.y * groups_per_split;
   const int g1 = min(ngroups, g0 + groups_per_split);
   const bool fused = gridDim.y == 1;
-  float* sx = sxw[wave];
   if (fused)
     for (int i = tid; i < E; i += 256) shist[i] = 0;
 
-  // x rows of this wave: lane -> row lane/4, 32 columns
-  const int xr = lane >> 2, xc = (lane & 3) * 32;
-  const uint16_t* xrow = (t0 + xr) < T ? x + (size_t)(t0 + xr) * d + xc : nullptr;
-  uint4 xv[4];
-  auto load_x = [&](int g) {
+  // x: lane holds token t0 + l16, the 8 bf16 at columns 32 c + 8 gq of a group
+  const int xt = t0 + l16;
+  const uint16_t* xrow = xt < T ? x + (size_t)xt * d + 8 * gq : nullptr;
+  uint4 xa[4], xn[4];
+  auto load_x = [&](int g, uint4 (&dst)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      xv[q] = xrow ? *reinterpret_cast<const uint4*>(xrow + g * kBlock + 8 * q)
-                   : make_uint4(0u, 0u, 0u, 0u);
+    for (int c = 0; c < 4; ++c)
+      dst[c] = xrow ? *reinterpret_cast<const uint4*>(xrow + g * kBlock + 32 * c)
+                    : make_uint4(0u, 0u, 0u, 0u);
   };
-  // W_router slice: thread -> float4 number tid + 256*j of the [WR][EP] slice
-  float4 wv[WV];
-  auto load_w = [&](int g, int step) {
+  // W fill: unit u -> expert u % EP, rows 8 (u / EP) .. + 7 of the fill
+  float wv[UPT][8];
+  auto load_w = [&](int row0) {
 #pragma unroll
-    for (int j = 0; j < WV; ++j) {
-      const int f4 = tid + 256 * j;
-      const int r = f4 / (EP / 4), c = (f4 % (EP / 4)) * 4;
-      const size_t row = (size_t)g * kBlock + step * WR + r;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (c + 3 < E && (E & 3) == 0) {  // 16-byte aligned rows
-        v = *reinterpret_cast<const float4*>(Wr + row * E + c);
-      } else if (c < E) {
-        if (c + 3 < E) v.w = Wr[row * E + c + 3];
-        v.x = Wr[row * E + c];
-        if (c + 1 < E) v.y = Wr[row * E + c + 1];
-        if (c + 2 < E) v.z = Wr[row * E + c + 2];
-      }
-      wv[j] = v;
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + 256 * j;
+      const int e = u % EP, r8 = u / EP;
+      const bool ok = u < UNITS && e < E;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wv[j][i] = ok ? Wr[(size_t)(row0 + 8 * r8 + i) * E + e] : 0.f;
+    }
+  };
+  auto store_w = [&]() {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = tid + 256 * j;
+      if (u >= UNITS) continue;
+      const int e = u % EP, r8 = u / EP;
+      uint32_t h[8], m[8], l[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) split3(wv[j][i], h[i], m[i], l[i]);
+      uint8_t* dst = wl + e * PITCH + 16 * r8;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(h[0] | h[1] << 16, h[2] | h[3] << 16,
+                                                  h[4] | h[5] << 16, h[6] | h[7] << 16);
+      *reinterpret_cast<uint4*>(dst + EP * PITCH) = make_uint4(
+          m[0] | m[1] << 16, m[2] | m[3] << 16, m[4] | m[5] << 16, m[6] | m[7] << 16);
+      *reinterpret_cast<uint4*>(dst + 2 * EP * PITCH) = make_uint4(
+          l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16);
     }
   };
 
   v4f tot[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) tot[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4f part[NBW];
 
   if (g0 < g1) {
-    load_x(g0);
-    load_w(g0, 0);
+    load_x(g0, xa);
+    load_w(g0 * kBlock);
   }
   for (int g = g0; g < g1; ++g) {
+    // ---- 1x128 quantisation of x for the wave's 16 tokens: row l16's 128
+    // values sit in the four lanes l16 + 16 gq
+    {
+      float v[32];
+      float am = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) part[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-    for (int step = 0; step < STEPS; ++step) {
-      __syncthreads();  // previous step's LDS readers are done
-      if (step == 0) {  // x rows of group g as fp32
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w4[4] = {xa[c].x, xa[c].y, xa[c].z, xa[c].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t w4[4] = {xv[q].x, xv[q].y, xv[q].z, xv[q].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            sx[xr * XP + xc + 8 * q + 2 * j] = bf16_to_f32(static_cast<uint16_t>(w4[j] & 0xffffu));
-            sx[xr * XP + xc + 8 * q + 2 * j + 1] = bf16_to_f32(static_cast<uint16_t>(w4[j] >> 16));
-          }
+          v[8 * c + 2 * q] = bf16_to_f32(static_cast<uint16_t>(w4[q] & 0xffffu));
+          v[8 * c + 2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(w4[q] >> 16));
         }
       }
 #pragma unroll
-      for (int j = 0; j < WV; ++j) {
-        const int f4 = tid + 256 * j;
-        const int r = f4 / (EP / 4), c = (f4 % (EP / 4)) * 4;
-        *reinterpret_cast<float4*>(sw + r * WP + c) = wv[j];
+      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+      am = fmaxf(am, __shfl_xor(am, 16));
+      am = fmaxf(am, __shfl_xor(am, 32));
+      const float s = am > 0.f ? am / kFp8Max : 1.0f;
+      if (xt < T) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float q[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[8 * c + i] / s, -kFp8Max), kFp8Max);
+          *reinterpret_cast<uint2*>(xq + (size_t)xt * d + g * kBlock + 32 * c + 8 * gq) =
+              make_uint2(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), f32x4_to_e4m3(q[4], q[5], q[6], q[7]));
+        }
+        if (gq == 0) xs[(size_t)xt * ngroups + g] = s;
       }
+    }
+    v4f part[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) part[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < FILLS; ++f) {
+      __syncthreads();  // the previous fill's readers are done
+      store_w();
       __syncthreads();
-      // prefetch the next slice (and the next x rows) while computing this one
-      if (step + 1 < STEPS) {
-        load_w(g, step + 1);
-      } else if (g + 1 < g1) {
-        load_w(g + 1, 0);
-        load_x(g + 1);
-      }
-      if (step == 0) {
-        // quantisation of group g: s = amax/448 (1 for an all-zero group), q = e4m3(x/s)
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + r;
-          const float a = sx[r * XP + 2 * lane], b = sx[r * XP + 2 * lane + 1];
-          const float amax = wave_max(fmaxf(fabsf(a), fabsf(b)));
-          const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-          const float qa = fminf(fmaxf(a / s, -kFp8Max), kFp8Max);
-          const float qb = fminf(fmaxf(b / s, -kFp8Max), kFp8Max);
-          if (t < T) {
-            reinterpret_cast<uint16_t*>(xq + (size_t)t * d + g * kBlock)[lane] =
-                static_cast<uint16_t>(f32x2_to_e4m3(qa, qb));
-            if (lane == 0) xs[(size_t)t * ngroups + g] = s;
+      // prefetch the next fill (and, at the group's first fill, the next group's x)
+      if (f + 1 < FILLS) load_w(g * kBlock + (f + 1) * KC);
+      else if (g + 1 < g1) load_w((g + 1) * kBlock);
+      if (f == 0 && g + 1 < g1) load_x(g + 1, xn);
+#pragma unroll
+      for (int sc = 0; sc < KC / 32; ++sc) {
+        const v8bf a = __builtin_bit_cast(v8bf, xa[f * (KC / 32) + sc]);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const uint8_t* pb = wl + (16 * nb + l16) * PITCH + 64 * sc + 16 * gq;
+#pragma unroll
+          for (int pl = 0; pl < 3; ++pl) {
+            const v8bf b = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(pb + pl * EP * PITCH));
+            part[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, part[nb], 0, 0, 0);
           }
         }
-      }
-      // logits: K = 4 per MFMA
-#pragma unroll 4
-      for (int k4 = 0; k4 < WR / 4; ++k4) {
-        const float a = sx[(lane & 15) * XP + step * WR + 4 * k4 + (lane >> 4)];
-        const float* wrow = sw + (4 * k4 + (lane >> 4)) * WP + (lane & 15);
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          part[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, wrow[nb * 16], part[nb], 0, 0, 0);
       }
     }
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) tot[nb] += part[nb];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) xa[c] = xn[c];
   }
 
   if (!fused) {
-    // partial logits [split][T][E]
+    // partial logits [split][T][E]: lane holds tokens 4 gq + i, expert 16 nb + l16
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-      const int e = nb * 16 + (lane & 15);
+      const int e = nb * 16 + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 4 * (lane >> 4) + i;
+        const int t = t0 + 4 * gq + i;
         if (t < T && e < E) partial[((size_t)blockIdx.y * T + t) * E + e] = tot[nb][i];
       }
     }
@@ -259,47 +288,53 @@ __global__ __launch_bounds__(256) void router_kernel(
   for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
 
-// Split-K finish: sum the partial logits of every split in split order, then
-// top-k + softmax + tile histogram.  Same token mapping as router_kernel.
+// Split-K finish: the logit of every (token, expert) of the tile is the sum of
+// its partials in split order; every thread loads all splits of its pairs at
+// once.  Then top-k + softmax + tile histogram with the router's layout.
 template <int NBW>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial,
-                                                          int nsplit, const float* __restrict__ br,
-                                                          int T, int E, int k,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w,
-                                                          int32_t* __restrict__ hist) {
+__global__ __launch_bounds__(512) void router_finish_kernel(const float* __restrict__ partial,
+                                                             int nsplit, const float* __restrict__ br,
+                                                             int T, int E, int k,
+                                                             int32_t* __restrict__ topk_idx,
+                                                             float* __restrict__ topk_w,
+                                                             int32_t* __restrict__ hist) {
+  constexpr int EP = NBW * 16;
+  __shared__ float sl[RT_TT * EP];
   __shared__ int shist[kMaxExperts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * RT_TT + wave * 16;
-  for (int i = threadIdx.x; i < E; i += 256) shist[i] = 0;
-  v4f tot[NBW];
+  const int tid = threadIdx.x;
+  const int tt0 = blockIdx.x * RT_TT;
+  for (int i = tid; i < E; i += 512) shist[i] = 0;
+  for (int pidx = tid; pidx < RT_TT * EP; pidx += 512) {
+    const int tl = pidx / EP, e = pidx % EP;
+    const int t = tt0 + tl;
+    float s = 0.f;
+    if (t < T && e < E) {
+      const float* p = partial + (size_t)t * E + e;
+      const size_t stride = (size_t)T * E;
+      for (int s0 = 0; s0 < nsplit; s0 += 16) {  // 16 loads in flight, summed in split order
+        float v[16];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int e = nb * 16 + (lane & 15);
+        for (int j = 0; j < 16; ++j) v[j] = s0 + j < nsplit ? p[(s0 + j) * stride] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * (lane >> 4) + i;
-      float s = 0.f;
-      if (t < T && e < E) {
-        const float* p = partial + (size_t)t * E + e;
-        const size_t stride = (size_t)T * E;
-        int sp = 0;
-        for (; sp + 8 <= nsplit; sp += 8) {  // 8 loads in flight, summed in split order
-          float v[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(sp + u) * stride];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) s += v[u];
-        }
-        for (; sp < nsplit; ++sp) s += p[(size_t)sp * stride];
+        for (int j = 0; j < 16; ++j)
+          if (s0 + j < nsplit) s += v[j];
       }
-      tot[nb][i] = s;
     }
+    sl[pidx] = s;
   }
-  __syncthreads();
-  topk_emit<NBW>(tot, br, t0, T, E, k, topk_idx, topk_w, shist);
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
+  __syncthreads();  // the sums are in LDS and shist is cleared
+  if (tid < 256) {   // waves 0-3: 16 tokens each, in the router's layout
+    const int lane = tid & 63, wave = tid >> 6;
+    v4f tot[NBW];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        tot[nb][i] = sl[(wave * 16 + 4 * (lane >> 4) + i) * EP + nb * 16 + (lane & 15)];
+    topk_emit<NBW>(tot, br, tt0 + wave * 16, T, E, k, topk_idx, topk_w, shist);
+  }
+  __syncthreads();  // the histogram atomics are done
+  for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
 
 template <int NBW>
@@ -314,7 +349,7 @@ hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br
   hipLaunchKernelGGL((router_kernel<NBW>), dim3(tiles, ns), dim3(256), 0, stream, x, Wr, br, T, d,
                      E, k, gps, partial, topk_idx, topk_w, hist, xq, xs);
   if (ns > 1)
-    hipLaunchKernelGGL((router_topk_kernel<NBW>), dim3(tiles), dim3(256), 0, stream, partial, ns,
+    hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(tiles), dim3(512), 0, stream, partial, ns,
                        br, T, E, k, topk_idx, topk_w, hist);
   return hipGetLastError();
 }
@@ -323,9 +358,9 @@ hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br
 
 int router_splits(int T, int d) {
   if (T <= 0) return 1;
-  const int waves = 4 * ceil_div(T, RT_TT);
+  const int tiles = ceil_div(T, RT_TT);
   const int ngroups = d / kBlock;
-  const int want = ceil_div(1024, waves);
+  const int want = ceil_div(256, tiles);  // about one workgroup per CU
   const int ns = want < ngroups ? want : ngroups;
   if (ns <= 1) return 1;
   const int gps = ceil_div(ngroups, ns);
