@@ -113,7 +113,9 @@ moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_r
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream);
 
-/* The forward is six kernels run in this order on the stream. */
+/* The forward runs in six stages, in this order on the stream.  For a batch
+ * of at most 64 tokens the router stage performs the whole routing (counts,
+ * offsets, tile lists, placement) and the scan and place stages have no work. */
 #define MOE_STAGE_ROUTER 0  /* router logits, top-k, softmax, x quantisation, tile histogram */
 #define MOE_STAGE_SCAN 1    /* expert counts, offsets, per-tile row bases, GEMM tile tables   */
 #define MOE_STAGE_PLACE 2   /* permuted row of every (token, slot)                             */

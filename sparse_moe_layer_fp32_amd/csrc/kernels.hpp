@@ -48,9 +48,18 @@ struct GemmArgs {
 // >1: partial logits [splits][T][E] fp32 in `partial`, then a top-k kernel).
 int router_splits(int T, int d);
 
+// Outputs of the whole-batch routing path (T <= RT_TT): the router stage then
+// also writes counts, offsets, both tile lists and the placement.
+struct SmallRoute {
+  int32_t *counts, *offsets, *tile_off0, *tile_off1, *tiles0, *tiles1, *row_of, *row_token;
+  int bm0, nt0, max0, bm1, nt1, max1;
+};
+
+// sr == nullptr: top-k + histogram per router tile (scan and placement follow
+// as their own stages); otherwise the whole routing of a one-tile batch.
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
                          int k, float* partial, int32_t* topk_idx, float* topk_w, int32_t* hist,
-                         uint8_t* xq, float* xs, hipStream_t stream);
+                         uint8_t* xq, float* xs, const SmallRoute* sr, hipStream_t stream);
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,

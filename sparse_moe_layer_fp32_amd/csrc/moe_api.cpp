@@ -150,15 +150,21 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   const int nz = E < R ? E : R;  // experts that can hold rows
   const int max_g = (ceil_div(R, gs.bm) + nz) * nt_g;
   const int max_p = (ceil_div(R, ps.bm) + nz) * nt_p;
+  const bool small = NT == 1;  // the whole routing runs in the router stage
 
   for (int stage = first_stage; stage <= last_stage; ++stage) {
     hipError_t err = hipSuccess;
     switch (stage) {
-      case MOE_STAGE_ROUTER:
+      case MOE_STAGE_ROUTER: {
+        const moe::SmallRoute sr{counts,  offsets, tile_off0, tile_off1, tiles0, tiles1, row_of,
+                                 row_token, gs.bm,   nt_g,      max_g,     ps.bm,  nt_p,   max_p};
         err = moe::launch_router(static_cast<const uint16_t*>(x), W_router, b_router, T, d, E, k,
-                                 partial, topk_idx, topk_w, hist, xq, xs, stream);
+                                 partial, topk_idx, topk_w, hist, xq, xs, small ? &sr : nullptr,
+                                 stream);
         break;
+      }
       case MOE_STAGE_SCAN:
+        if (small) break;  // done by the router stage
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
                                      tile_base, tile_off0, tile_off1, stream);
         if (err == hipSuccess)
@@ -169,6 +175,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                                        stream);
         break;
       case MOE_STAGE_PLACE:
+        if (small) break;  // done by the router stage
         err = moe::launch_route_place(topk_idx, tile_base, T, E, k, row_of, row_token, stream);
         break;
       case MOE_STAGE_GATEUP: {

@@ -38,7 +38,8 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 template <int NBW>
 __device__ void topk_emit(const v4f (&tot)[NBW], const float* __restrict__ br, int t_base, int T,
                           int E, int k, int32_t* __restrict__ topk_idx,
-                          float* __restrict__ topk_w, int* shist) {
+                          float* __restrict__ topk_w, int* shist, int* spick = nullptr,
+                          int spick_base = 0) {
   const int lane = threadIdx.x & 63;
   float bias[NBW];
 #pragma unroll
@@ -96,6 +97,7 @@ __device__ void topk_emit(const v4f (&tot)[NBW], const float* __restrict__ br, i
           topk_idx[(size_t)t * k + s] = sel_e[s];
           topk_w[(size_t)t * k + s] = ex[s] / sum;
           atomicAdd(&shist[sel_e[s]], 1);
+          if (spick) spick[(t - spick_base) * k + s] = sel_e[s];
         }
       }
     }
@@ -337,18 +339,165 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
   for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
 
+// All routing of a batch that fits one router tile (T <= RT_TT, the decode
+// regime) in one workgroup: the split partials are summed in split order,
+// then top-k + softmax, the expert counts and offsets (exclusive scan), the
+// stable placement of every (token, slot) pair, and the tile lists of both
+// GEMMs (the same entries as tile_table_kernel).  With one split the router
+// already chose the experts (have_topk) and only the rest runs here.
+template <int NBW>
+__global__ __launch_bounds__(512) void route_small_kernel(
+    const float* __restrict__ partial, int nsplit, bool have_topk, const float* __restrict__ br,
+    int T, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off0,
+    int32_t* __restrict__ tile_off1, int4* __restrict__ tiles0, int4* __restrict__ tiles1, int bm0,
+    int nt0, int max0, int bm1, int nt1, int max1, int32_t* __restrict__ row_of,
+    int32_t* __restrict__ row_token) {
+  constexpr int EP = NBW * 16;
+  __shared__ float sl[RT_TT * EP];
+  __shared__ int spick[RT_TT * kMaxTopK];
+  __shared__ int scnt[kMaxExperts], soff[kMaxExperts + 1], so0[kMaxExperts + 1], so1[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  const int R = T * k;
+  for (int i = tid; i < E; i += 512) scnt[i] = 0;
+  if (!have_topk) {
+    for (int pidx = tid; pidx < RT_TT * EP; pidx += 512) {
+      const int t = pidx / EP, e = pidx % EP;
+      float s = 0.f;
+      if (t < T && e < E) {
+        const float* p = partial + (size_t)t * E + e;
+        const size_t stride = (size_t)T * E;
+        for (int s0 = 0; s0 < nsplit; s0 += 16) {
+          float v[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) v[j] = s0 + j < nsplit ? p[(s0 + j) * stride] : 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            if (s0 + j < nsplit) s += v[j];
+        }
+      }
+      sl[pidx] = s;
+    }
+  } else {
+    for (int p = tid; p < R; p += 512) spick[p] = topk_idx[p];
+  }
+  __syncthreads();
+  if (!have_topk) {
+    if (tid < 256) {
+      const int lane = tid & 63, wave = tid >> 6;
+      v4f tot[NBW];
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          tot[nb][i] = sl[(wave * 16 + 4 * (lane >> 4) + i) * EP + nb * 16 + (lane & 15)];
+      topk_emit<NBW>(tot, br, wave * 16, T, E, k, topk_idx, topk_w, scnt, spick, 0);
+    }
+  } else {
+    for (int p = tid; p < R; p += 512) atomicAdd(&scnt[spick[p]], 1);
+  }
+  __syncthreads();
+  // exclusive scans of the counts and of both GEMMs' tiles per expert (wave 0)
+  if (tid < 64) {
+    int c[4], t0v[4], t1v[4], rc = 0, r0 = 0, r1 = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      c[q] = e < E ? scnt[e] : 0;
+      t0v[q] = ceil_div(c[q], bm0) * nt0;
+      t1v[q] = ceil_div(c[q], bm1) * nt1;
+      rc += c[q];
+      r0 += t0v[q];
+      r1 += t1v[q];
+    }
+    int ic = rc, i0 = r0, i1 = r1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int yc = __shfl_up(ic, o), y0 = __shfl_up(i0, o), y1 = __shfl_up(i1, o);
+      if (tid >= o) {
+        ic += yc;
+        i0 += y0;
+        i1 += y1;
+      }
+    }
+    int pc = ic - rc, p0 = i0 - r0, p1 = i1 - r1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      if (e < E) {
+        soff[e] = pc;
+        so0[e] = p0;
+        so1[e] = p1;
+      }
+      pc += c[q];
+      p0 += t0v[q];
+      p1 += t1v[q];
+    }
+    if (tid == 63) {
+      soff[E] = ic;
+      so0[E] = i0;
+      so1[E] = i1;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += 512) {
+    if (e < E) counts[e] = scnt[e];
+    offsets[e] = soff[e];
+    tile_off0[e] = so0[e];
+    tile_off1[e] = so1[e];
+  }
+  // stable placement: rank of a pair among the earlier pairs of its expert
+  for (int p = tid; p < R; p += 512) {
+    const int e = spick[p];
+    int rank = 0;
+    for (int q = 0; q < p; ++q) rank += (spick[q] == e);
+    const int row = soff[e] + rank;
+    row_of[p] = row;
+    row_token[row] = p / k;
+  }
+  // tile lists (expert by binary search of the tile offsets; inside the expert:
+  // column group of kTileGroup tiles, row block, column tile)
+  for (int pass = 0; pass < 2; ++pass) {
+    const int* so = pass == 0 ? so0 : so1;
+    const int bm = pass == 0 ? bm0 : bm1, n_tiles = pass == 0 ? nt0 : nt1;
+    int4* tiles = pass == 0 ? tiles0 : tiles1;
+    const int total = min(so[E], pass == 0 ? max0 : max1);
+    for (int L = tid; L < total; L += 512) {
+      int lo = 0, hi = E;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (so[mid] <= L) lo = mid; else hi = mid;
+      }
+      const int cnt = scnt[lo];
+      const int mt = ceil_div(cnt, bm);
+      const int local = L - so[lo];
+      const int ng = local / (mt * kTileGroup);
+      const int rem = local - ng * mt * kTileGroup;
+      const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
+      const int m = rem / gw;
+      tiles[L] = make_int4(lo, soff[lo] + m * bm, min(bm, cnt - m * bm), ng * kTileGroup + rem % gw);
+    }
+  }
+}
+
 template <int NBW>
 hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br, int T, int d,
                              int E, int k, int nsplit, float* partial, int32_t* topk_idx,
                              float* topk_w, int32_t* hist, uint8_t* xq, float* xs,
-                             hipStream_t stream) {
+                             const SmallRoute* sr, hipStream_t stream) {
   const int tiles = ceil_div(T, RT_TT);
   const int ngroups = d / kBlock;
   const int gps = ceil_div(ngroups, nsplit);
   const int ns = ceil_div(ngroups, gps);
   hipLaunchKernelGGL((router_kernel<NBW>), dim3(tiles, ns), dim3(256), 0, stream, x, Wr, br, T, d,
                      E, k, gps, partial, topk_idx, topk_w, hist, xq, xs);
-  if (ns > 1)
+  if (sr != nullptr)
+    hipLaunchKernelGGL((route_small_kernel<NBW>), dim3(1), dim3(512), 0, stream, partial, ns, ns == 1,
+                       br, T, E, k, topk_idx, topk_w, sr->counts, sr->offsets, sr->tile_off0,
+                       sr->tile_off1, reinterpret_cast<int4*>(sr->tiles0),
+                       reinterpret_cast<int4*>(sr->tiles1), sr->bm0, sr->nt0, sr->max0, sr->bm1,
+                       sr->nt1, sr->max1, sr->row_of, sr->row_token);
+  else if (ns > 1)
     hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(tiles), dim3(512), 0, stream, partial, ns,
                        br, T, E, k, topk_idx, topk_w, hist);
   return hipGetLastError();
@@ -369,13 +518,13 @@ int router_splits(int T, int d) {
 
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
                          int k, float* partial, int32_t* topk_idx, float* topk_w, int32_t* hist,
-                         uint8_t* xq, float* xs, hipStream_t stream) {
+                         uint8_t* xq, float* xs, const SmallRoute* sr, hipStream_t stream) {
   const int nsplit = router_splits(T, d);
   switch (ceil_div(E, 16)) {
 #define MOE_ROUTER_CASE(n)                                                                     \
   case n:                                                                                      \
     return launch_router_nbw<n>(x, Wr, br, T, d, E, k, nsplit, partial, topk_idx, topk_w, hist, \
-                                xq, xs, stream);
+                                xq, xs, sr, stream);
     MOE_ROUTER_CASE(1)
     MOE_ROUTER_CASE(2)
     MOE_ROUTER_CASE(3)
