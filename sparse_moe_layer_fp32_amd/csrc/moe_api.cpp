@@ -32,7 +32,7 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
     return at;
   };
   const int64_t ns = moe::router_splits((int)T, (int)d);
-  l.partial = put(ns > 1 ? 4 * ns * T * E : 0);
+  l.partial = put(ns > 1 ? 4 * ns * T * (16 * ceil_div((int)E, 16)) : 0);  // experts padded to 16
   l.topk_idx = put(4 * R);
   l.topk_w = put(4 * R);
   l.hist = put(4 * NT * E);

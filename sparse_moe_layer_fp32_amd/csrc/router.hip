@@ -272,14 +272,15 @@ __global__ __launch_bounds__(256) void router_kernel(
   }
 
   if (!fused) {
-    // partial logits [split][T][E]: lane holds tokens 4 gq + i, expert 16 nb + l16
+    // partial logits [split][T][EP] (padded experts hold 0): lane holds tokens
+    // 4 gq + i, expert 16 nb + l16
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const int e = nb * 16 + l16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 4 * gq + i;
-        if (t < T && e < E) partial[((size_t)blockIdx.y * T + t) * E + e] = tot[nb][i];
+        if (t < T) partial[((size_t)blockIdx.y * T + t) * EP + e] = tot[nb][i];
       }
     }
     return;
@@ -288,6 +289,88 @@ __global__ __launch_bounds__(256) void router_kernel(
   topk_emit<NBW>(tot, br, t0, T, E, k, topk_idx, topk_w, shist);
   __syncthreads();
   for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
+}
+
+// Top-k + softmax of one token by one thread, from its logits in LDS (the
+// same 64-bit keys, ties and softmax as topk_emit): every key passes through
+// a sorted list of k entries (compare-exchange down the list).  Writes the
+// picks, the weights, the histogram and optionally an LDS copy of the picks
+// and the token's bit in the per-expert token masks.
+__device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k, int t,
+                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int* shist,
+                            int* spick_row, uint32_t* smask_lo, uint32_t* smask_hi, int tl) {
+  uint64_t best[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) best[s] = 0ull;
+  for (int e = 0; e < E; ++e) {
+    uint64_t carry = ((uint64_t)ordered_key(sl_row[e] + sbr[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+      if (s < k) {
+        const uint64_t b = best[s];
+        best[s] = carry > b ? carry : b;
+        carry = carry > b ? b : carry;
+      }
+    }
+  }
+  const float l0 = key_value((uint32_t)(best[0] >> 32));
+  float ex[kMaxTopK];
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    ex[s] = s < k ? expf(key_value((uint32_t)(best[s] >> 32)) - l0) : 0.f;
+    sum += ex[s];
+  }
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    if (s < k) {
+      const int e = (int)(0xffffffffu - (uint32_t)best[s]);
+      topk_idx[(size_t)t * k + s] = e;
+      topk_w[(size_t)t * k + s] = ex[s] / sum;
+      atomicAdd(&shist[e], 1);
+      if (spick_row) spick_row[s] = e;
+      if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
+    }
+  }
+}
+
+// Logits of the tile's RT_TT tokens into sl [RT_TT][EP + 1] (odd pitch: the
+// per-token readers of topk_thread hit distinct banks): the sum of every
+// (token, expert) partial in split order.  A thread takes 4 experts of one
+// token (one float4 per split, up to 16 splits in flight per round).
+template <int EP>
+__device__ void sum_partials(const float* __restrict__ partial, int nsplit, int T, int tt0,
+                             float* sl, int nthreads) {
+  constexpr int Q = EP / 4;
+  const size_t stride = (size_t)T * EP;
+  for (int q = threadIdx.x; q < RT_TT * Q; q += nthreads) {
+    const int tl = q / Q, e4 = 4 * (q % Q);
+    const int t = tt0 + tl;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < T) {
+      const float* p = partial + (size_t)t * EP + e4;
+      for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        float4 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          v[j] = s0 + j < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + j) * stride)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (s0 + j < nsplit) {
+            s.x += v[j].x;
+            s.y += v[j].y;
+            s.z += v[j].z;
+            s.w += v[j].w;
+          }
+      }
+    }
+    float* dst = sl + tl * (EP + 1) + e4;
+    dst[0] = s.x;
+    dst[1] = s.y;
+    dst[2] = s.z;
+    dst[3] = s.w;
+  }
 }
 
 // Split-K finish: the logit of every (token, expert) of the tile is the sum of
@@ -301,40 +384,20 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
                                                              float* __restrict__ topk_w,
                                                              int32_t* __restrict__ hist) {
   constexpr int EP = NBW * 16;
-  __shared__ float sl[RT_TT * EP];
+  __shared__ float sl[RT_TT * (EP + 1)];
   __shared__ int shist[kMaxExperts];
+  __shared__ float sbr[kMaxExperts];
   const int tid = threadIdx.x;
   const int tt0 = blockIdx.x * RT_TT;
-  for (int i = tid; i < E; i += 512) shist[i] = 0;
-  for (int pidx = tid; pidx < RT_TT * EP; pidx += 512) {
-    const int tl = pidx / EP, e = pidx % EP;
-    const int t = tt0 + tl;
-    float s = 0.f;
-    if (t < T && e < E) {
-      const float* p = partial + (size_t)t * E + e;
-      const size_t stride = (size_t)T * E;
-      for (int s0 = 0; s0 < nsplit; s0 += 16) {  // 16 loads in flight, summed in split order
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = s0 + j < nsplit ? p[(s0 + j) * stride] : 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (s0 + j < nsplit) s += v[j];
-      }
-    }
-    sl[pidx] = s;
+  for (int i = tid; i < E; i += 512) {
+    shist[i] = 0;
+    sbr[i] = br[i];
   }
-  __syncthreads();  // the sums are in LDS and shist is cleared
-  if (tid < 256) {   // waves 0-3: 16 tokens each, in the router's layout
-    const int lane = tid & 63, wave = tid >> 6;
-    v4f tot[NBW];
-#pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        tot[nb][i] = sl[(wave * 16 + 4 * (lane >> 4) + i) * EP + nb * 16 + (lane & 15)];
-    topk_emit<NBW>(tot, br, tt0 + wave * 16, T, E, k, topk_idx, topk_w, shist);
-  }
+  sum_partials<EP>(partial, nsplit, T, tt0, sl, 512);
+  __syncthreads();  // the sums are in LDS, shist and sbr are set
+  const int t = tt0 + tid;
+  if (tid < RT_TT && t < T)
+    topk_thread(sl + tid * (EP + 1), sbr, E, k, t, topk_idx, topk_w, shist, nullptr, nullptr, nullptr, 0);
   __syncthreads();  // the histogram atomics are done
   for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
@@ -354,47 +417,34 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     int nt0, int max0, int bm1, int nt1, int max1, int32_t* __restrict__ row_of,
     int32_t* __restrict__ row_token) {
   constexpr int EP = NBW * 16;
-  __shared__ float sl[RT_TT * EP];
+  __shared__ float sl[RT_TT * (EP + 1)];
   __shared__ int spick[RT_TT * kMaxTopK];
   __shared__ int scnt[kMaxExperts], soff[kMaxExperts + 1], so0[kMaxExperts + 1], so1[kMaxExperts + 1];
+  __shared__ uint32_t smask[2][kMaxExperts];  // tokens (bits) that chose each expert
   const int tid = threadIdx.x;
   const int R = T * k;
-  for (int i = tid; i < E; i += 512) scnt[i] = 0;
+  __shared__ float sbr[kMaxExperts];
+  for (int i = tid; i < E; i += 512) {
+    scnt[i] = 0;
+    smask[0][i] = smask[1][i] = 0u;
+    sbr[i] = br[i];
+  }
   if (!have_topk) {
-    for (int pidx = tid; pidx < RT_TT * EP; pidx += 512) {
-      const int t = pidx / EP, e = pidx % EP;
-      float s = 0.f;
-      if (t < T && e < E) {
-        const float* p = partial + (size_t)t * E + e;
-        const size_t stride = (size_t)T * E;
-        for (int s0 = 0; s0 < nsplit; s0 += 16) {
-          float v[16];
-#pragma unroll
-          for (int j = 0; j < 16; ++j) v[j] = s0 + j < nsplit ? p[(s0 + j) * stride] : 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j)
-            if (s0 + j < nsplit) s += v[j];
-        }
-      }
-      sl[pidx] = s;
-    }
+    sum_partials<EP>(partial, nsplit, T, 0, sl, 512);
   } else {
     for (int p = tid; p < R; p += 512) spick[p] = topk_idx[p];
   }
   __syncthreads();
   if (!have_topk) {
-    if (tid < 256) {
-      const int lane = tid & 63, wave = tid >> 6;
-      v4f tot[NBW];
-#pragma unroll
-      for (int nb = 0; nb < NBW; ++nb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          tot[nb][i] = sl[(wave * 16 + 4 * (lane >> 4) + i) * EP + nb * 16 + (lane & 15)];
-      topk_emit<NBW>(tot, br, wave * 16, T, E, k, topk_idx, topk_w, scnt, spick, 0);
-    }
+    if (tid < T)
+      topk_thread(sl + tid * (EP + 1), sbr, E, k, tid, topk_idx, topk_w, scnt, spick + tid * k, smask[0],
+                  smask[1], tid);
   } else {
-    for (int p = tid; p < R; p += 512) atomicAdd(&scnt[spick[p]], 1);
+    for (int p = tid; p < R; p += 512) {
+      const int t = p / k;
+      atomicAdd(&scnt[spick[p]], 1);
+      atomicOr(&smask[t >> 5][spick[p]], 1u << (t & 31));
+    }
   }
   __syncthreads();
   // exclusive scans of the counts and of both GEMMs' tiles per expert (wave 0)
@@ -446,14 +496,16 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     tile_off0[e] = so0[e];
     tile_off1[e] = so1[e];
   }
-  // stable placement: rank of a pair among the earlier pairs of its expert
+  // stable placement: the rank of pair (t, j) within its expert is the number
+  // of earlier tokens that chose the expert (a token picks an expert once)
   for (int p = tid; p < R; p += 512) {
-    const int e = spick[p];
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += (spick[q] == e);
+    const int e = spick[p], t = p / k;
+    const uint32_t below = (1u << (t & 31)) - 1u;
+    const int rank = t < 32 ? __popc(smask[0][e] & below)
+                            : __popc(smask[0][e]) + __popc(smask[1][e] & below);
     const int row = soff[e] + rank;
     row_of[p] = row;
-    row_token[row] = p / k;
+    row_token[row] = t;
   }
   // tile lists (expert by binary search of the tile offsets; inside the expert:
   // column group of kTileGroup tiles, row block, column tile)
