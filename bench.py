@@ -32,6 +32,39 @@ from sparse_moe_layer_fp32_amd import inputs as gen  # noqa: E402
 METRIC = "MoE-layer tokens/s + % of FP8 MFMA peak (prefill) / % HBM BW (decode)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
+
+# HBM traffic of one gate/up GEMM launch from rocprofv3 --pmc runs (one run for
+# FETCH_SIZE, one for WRITE_SIZE, KiB per dispatch) of
+#   bench.py --workload W --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration-mib 1024
+# Each counter is scaled by what it reads for that run's 1 GiB device copy:
+# FETCH_SIZE counts the 128-byte fabric reads of gfx950 as 64 bytes (the copy
+# reads as 524312 KiB), WRITE_SIZE reads the copy exactly.  Keyed by the
+# SHA-256 of the GEMM source the counters were taken on: any change to the
+# kernels reports null until they are measured again.
+TRAFFIC = {
+    "c1": {"gemm_sha256": "92db357d303f25dafa9254f5810a78d180033f1a98328fd59fdd1017981ced53",
+           "fetch_kib": 271898.225, "write_kib": 765.15625,
+           "copy_fetch_kib": 524313.6875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "92db357d303f25dafa9254f5810a78d180033f1a98328fd59fdd1017981ced53",
+           "fetch_kib": 887459.0, "write_kib": 103982.48125,
+           "copy_fetch_kib": 524306.25, "copy_write_kib": 1048576.0},
+}
+
+
+def gemm_src_sha():
+    import hashlib
+    with open(GEMM_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    t = TRAFFIC.get(workload)
+    if t is None or t["gemm_sha256"] != gemm_src_sha():
+        return None
+    fetch = t["fetch_kib"] * (1 << 20) / t["copy_fetch_kib"]
+    write = t["write_kib"] * (1 << 20) / t["copy_write_kib"]
+    return int(round((fetch + write) * 1024))
 
 
 def log(*a):
@@ -167,12 +200,14 @@ def main():
     if decode:
         ach = ga["bytes"] / (gate_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)}
     else:
         ach = ga["flops"] / (gate_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4), "traffic": None}
-    roof["kernel"] = "grouped_gemm_kernel (gate/up + bias + SwiGLU + h quantisation)"
+                "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload)}
+    roof["kernel"] = ("grouped_gemm_dma_kernel<true, 32, 256>" if decode else
+                      "grouped_gemm_wide_kernel<true>") + " (gate/up + bias + SwiGLU + h quantisation)"
     roof["avg_ms"] = round(gate_ms, 5)
     roof["algorithmic_bytes"] = ga["bytes"]
     roof["algorithmic_flops"] = ga["flops"]

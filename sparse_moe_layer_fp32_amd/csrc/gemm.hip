@@ -145,26 +145,6 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff) {
       : "s"(lds), "v"(voff), "s"(rsrc)
       : "memory");
 }
-// The same loads without a memory clobber, for loads into a stage that no
-// LDS access of the current step touches: the compiler may then move LDS
-// reads across them.  They stay ordered with the ring's fenced barriers and
-// with every other volatile asm.
-__device__ __forceinline__ void dma16n(v4i rsrc, uint32_t lds, uint32_t voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc));
-}
-__device__ __forceinline__ void dma4n(v4i rsrc, uint32_t lds, uint32_t voff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc));
-}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
       static_cast<int>(reinterpret_cast<uintptr_t>(p))));
