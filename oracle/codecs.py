@@ -69,7 +69,8 @@ def bf16_round(v: np.ndarray) -> np.ndarray:
     """fp64 values -> nearest bf16 value (as fp64), ties to even.
 
     Written directly on the binary64 representation: keep 8 significant bits.
-    Used only to report the rounding floor of bf16 outputs.
+    Reports the rounding floor of bf16 outputs and rounds the optional bf16
+    gate weights.
     """
     v = np.asarray(v, dtype=np.float64)
     with np.errstate(divide="ignore", invalid="ignore"):

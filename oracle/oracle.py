@@ -71,6 +71,25 @@ def gate_weights(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return z / z.sum(axis=1, keepdims=True)
 
 
+def gate_weights_all(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Routing variant: the softmax is taken over all E logits before top-k
+    (the DeepSeek-style rule that "GPT-OSS on day 0", section "MoE", contrasts
+    with gpt-oss's softmax over the selected experts).  Reading: the selected
+    experts keep their full-softmax probabilities, not renormalised over the
+    k.  Max-subtracted form, fp64 [T, k]."""
+    z = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = z / z.sum(axis=1, keepdims=True)
+    return np.take_along_axis(p, idx, axis=1)
+
+
+def bf16_round_weights(w: np.ndarray) -> np.ndarray:
+    """Gate weights rounded to bf16 (round to nearest even), as fp64.  The
+    section "MoE" calls for the expert weights in bf16 (reading: an option;
+    the default keeps them in fp32 on the GPU and fp64 here)."""
+    from .codecs import bf16_round
+    return bf16_round(np.asarray(w, np.float64))
+
+
 def permutation(idx: np.ndarray, E: int):
     """Expert-contiguous order of the routed (token, slot) pairs.
 
@@ -151,10 +170,21 @@ def expert_mlp(xdeq: np.ndarray, Wgu_e, Sgu_e, bgu_e, Wdn_e, Sdn_e, bdn_e, retur
 
 
 def route(inp: dict):
-    """Steps 2-5 for all tokens."""
+    """Steps 2-5 for all tokens.  Optional keys of ``inp``: ``routing`` =
+    "topk_softmax" (default: softmax over the selected logits) or
+    "softmax_topk" (softmax over all logits, ``gate_weights_all``), and
+    ``gate_bf16`` (round the gate weights to bf16)."""
     logits = router_logits(inp["x"], inp["W_router"], inp["b_router"])
     idx = topk_select(logits, inp["k"])
-    w = gate_weights(logits, idx)
+    routing = inp.get("routing", "topk_softmax")
+    if routing == "topk_softmax":
+        w = gate_weights(logits, idx)
+    elif routing == "softmax_topk":
+        w = gate_weights_all(logits, idx)
+    else:
+        raise ValueError(f"unknown routing {routing!r}")
+    if inp.get("gate_bf16", False):
+        w = bf16_round_weights(w)
     counts, offsets, row_of, row_token = permutation(idx, inp["E"])
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                 row_of=row_of, row_token=row_token)

@@ -134,6 +134,63 @@ def test_gate_weights_closed_forms():
     np.testing.assert_array_equal(oracle.gate_weights(L2, idx4), w4)
 
 
+# ------------------------------------------------------------------ P5b: routing variant and bf16 gate weights
+def test_gate_weights_all_vs_library_softmax():
+    """Softmax over all logits before top-k: the selected experts keep their
+    full-softmax probabilities (scipy's softmax as the library special case)."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(31)
+    L = rng.normal(scale=2, size=(120, 16))
+    for k in (1, 4, 16):
+        idx = oracle.topk_select(L, k)
+        w = oracle.gate_weights_all(L, idx)
+        np.testing.assert_allclose(w, np.take_along_axis(softmax(L, axis=1), idx, 1), rtol=1e-13)
+        assert np.all(np.diff(w, axis=1) <= 0)
+        if k == 16:
+            assert np.max(np.abs(w.sum(1) - 1)) <= 1e-14      # every expert selected: sums to 1
+        else:
+            assert np.all(w.sum(1) < 1)
+    # unlike the selected-only softmax, an unselected logit moves the weights
+    idx = oracle.topk_select(L, 4)
+    L2 = L.copy()
+    for t in range(len(L)):
+        e = [x for x in range(16) if x not in idx[t]][0]
+        L2[t, e] += 0.5
+    assert not np.allclose(oracle.gate_weights_all(L2, idx), oracle.gate_weights_all(L, idx))
+    # k = 1: the full softmax probability, a logistic against the log-sum-exp of the rest
+    i1 = oracle.topk_select(L, 1)
+    l_top = np.take_along_axis(L, i1, 1)[:, 0]
+    others = np.log(np.exp(L).sum(1) - np.exp(l_top))
+    np.testing.assert_allclose(oracle.gate_weights_all(L, i1)[:, 0],
+                               1.0 / (1.0 + np.exp(others - l_top)), rtol=1e-12)
+
+
+def test_bf16_gate_weights():
+    rng = np.random.default_rng(32)
+    w = rng.uniform(0, 1, size=5000)
+    r = oracle.bf16_round_weights(w)
+    # every value is a bf16 (via torch's exact bf16 cast of the rounded value) and is the nearest one
+    np.testing.assert_array_equal(torch.from_numpy(r).to(torch.bfloat16).to(torch.float64).numpy(), r)
+    np.testing.assert_array_equal(r, torch.from_numpy(w).to(torch.bfloat16).to(torch.float64).numpy())
+    assert np.all(np.abs(r - w) <= 2.0 ** -8 * np.abs(w))      # 8 significant bits: unit roundoff 2^-8
+
+
+def test_route_options_change_only_the_weights():
+    layer = gen.custom_layer(256, 256, 8, 3, layer_id=333)
+    inp = gen.make_inputs(layer, T=50)
+    a = oracle.route(inp)
+    b = oracle.route(dict(inp, routing="softmax_topk"))
+    c = oracle.route(dict(inp, routing="softmax_topk", gate_bf16=True))
+    for key in ("idx", "counts", "offsets", "row_of", "row_token"):
+        np.testing.assert_array_equal(a[key], b[key])
+        np.testing.assert_array_equal(a[key], c[key])
+    # the selected-only weights are the all-expert ones renormalised over the k
+    np.testing.assert_allclose(a["w"], b["w"] / b["w"].sum(1, keepdims=True), rtol=1e-13)
+    np.testing.assert_array_equal(c["w"], oracle.bf16_round_weights(b["w"]))
+    with pytest.raises(ValueError):
+        oracle.route(dict(inp, routing="bogus"))
+
+
 # ------------------------------------------------------------------ P6: permutation
 @pytest.mark.parametrize("T,E,k", [(1, 4, 2), (37, 8, 3), (300, 64, 8), (5, 3, 3)])
 def test_permutation_invariants(T, E, k):
