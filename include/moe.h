@@ -65,7 +65,7 @@ typedef enum {
   MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_bytes */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
   MOE_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError)           */
-  MOE_ERR_FLAGS = -7        /* unknown bits in `flags`                            */
+  MOE_ERR_FLAGS = -7        /* unknown bits in `flags`, path 3, or a bad stage range */
 } moe_status;
 
 #define MOE_MAX_EXPERTS 256
@@ -73,10 +73,21 @@ typedef enum {
 #define MOE_BLOCK 128
 #define MOE_MAX_HIDDEN 8192 /* d and f: at most 64 blocks of 128 */
 
-/* Path selection for the expert GEMMs (argument `flags`). */
+/* Argument `flags`: bits 0-1 select the path of the expert GEMMs, */
 #define MOE_PATH_AUTO 0u    /* pick by the mean rows per expert, T*k/E           */
 #define MOE_PATH_PREFILL 1u /* large row tiles, MFMA-bound shape                  */
 #define MOE_PATH_DECODE 2u  /* small row tiles streaming weights (memory-bound)   */
+#define MOE_PATH_MASK 3u
+/* and two bits change the gate weights (the expert selection never changes).
+ * MOE_ROUTE_SOFTMAX_ALL: the softmax runs over all E logits before top-k and
+ * each selected expert keeps its full-softmax probability (not renormalised
+ * over the k): the routing rule that "GPT-OSS on day 0", section "MoE",
+ * contrasts with gpt-oss's softmax over the selected logits (the default).
+ * MOE_GATE_BF16: the gate weights are rounded to bf16 (nearest even) before
+ * the combine (the same section keeps the expert weights in bf16; by default
+ * they stay fp32). */
+#define MOE_ROUTE_SOFTMAX_ALL 4u
+#define MOE_GATE_BF16 8u
 
 /* Bytes of device workspace moe_forward needs for these sizes (0 if the sizes
  * are invalid).  The workspace holds the routing tables, the quantised
@@ -105,8 +116,9 @@ moe_status moe_forward(const void* x, const float* W_router, const float* b_rout
                        int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* moe_forward with an explicit GEMM path (MOE_PATH_*); same results to
- * rounding of the fp32 accumulation order. */
+/* moe_forward with `flags`: a GEMM path (MOE_PATH_*; the paths give the same
+ * results to rounding of the fp32 accumulation order) and the gate-weight
+ * options MOE_ROUTE_SOFTMAX_ALL and MOE_GATE_BF16. */
 moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_router, int32_t k,
                           const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                           const uint8_t* W_down, const float* S_down, const void* b_down,

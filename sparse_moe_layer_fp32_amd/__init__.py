@@ -17,6 +17,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsparse_moe.so")
 
 PATHS = {"auto": 0, "prefill": 1, "decode": 2}
+ROUTINGS = {"topk_softmax": 0, "softmax_topk": 4}   # MOE_ROUTE_SOFTMAX_ALL
+GATE_BF16 = 8                                       # MOE_GATE_BF16
+
+
+def flags_of(path="auto", routing="topk_softmax", gate_bf16=False) -> int:
+    """The C ABI's `flags` word: GEMM path, gate-weight rule, bf16 gate weights."""
+    return PATHS[path] | ROUTINGS[routing] | (GATE_BF16 if gate_bf16 else 0)
 BLOCK = 128
 MAX_EXPERTS = 256
 MAX_TOPK = 8
@@ -136,31 +143,34 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
 
 
 def forward(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
-            out=None, workspace=None, path="auto", stream=None):
+            out=None, workspace=None, path="auto", stream=None, routing="topk_softmax",
+            gate_bf16=False):
     """bf16 [T, d] output of the block; every argument is a device tensor laid
     out as ``include/moe.h`` states (bf16 tensors may be any 2-byte dtype,
     e4m3 tensors any 1-byte dtype)."""
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
                              S_down, b_down, out, workspace)
-    _check(lib().moe_forward_ex(*args, PATHS[path], _stream(x.device, stream, ws, out)))
+    _check(lib().moe_forward_ex(*args, flags_of(path, routing, gate_bf16),
+                                _stream(x.device, stream, ws, out)))
     return out
 
 
 def forward_stages(first, last, x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
-                   S_down, b_down, out, workspace, path="auto", stream=None):
+                   S_down, b_down, out, workspace, path="auto", stream=None, routing="topk_softmax",
+                   gate_bf16=False):
     """Stages ``first``..``last`` (names of ``STAGES`` or ints) of ``forward`` on a
     caller-kept workspace; all stages must run in order on that workspace."""
     first = STAGES.get(first, first)
     last = STAGES.get(last, last)
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
                              S_down, b_down, out, workspace)
-    _check(lib().moe_forward_stages(*args, PATHS[path], int(first), int(last),
+    _check(lib().moe_forward_stages(*args, flags_of(path, routing, gate_bf16), int(first), int(last),
                                     _stream(x.device, stream, ws, out)))
     return out
 
 
 def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
-                  path="auto", stream=None):
+                  path="auto", stream=None, routing="topk_softmax", gate_bf16=False):
     """``forward`` plus the intermediates (routing, permutation, quantised
     activations and h, per-row expert outputs) as a dict of device tensors."""
     T, d = x.shape
@@ -181,7 +191,8 @@ def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
                              S_down, b_down, None, None)
     order = ["topk_idx", "topk_w", "offsets", "row_token", "row_of", "xq", "xs", "hq", "hs", "y"]
-    _check(lib().moe_forward_debug(*args, PATHS[path], _stream(dev, stream, ws, out, *dbg.values()),
+    _check(lib().moe_forward_debug(*args, flags_of(path, routing, gate_bf16),
+                                   _stream(dev, stream, ws, out, *dbg.values()),
                                    *[_ptr(dbg[n]) for n in order]))
     dbg["out"] = out
     return dbg
@@ -217,8 +228,9 @@ class MoeBlock:
             self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=p["W_router"].device)
         return self._ws
 
-    def __call__(self, x, out=None, path="auto", stream=None):
+    def __call__(self, x, out=None, path="auto", stream=None, routing="topk_softmax", gate_bf16=False):
         p = self.p
         return forward(x, p["W_router"], p["b_router"], p["k"], p["W_gateup"], p["S_gateup"],
                        p["b_gateup"], p["W_down"], p["S_down"], p["b_down"], out=out,
-                       workspace=self.workspace(x.shape[0]), path=path, stream=stream)
+                       workspace=self.workspace(x.shape[0]), path=path, stream=stream,
+                       routing=routing, gate_bf16=gate_bf16)

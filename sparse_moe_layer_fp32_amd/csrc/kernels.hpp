@@ -57,9 +57,15 @@ struct SmallRoute {
 
 // sr == nullptr: top-k + histogram per router tile (scan and placement follow
 // as their own stages); otherwise the whole routing of a one-tile batch.
+// Gate-weight rule (bits of gate_mode): softmax over all E logits instead of
+// the selected k; round the weights to bf16.
+constexpr int kGateSoftmaxAll = 1;
+constexpr int kGateBf16 = 2;
+
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
-                         int k, float* partial, int32_t* topk_idx, float* topk_w, int32_t* hist,
-                         uint8_t* xq, float* xs, const SmallRoute* sr, hipStream_t stream);
+                         int k, int gate_mode, float* partial, int32_t* topk_idx, float* topk_w,
+                         int32_t* hist, uint8_t* xq, float* xs, const SmallRoute* sr,
+                         hipStream_t stream);
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,

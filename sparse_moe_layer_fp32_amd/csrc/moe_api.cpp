@@ -103,7 +103,12 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                               int32_t first_stage, int32_t last_stage, void* stream_) {
   const moe_status sz = check_sizes(T, d, f, E, k);
   if (sz != MOE_OK) return sz;
-  if (flags > MOE_PATH_DECODE) return MOE_ERR_FLAGS;
+  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16)) != 0u ||
+      (flags & MOE_PATH_MASK) == MOE_PATH_MASK)
+    return MOE_ERR_FLAGS;
+  const uint32_t path = flags & MOE_PATH_MASK;
+  const int gate_mode = ((flags & MOE_ROUTE_SOFTMAX_ALL) ? moe::kGateSoftmaxAll : 0) |
+                        ((flags & MOE_GATE_BF16) ? moe::kGateBf16 : 0);
   if (first_stage < 0 || last_stage >= MOE_NUM_STAGES || first_stage > last_stage)
     return MOE_ERR_FLAGS;
   if (T == 0) return MOE_OK;
@@ -141,8 +146,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   const int R = T * k;
   const int NT = ceil_div(T, moe::RT_TT);
   bool decode;
-  if (flags == MOE_PATH_AUTO) decode = (int64_t)R <= 32 * (int64_t)E;
-  else decode = flags == MOE_PATH_DECODE;
+  if (path == MOE_PATH_AUTO) decode = (int64_t)R <= 32 * (int64_t)E;
+  else decode = path == MOE_PATH_DECODE;
   const moe::GemmShape gs = decode ? moe::kGatedDecode : moe::kGatedPrefill;
   const moe::GemmShape ps = decode ? moe::kPlainDecode : moe::kPlainPrefill;
   const int nt_g = f / moe::kBlock;
@@ -159,8 +164,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         const moe::SmallRoute sr{counts,  offsets, tile_off0, tile_off1, tiles0, tiles1, row_of,
                                  row_token, gs.bm,   nt_g,      max_g,     ps.bm,  nt_p,   max_p};
         err = moe::launch_router(static_cast<const uint16_t*>(x), W_router, b_router, T, d, E, k,
-                                 partial, topk_idx, topk_w, hist, xq, xs, small ? &sr : nullptr,
-                                 stream);
+                                 gate_mode, partial, topk_idx, topk_w, hist, xq, xs,
+                                 small ? &sr : nullptr, stream);
         break;
       }
       case MOE_STAGE_SCAN:

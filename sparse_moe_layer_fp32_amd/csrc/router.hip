@@ -35,9 +35,17 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 // complemented expert index, so ties go to the lower index; absent experts
 // have key 0 below every real key), softmax over the k selected logits,
 // writes, and counts the picks into the tile histogram.
+// Gate weight of pick s from ex[s] = exp(l_s - l_max) and the normaliser
+// (the selected logits' sum, or all logits' for kGateSoftmaxAll), optionally
+// rounded to bf16.
+__device__ __forceinline__ float gate_weight(float ex, float sum, int gate_mode) {
+  const float w = ex / sum;
+  return (gate_mode & kGateBf16) ? bf16_to_f32(f32_to_bf16(w)) : w;
+}
+
 template <int NBW>
 __device__ void topk_emit(const v4f (&tot)[NBW], const float* __restrict__ br, int t_base, int T,
-                          int E, int k, int32_t* __restrict__ topk_idx,
+                          int E, int k, int gate_mode, int32_t* __restrict__ topk_idx,
                           float* __restrict__ topk_w, int* shist, int* spick = nullptr,
                           int spick_base = 0) {
   const int lane = threadIdx.x & 63;
@@ -90,12 +98,23 @@ __device__ void topk_emit(const v4f (&tot)[NBW], const float* __restrict__ br, i
       ex[s] = s < k ? expf(sel_l[s] - sel_l[0]) : 0.f;
       sum += ex[s];
     }
+    if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits (xor tree: same in every lane)
+      float part = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int e = nb * 16 + (lane & 15);
+        if (e < E) part += expf(tot[nb][i] + bias[nb] - sel_l[0]);
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o);
+      sum = part;
+    }
     if (t < T) {
 #pragma unroll
       for (int s = 0; s < kMaxTopK; ++s) {
         if (s < k && (lane & 15) == s) {
           topk_idx[(size_t)t * k + s] = sel_e[s];
-          topk_w[(size_t)t * k + s] = ex[s] / sum;
+          topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
           atomicAdd(&shist[sel_e[s]], 1);
           if (spick) spick[(t - spick_base) * k + s] = sel_e[s];
         }
@@ -138,7 +157,7 @@ constexpr int w_fill(int nbw) { return nbw <= 4 ? kBlock : nbw <= 8 ? kBlock / 2
 template <int NBW>
 __global__ __launch_bounds__(256) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ br,
-    int T, int d, int E, int k, int groups_per_split, float* __restrict__ partial,
+    int T, int d, int E, int k, int gate_mode, int groups_per_split, float* __restrict__ partial,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist,
     uint8_t* __restrict__ xq, float* __restrict__ xs) {
   constexpr int EP = NBW * 16;                   // experts padded to 16
@@ -286,7 +305,7 @@ __global__ __launch_bounds__(256) void router_kernel(
     return;
   }
   __syncthreads();  // shist cleared
-  topk_emit<NBW>(tot, br, t0, T, E, k, topk_idx, topk_w, shist);
+  topk_emit<NBW>(tot, br, t0, T, E, k, gate_mode, topk_idx, topk_w, shist);
   __syncthreads();
   for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
@@ -296,9 +315,10 @@ __global__ __launch_bounds__(256) void router_kernel(
 // a sorted list of k entries (compare-exchange down the list).  Writes the
 // picks, the weights, the histogram and optionally an LDS copy of the picks
 // and the token's bit in the per-expert token masks.
-__device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k, int t,
-                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int* shist,
-                            int* spick_row, uint32_t* smask_lo, uint32_t* smask_hi, int tl) {
+__device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k, int gate_mode,
+                            int t, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                            int* shist, int* spick_row, uint32_t* smask_lo, uint32_t* smask_hi,
+                            int tl) {
   uint64_t best[kMaxTopK];
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) best[s] = 0ull;
@@ -321,12 +341,16 @@ __device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k,
     ex[s] = s < k ? expf(key_value((uint32_t)(best[s] >> 32)) - l0) : 0.f;
     sum += ex[s];
   }
+  if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits, in expert order
+    sum = 0.f;
+    for (int e = 0; e < E; ++e) sum += expf(sl_row[e] + sbr[e] - l0);
+  }
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) {
     if (s < k) {
       const int e = (int)(0xffffffffu - (uint32_t)best[s]);
       topk_idx[(size_t)t * k + s] = e;
-      topk_w[(size_t)t * k + s] = ex[s] / sum;
+      topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
       atomicAdd(&shist[e], 1);
       if (spick_row) spick_row[s] = e;
       if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
@@ -379,7 +403,7 @@ __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int 
 template <int NBW>
 __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restrict__ partial,
                                                              int nsplit, const float* __restrict__ br,
-                                                             int T, int E, int k,
+                                                             int T, int E, int k, int gate_mode,
                                                              int32_t* __restrict__ topk_idx,
                                                              float* __restrict__ topk_w,
                                                              int32_t* __restrict__ hist) {
@@ -397,7 +421,8 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
   __syncthreads();  // the sums are in LDS, shist and sbr are set
   const int t = tt0 + tid;
   if (tid < RT_TT && t < T)
-    topk_thread(sl + tid * (EP + 1), sbr, E, k, t, topk_idx, topk_w, shist, nullptr, nullptr, nullptr, 0);
+    topk_thread(sl + tid * (EP + 1), sbr, E, k, gate_mode, t, topk_idx, topk_w, shist, nullptr,
+                nullptr, nullptr, 0);
   __syncthreads();  // the histogram atomics are done
   for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
@@ -411,7 +436,7 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
 template <int NBW>
 __global__ __launch_bounds__(512) void route_small_kernel(
     const float* __restrict__ partial, int nsplit, bool have_topk, const float* __restrict__ br,
-    int T, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int T, int E, int k, int gate_mode, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ tile_off0,
     int32_t* __restrict__ tile_off1, int4* __restrict__ tiles0, int4* __restrict__ tiles1, int bm0,
     int nt0, int max0, int bm1, int nt1, int max1, int32_t* __restrict__ row_of,
@@ -437,7 +462,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   __syncthreads();
   if (!have_topk) {
     if (tid < T)
-      topk_thread(sl + tid * (EP + 1), sbr, E, k, tid, topk_idx, topk_w, scnt, spick + tid * k, smask[0],
+      topk_thread(sl + tid * (EP + 1), sbr, E, k, gate_mode, tid, topk_idx, topk_w, scnt, spick + tid * k, smask[0],
                   smask[1], tid);
   } else {
     for (int p = tid; p < R; p += 512) {
@@ -534,7 +559,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
 
 template <int NBW>
 hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br, int T, int d,
-                             int E, int k, int nsplit, float* partial, int32_t* topk_idx,
+                             int E, int k, int gate_mode, int nsplit, float* partial, int32_t* topk_idx,
                              float* topk_w, int32_t* hist, uint8_t* xq, float* xs,
                              const SmallRoute* sr, hipStream_t stream) {
   const int tiles = ceil_div(T, RT_TT);
@@ -542,16 +567,16 @@ hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br
   const int gps = ceil_div(ngroups, nsplit);
   const int ns = ceil_div(ngroups, gps);
   hipLaunchKernelGGL((router_kernel<NBW>), dim3(tiles, ns), dim3(256), 0, stream, x, Wr, br, T, d,
-                     E, k, gps, partial, topk_idx, topk_w, hist, xq, xs);
+                     E, k, gate_mode, gps, partial, topk_idx, topk_w, hist, xq, xs);
   if (sr != nullptr)
     hipLaunchKernelGGL((route_small_kernel<NBW>), dim3(1), dim3(512), 0, stream, partial, ns, ns == 1,
-                       br, T, E, k, topk_idx, topk_w, sr->counts, sr->offsets, sr->tile_off0,
+                       br, T, E, k, gate_mode, topk_idx, topk_w, sr->counts, sr->offsets, sr->tile_off0,
                        sr->tile_off1, reinterpret_cast<int4*>(sr->tiles0),
                        reinterpret_cast<int4*>(sr->tiles1), sr->bm0, sr->nt0, sr->max0, sr->bm1,
                        sr->nt1, sr->max1, sr->row_of, sr->row_token);
   else if (ns > 1)
     hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(tiles), dim3(512), 0, stream, partial, ns,
-                       br, T, E, k, topk_idx, topk_w, hist);
+                       br, T, E, k, gate_mode, topk_idx, topk_w, hist);
   return hipGetLastError();
 }
 
@@ -569,13 +594,14 @@ int router_splits(int T, int d) {
 }
 
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
-                         int k, float* partial, int32_t* topk_idx, float* topk_w, int32_t* hist,
-                         uint8_t* xq, float* xs, const SmallRoute* sr, hipStream_t stream) {
+                         int k, int gate_mode, float* partial, int32_t* topk_idx, float* topk_w,
+                         int32_t* hist, uint8_t* xq, float* xs, const SmallRoute* sr,
+                         hipStream_t stream) {
   const int nsplit = router_splits(T, d);
   switch (ceil_div(E, 16)) {
 #define MOE_ROUTER_CASE(n)                                                                     \
   case n:                                                                                      \
-    return launch_router_nbw<n>(x, Wr, br, T, d, E, k, nsplit, partial, topk_idx, topk_w, hist, \
+    return launch_router_nbw<n>(x, Wr, br, T, d, E, k, gate_mode, nsplit, partial, topk_idx, topk_w, hist, \
                                 xq, xs, sr, stream);
     MOE_ROUTER_CASE(1)
     MOE_ROUTER_CASE(2)

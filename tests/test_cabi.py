@@ -70,13 +70,23 @@ def call(T=64, d=256, f=256, E=8, k=2, ws=None, flags=0, null=None, misalign=Non
     (dict(d=0), ERR_SHAPE), (dict(k=0), ERR_UNSUP), (dict(k=9, E=16), ERR_UNSUP),
     (dict(k=5, E=4), ERR_UNSUP), (dict(E=257), ERR_UNSUP), (dict(T=1 << 27, k=4), ERR_UNSUP),
     (dict(d=8320), ERR_UNSUP), (dict(f=8320), ERR_UNSUP), (dict(T=1 << 20, d=4096, k=1), ERR_UNSUP),
-    (dict(flags=3), ERR_FLAGS), (dict(ws=100), ERR_WS), (dict(null=0), ERR_NULL),
+    (dict(flags=3), ERR_FLAGS), (dict(flags=16), ERR_FLAGS), (dict(flags=3 | 4), ERR_FLAGS),
+    (dict(flags=1 << 31), ERR_FLAGS), (dict(ws=100), ERR_WS), (dict(null=0), ERR_NULL),
     (dict(null=9), ERR_NULL), (dict(null=10), ERR_NULL), (dict(misalign=3), ERR_ALIGN),
     (dict(misalign=0), ERR_ALIGN), (dict(stages=(3, 2)), ERR_FLAGS), (dict(stages=(0, 6)), ERR_FLAGS),
     (dict(stages=(-1, 2)), ERR_FLAGS),
 ])
 def test_argument_errors(kw, want):
     assert call(**kw) == want
+
+
+def test_gate_options_are_accepted_flags():
+    # the routing options are valid bits: with an empty batch the call returns OK
+    for fl in (4, 8, 12, 1 | 4, 2 | 8, 1 | 4 | 8):
+        assert call(T=0, null=0, flags=fl) == OK
+    assert moe.flags_of("decode", "softmax_topk", True) == 2 | 4 | 8
+    with pytest.raises(KeyError):
+        moe.flags_of(routing="sigmoid")
 
 
 def test_empty_batch_is_a_noop():

@@ -28,7 +28,8 @@ def run_debug(inp, path):
     p = moe.device_inputs(inp)
     dbg = moe.forward_debug(p["x"], p["W_router"], p["b_router"], p["k"], p["W_gateup"],
                             p["S_gateup"], p["b_gateup"], p["W_down"], p["S_down"], p["b_down"],
-                            path=path)
+                            path=path, routing=inp.get("routing", "topk_softmax"),
+                            gate_bf16=inp.get("gate_bf16", False))
     torch.cuda.synchronize()
     return dbg
 
@@ -81,6 +82,49 @@ def test_small_shapes_vs_oracle(shape, path):
     assert np.all(g[:, dr:] == 0), "padded output columns must be exactly zero"
     _say(f"   out {m}\n   h decisions differing from the oracle: {nflip}/{ncodes}; "
          f"down-stage err/bound {worst:.3f}")
+
+
+GATE_SHAPES = [
+    # (T, d, d_real, f, E, k): one-workgroup routing with split partials, with the
+    # router's in-place top-k (one 128-column group), the per-token finisher,
+    # and several tiles with the in-place top-k
+    (64, 256, 256, 256, 8, 2),
+    (1, 128, 128, 128, 2, 1),
+    (513, 384, 384, 512, 7, 3),
+    (77, 128, 128, 128, 256, 8),
+]
+GATE_OPTS = [("softmax_topk", False), ("softmax_topk", True), ("topk_softmax", True)]
+
+
+@pytest.mark.parametrize("routing,gate_bf16", GATE_OPTS, ids=[f"{r}-bf16{int(b)}" for r, b in GATE_OPTS])
+@pytest.mark.parametrize("shape", GATE_SHAPES, ids=[f"T{s[0]}-d{s[1]}-E{s[4]}-k{s[5]}" for s in GATE_SHAPES])
+def test_gate_options_vs_oracle(shape, routing, gate_bf16):
+    """Softmax over all experts before top-k, and bf16 gate weights: the same
+    selection and permutation, the oracle's weights, and the output gates."""
+    T, d, dr, f, E, k = shape
+    layer = gen.custom_layer(d, f, E, k, d_real=dr, layer_id=3000 + d + f + E + k)
+    inp = dict(gen.make_inputs(layer, T=T), routing=routing, gate_bf16=gate_bf16)
+    _say(f"[gate] shape={shape} routing={routing} bf16={gate_bf16}")
+    dbg = run_debug(inp, "auto")
+    ref = parity.oracle_ref(inp)
+    parity.check_routing(dbg, ref, T, k, gate_bf16=gate_bf16)
+    parity.check_combine_stage(dbg)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, dr)
+    _say(f"   out {m}")
+
+
+def test_gate_options_full_size_decode():
+    """The decode-shaped layer with both options (routing of every token)."""
+    inp = dict(gen.make_inputs("c1"), routing="softmax_topk", gate_bf16=True)
+    T, k = inp["T"], inp["k"]
+    dbg = run_debug(inp, "auto")
+    ref = parity.oracle_ref(inp)
+    parity.check_routing(dbg, ref, T, k, gate_bf16=True)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, inp["d_real"])
+    assert m["gate"] == "literal", m
+    _say(f"[gate] c1 out {m}")
 
 
 def test_deterministic_bits():
