@@ -7,7 +7,10 @@ The FP8 format is the one the "GPT-OSS on day 0" post serves the experts in
 (section "GPT-OSS on Hopper": FP8 with 128x128 block scaling).  Its element
 type is OCP E4M3 ("fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities, NaN = S.1111.111, largest finite 448, smallest
-subnormal 2^-9.  Everything here is written from that definition.
+subnormal 2^-9.  The MXFP8 variant (the post's section "Quantization" on
+Blackwell: microscaling) adds the OCP E8M0 scale: 8 exponent bits with bias
+127, no sign and no mantissa, code 0xFF = NaN.  Everything here is written
+from those definitions.
 """
 from __future__ import annotations
 
@@ -58,6 +61,16 @@ def e4m3_encode_rne(v: np.ndarray) -> np.ndarray:
     idx = np.searchsorted(_POS_VALUES, r)            # r is exactly a table value
     codes = idx.astype(np.uint8) | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
     return np.where(np.isnan(v), np.uint8(0x7F), codes).astype(np.uint8)
+
+
+E8M0_BIAS = 127
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale codes (uint8) -> fp64 powers of two 2^(c - 127); 0xFF -> NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    v = np.ldexp(1.0, c - E8M0_BIAS)
+    return np.where(c == 0xFF, np.nan, v)
 
 
 def bf16_decode(bits: np.ndarray) -> np.ndarray:

@@ -27,6 +27,12 @@ weighted accumulation):
 9. ``Y = deq(hq) @ deq(W_down) + b_down`` (fp64);
 10. ``out[t] = sum_j w[t,j] * Y[row(t,j)]`` in fp64, not rounded.
 
+MXFP8 variant (``inp["format"] == "mx"``; the post's section
+"Quantization" names microscaling as the Blackwell format, with the weights
+converted statically): steps 6 and 8 quantise per row per 32 columns with a
+power-of-two E8M0 scale, and the weights carry one E8M0 scale per 32 rows
+of K per column; everything else is unchanged.
+
 Readings of points the pages leave open are listed in the repository's
 design notes; each is marked "reading:" below where it is taken.
 
@@ -40,9 +46,10 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import bf16_decode, e4m3_decode, e4m3_encode_rne
+from .codecs import E8M0_BIAS, bf16_decode, e4m3_decode, e4m3_encode_rne, e8m0_decode
 
 GROUP = 128
+MX_GROUP = 32
 FP8_MAX = np.float32(448.0)
 
 
@@ -144,6 +151,65 @@ def dequant_weight(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
             * blk[:, None, :, None]).reshape(K, N)
 
 
+# ----------------------------------------------------------------------------- MXFP8
+#: 448 * 2^e for every exponent an E8M0 code can hold (1..254 -> -126..127, and 0 -> -127)
+_MX_EXPONENTS = np.arange(-E8M0_BIAS, E8M0_BIAS + 1)
+_MX_LIMITS = 448.0 * np.ldexp(1.0, _MX_EXPONENTS)
+
+
+def mx_scale_exponent(amax: np.ndarray) -> np.ndarray:
+    """Exponent e of the E8M0 scale 2^e of an MX block with largest magnitude ``amax``.
+
+    Reading: e is the smallest exponent with ``amax <= 448 * 2^e``, so no
+    element of the block saturates (the common Blackwell MXFP8 recipe); the
+    OCP rule floor(log2 amax) - 8 may clip the largest elements instead.  An
+    all-zero block gets the smallest scale, 2^-127.  Exact: the comparison
+    runs on fp64 values that hold 448 * 2^e and every fp32 amax exactly.
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    i = np.searchsorted(_MX_LIMITS, a.reshape(-1), side="left")
+    return _MX_EXPONENTS[np.minimum(i, len(_MX_LIMITS) - 1)].reshape(a.shape)
+
+
+def quantize_mx(v: np.ndarray):
+    """Per-row 1x32 MXFP8 quantisation of fp32 values ``v`` [N, K].
+
+    ``X = 2^e`` (``mx_scale_exponent`` of the block's amax), codes
+    ``e4m3_rne(v / X)``: the division by a power of two is exact, and
+    ``|v / X| <= 448`` by the choice of e.  Returns (codes uint8 [N, K],
+    E8M0 scale codes uint8 [N, K/32] = e + 127).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    N, K = v.shape
+    g = v.reshape(N, K // MX_GROUP, MX_GROUP).astype(np.float64)
+    amax = np.abs(g).max(axis=2) if N * K else np.zeros((N, K // MX_GROUP))
+    e = mx_scale_exponent(amax)
+    codes = e4m3_encode_rne(g / np.ldexp(1.0, e)[:, :, None])
+    return codes.reshape(N, K), (e + E8M0_BIAS).astype(np.uint8)
+
+
+def dequant_mx(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Inverse of ``quantize_mx`` in fp64: code value times its block's 2^e."""
+    N, K = codes.shape
+    return (e4m3_decode(codes).reshape(N, K // MX_GROUP, MX_GROUP)
+            * e8m0_decode(scales)[:, :, None]).reshape(N, K)
+
+
+def dequant_weight_mx(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """One expert's e4m3 matrix [K, N] times its E8M0 scales [K/32, N] (one per
+    32 rows of K per column: the MX blocks run along the contraction) -> fp64."""
+    K, N = codes.shape
+    return (e4m3_decode(codes).reshape(K // MX_GROUP, MX_GROUP, N)
+            * e8m0_decode(scales)[:, None, :]).reshape(K, N)
+
+
+#: quantise activations, dequantise them, dequantise one expert's weights
+FORMATS = {
+    "block128": (quantize_groups, dequant_groups, dequant_weight),
+    "mx": (quantize_mx, dequant_mx, dequant_weight_mx),
+}
+
+
 # ----------------------------------------------------------------------------- experts
 def silu(z: np.ndarray) -> np.ndarray:
     """z * sigmoid(z), fp64."""
@@ -151,19 +217,22 @@ def silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def expert_mlp(xdeq: np.ndarray, Wgu_e, Sgu_e, bgu_e, Wdn_e, Sdn_e, bdn_e, return_h=False):
+def expert_mlp(xdeq: np.ndarray, Wgu_e, Sgu_e, bgu_e, Wdn_e, Sdn_e, bdn_e, return_h=False,
+               fmt="block128"):
     """One expert on its rows: biased gate/up projection, SwiGLU, h quantisation,
     biased down projection ("GPT-OSS on day 0", section "GPT-OSS on Hopper":
     SwiGLU experts with biases; section "MoE": the bias sits in the GEMM).
+    ``fmt`` picks the FP8 scaling (``FORMATS``).
 
     Reading: columns [0,f) of the gate/up matrix are the gate, [f,2f) the up
     projection; h is rounded to fp32 before its quantisation.
     """
+    quant, deq, wdeq = FORMATS[fmt]
     f = Wgu_e.shape[1] // 2
-    P = xdeq @ dequant_weight(Wgu_e, Sgu_e) + bf16_decode(bgu_e)
+    P = xdeq @ wdeq(Wgu_e, Sgu_e) + bf16_decode(bgu_e)
     h = silu(P[:, :f]) * P[:, f:]
-    hq, hs = quantize_groups(h.astype(np.float32))
-    Y = dequant_groups(hq, hs) @ dequant_weight(Wdn_e, Sdn_e) + bf16_decode(bdn_e)
+    hq, hs = quant(h.astype(np.float32))
+    Y = deq(hq, hs) @ wdeq(Wdn_e, Sdn_e) + bf16_decode(bdn_e)
     if return_h:
         return Y, P, h, hq, hs
     return Y
@@ -194,15 +263,19 @@ def forward(inp: dict, tokens=None, keep=False):
     """The whole block. ``tokens`` (optional) restricts the expert work and the
     output to a subset of tokens; routing and permutation cover all tokens.
 
+    ``inp["format"]`` (optional): "block128" (default) or "mx".
+
     Returns a dict: out64 [len(tokens), d] fp64 (unrounded), routing arrays,
     xq/xs for the evaluated tokens, and (with ``keep``) per-row intermediates.
     """
     T, k, E = inp["T"], inp["k"], inp["E"]
+    fmt = inp.get("format", "block128")
+    quant, deq, _ = FORMATS[fmt]
     r = route(inp)
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     x32 = bf16_decode(inp["x"][tok]).astype(np.float32)
-    xq, xs = quantize_groups(x32)
-    xdeq = dequant_groups(xq, xs)
+    xq, xs = quant(x32)
+    xdeq = deq(xq, xs)
     d = inp["d"]
     out = np.zeros((len(tok), d))
     inter = {}
@@ -212,7 +285,8 @@ def forward(inp: dict, tokens=None, keep=False):
         if len(pos) == 0:
             continue
         res = expert_mlp(xdeq[pos], inp["W_gateup"][e], inp["S_gateup"][e], inp["b_gateup"][e],
-                         inp["W_down"][e], inp["S_down"][e], inp["b_down"][e], return_h=keep)
+                         inp["W_down"][e], inp["S_down"][e], inp["b_down"][e], return_h=keep,
+                         fmt=fmt)
         Y = res[0] if keep else res
         np.add.at(out, pos, r["w"][tok[pos], slot][:, None] * Y)
         if keep:

@@ -114,6 +114,29 @@ def quantize_weight_blocks(w: np.ndarray):
     return codes, s.numpy().astype(np.float32)
 
 
+MX_BLOCK = 32         # MX block length along K
+
+
+def quantize_weight_mx(w: np.ndarray):
+    """Static MXFP8 conversion of one expert matrix ``w`` [K, N] (fp32).
+
+    One E8M0 scale 2^e per 32 consecutive K rows of a column, e the smallest
+    exponent with amax <= 448 * 2^e (amax = m * 2^p with m in [0.5, 1):
+    e = p - 9 if m <= 0.875, else p - 8), 2^-127 for an all-zero block;
+    codes = e4m3(w / 2^e), round-to-nearest-even.
+    Returns (codes uint8 [K, N], E8M0 codes uint8 [K/32, N]).
+    """
+    K, N = w.shape
+    t = torch.from_numpy(w).double().view(K // MX_BLOCK, MX_BLOCK, N)
+    amax = t.abs().amax(dim=1)
+    m, p = torch.frexp(amax)
+    e = torch.where(m <= 0.875, p - 9, p - 8)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127)).clamp(-127, 127)
+    q = t / torch.ldexp(torch.ones_like(amax), e).view(K // MX_BLOCK, 1, N)
+    codes = q.float().to(torch.float8_e4m3fn).view(torch.uint8).reshape(K, N).numpy()
+    return codes, (e + 127).to(torch.uint8).numpy()
+
+
 def _draw_router(layer: Layer, seed: int):
     d, dr, E = layer.d, layer.d_real, layer.E
     Wr = np.zeros((d, E), np.float32)
@@ -193,7 +216,7 @@ def draw_x(layer: Layer, T: int, seed: int, Wr, br, margin=MARGIN):
     return x
 
 
-def _expert_weights(layer: Layer, seed: int, e: int):
+def _expert_weights(layer: Layer, seed: int, e: int, fmt: str = "block128"):
     d, dr, f = layer.d, layer.d_real, layer.f
     wgu = np.zeros((d, 2 * f), np.float32)
     wgu[:dr] = _rng(seed, layer.layer_id, _T_WGU, e).standard_normal((dr, 2 * f), dtype=np.float32)
@@ -201,15 +224,21 @@ def _expert_weights(layer: Layer, seed: int, e: int):
     wdn = np.zeros((f, d), np.float32)
     wdn[:, :dr] = _rng(seed, layer.layer_id, _T_WDN, e).standard_normal((f, dr), dtype=np.float32)
     wdn[:, :dr] *= np.float32(1.0 / np.sqrt(f))
-    return quantize_weight_blocks(wgu), quantize_weight_blocks(wdn)
+    conv = quantize_weight_mx if fmt == "mx" else quantize_weight_blocks
+    return conv(wgu), conv(wdn)
 
 
 _WEIGHT_CACHE: dict = {}
 
 
-def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache: bool = True):
-    """All layer parameters as NumPy arrays (FP8 codes as uint8, bf16 as uint16 bits)."""
-    key = (layer, seed)
+def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache: bool = True,
+                 fmt: str = "block128"):
+    """All layer parameters as NumPy arrays (FP8 codes as uint8, bf16 as uint16 bits).
+    ``fmt``: "block128" (fp32 scales per 128x128 block) or "mx" (E8M0 scales
+    per 32 K rows per column); the underlying fp32 draws are the same."""
+    if fmt not in ("block128", "mx"):
+        raise ValueError(f"unknown weight format {fmt!r}")
+    key = (layer, seed, fmt)
     if cache and key in _WEIGHT_CACHE:
         return _WEIGHT_CACHE[key]
     d, f, E = layer.d, layer.f, layer.E
@@ -217,12 +246,16 @@ def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache:
     if layer.router == "zipf":
         br = _calibrate_zipf_bias(layer, seed, Wr)
     Wgu = np.empty((E, d, 2 * f), np.uint8)
-    Sgu = np.empty((E, d // BLOCK, 2 * f // BLOCK), np.float32)
     Wdn = np.empty((E, f, d), np.uint8)
-    Sdn = np.empty((E, f // BLOCK, d // BLOCK), np.float32)
+    if fmt == "mx":
+        Sgu = np.empty((E, d // MX_BLOCK, 2 * f), np.uint8)
+        Sdn = np.empty((E, f // MX_BLOCK, d), np.uint8)
+    else:
+        Sgu = np.empty((E, d // BLOCK, 2 * f // BLOCK), np.float32)
+        Sdn = np.empty((E, f // BLOCK, d // BLOCK), np.float32)
 
     def job(e):
-        (Wgu[e], Sgu[e]), (Wdn[e], Sdn[e]) = _expert_weights(layer, seed, e)
+        (Wgu[e], Sgu[e]), (Wdn[e], Sdn[e]) = _expert_weights(layer, seed, e, fmt)
 
     workers = workers or min(16, len(os.sched_getaffinity(0)))
     if E * d * f > (1 << 22):
@@ -244,13 +277,15 @@ def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache:
     return w
 
 
-def make_inputs(cfg, seed: int = 0, T: int | None = None, margin=MARGIN):
+def make_inputs(cfg, seed: int = 0, T: int | None = None, margin=MARGIN, fmt: str = "block128"):
     """Full input set for a named config (``"c0"`` ...) or a (Layer, T) pair.
 
-    Returns a dict with the layer shape (T, d, d_real, f, E, k) and the arrays
-    x (bf16 bits [T,d]), W_router [d,E], b_router [E], W_gateup (e4m3 [E,d,2f]),
-    S_gateup [E,d/128,2f/128], b_gateup (bf16 bits [E,2f]), W_down (e4m3 [E,f,d]),
-    S_down [E,f/128,d/128], b_down (bf16 bits [E,d]).
+    Returns a dict with the layer shape (T, d, d_real, f, E, k), the weight
+    ``format`` and the arrays x (bf16 bits [T,d]), W_router [d,E], b_router [E],
+    W_gateup (e4m3 [E,d,2f]), S_gateup, b_gateup (bf16 bits [E,2f]), W_down
+    (e4m3 [E,f,d]), S_down, b_down (bf16 bits [E,d]).  Scales: "block128"
+    fp32 [E,d/128,2f/128] and [E,f/128,d/128]; "mx" E8M0 uint8 [E,d/32,2f]
+    and [E,f/32,d].
     """
     if isinstance(cfg, str):
         c = CONFIGS[cfg]
@@ -258,9 +293,9 @@ def make_inputs(cfg, seed: int = 0, T: int | None = None, margin=MARGIN):
     else:
         layer = cfg
         assert T is not None
-    w = make_weights(layer, seed)
+    w = make_weights(layer, seed, fmt=fmt)
     x = draw_x(layer, T, seed, w["W_router"], w["b_router"], margin)
-    out = dict(T=T, d=layer.d, d_real=layer.d_real, f=layer.f, E=layer.E, k=layer.k, x=x)
+    out = dict(T=T, d=layer.d, d_real=layer.d_real, f=layer.f, E=layer.E, k=layer.k, x=x, format=fmt)
     out.update(w)
     return out
 

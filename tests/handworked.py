@@ -21,7 +21,7 @@ def load():
         return json.load(fh)
 
 
-def build(k: int) -> dict:
+def build(k: int, fmt: str = "block128") -> dict:
     d = f = 128
     E = 2
     x = np.zeros((1, d), np.float32)
@@ -45,14 +45,18 @@ def build(k: int) -> dict:
         Wdn[1] = 0x38
     else:
         bdn[1, 3] = 1.0
+    if fmt == "mx":  # the same power-of-two scales as E8M0 codes per 32 K rows per column
+        Sgu = np.full((E, d // 32, 2 * f), 127, np.uint8)
+        Sdn = np.stack([np.full((f // 32, d), 126, np.uint8), np.full((f // 32, d), 127, np.uint8)])
     return dict(T=1, d=d, d_real=d, f=f, E=E, k=k, x=_bf16(x), W_router=Wr, b_router=br,
                 W_gateup=Wgu, S_gateup=Sgu, b_gateup=_bf16(bgu), W_down=Wdn, S_down=Sdn,
-                b_down=_bf16(bdn))
+                b_down=_bf16(bdn), format=fmt)
 
 
-def expected(k: int) -> np.ndarray:
+def expected(k: int, fmt: str = "block128") -> np.ndarray:
     fx = load()
+    exp = fx["mx"]["expected"] if fmt == "mx" else fx["expected"]
     out = np.zeros(128)
-    for i, v in fx["expected"][f"k{k}"].items():
+    for i, v in exp[f"k{k}"].items():
         out[int(i)] = v
     return out

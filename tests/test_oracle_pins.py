@@ -344,3 +344,173 @@ def test_silu_vs_torch():
     z = np.linspace(-60, 60, 2001)
     np.testing.assert_allclose(oracle.silu(z), torch.nn.functional.silu(torch.from_numpy(z)).numpy(),
                                rtol=1e-15, atol=1e-300)
+
+
+# ------------------------------------------------------------------ MXFP8 variant
+def test_e8m0_decode_format_points():
+    fx = json.load(open(os.path.join(GOLD, "e8m0_points.json")))
+    for code, val in fx["points"].items():
+        assert codecs.e8m0_decode(np.uint8(int(code, 16))) == val, code
+    for code in fx["nan_codes"]:
+        assert np.isnan(codecs.e8m0_decode(np.uint8(int(code, 16))))
+    allv = codecs.e8m0_decode(np.arange(255, dtype=np.uint8))
+    assert np.all(allv[1:] == 2 * allv[:-1])                 # consecutive powers of two
+
+
+def _mx_exponent_frexp(a):
+    """Independent derivation: a = m 2^p, m in [0.5, 1); 448 = 0.875 * 2^9."""
+    m, p = np.frexp(np.asarray(a, np.float64))
+    e = np.where(m <= 0.875, p - 9, p - 8)
+    return np.clip(np.where(a > 0, e, -127), -127, 127)
+
+
+def test_mx_scale_exponent_closed_forms_and_minimality():
+    f32 = np.float32
+    cases = {448.0: 0, 3.5: -7, 1.0: -8, 0.875: -9, 0.0: -127, 449.0: 1, 224.0: -1, 224.5: 0,
+             float(np.nextafter(f32(448), f32(1e9))): 1, float(np.nextafter(f32(448), f32(0))): 0,
+             448.0 * 2.0 ** 100: 100, 448.0 * 2.0 ** -126: -126, 1e-45: -127}
+    for a, e in cases.items():
+        assert int(oracle.mx_scale_exponent(np.array(a))) == e, a
+    rng = np.random.default_rng(11)
+    a = np.concatenate([
+        np.abs(rng.normal(size=4000) * np.exp(rng.uniform(-60, 60, 4000))),
+        # ulp neighbours of 448 * 2^n, where a rounding slip would show
+        np.nextafter(np.float32(448) * np.float32(2.0) ** np.arange(-40, 40, dtype=np.float32),
+                     np.float32(np.inf)),
+        np.nextafter(np.float32(448) * np.float32(2.0) ** np.arange(-40, 40, dtype=np.float32),
+                     np.float32(0)),
+    ]).astype(np.float32).astype(np.float64)
+    e = oracle.mx_scale_exponent(a)
+    assert np.all(a <= 448.0 * np.ldexp(1.0, e))
+    assert np.all((e == -127) | (a > 448.0 * np.ldexp(1.0, e - 1)))
+    np.testing.assert_array_equal(e, _mx_exponent_frexp(a))
+
+
+def test_quantize_mx_vs_torch_cast():
+    """Library special case: the power-of-two scale from the frexp derivation,
+    then PyTorch's float8_e4m3fn cast of v / 2^e (exact division)."""
+    rng = np.random.default_rng(12)
+    v = (rng.normal(size=(48, 256)) * np.exp(rng.uniform(-8, 8, size=(48, 8))).repeat(32, 1))
+    v = v.astype(np.float32)
+    v[5, 64:96] = 0.0
+    q, sc = oracle.quantize_mx(v)
+    t = torch.from_numpy(v).double().view(48, 8, 32)
+    e = torch.from_numpy(_mx_exponent_frexp(t.abs().amax(dim=2).numpy()))
+    tq = (t / torch.ldexp(torch.ones(()), e.double()).unsqueeze(2)).float()
+    tq = tq.to(torch.float8_e4m3fn).view(torch.uint8).reshape(48, 256).numpy()
+    np.testing.assert_array_equal(q, tq)
+    np.testing.assert_array_equal(sc, (e.numpy() + 127).astype(np.uint8))
+    assert sc[5, 2] == 0 and np.all(q[5, 64:96] == 0)
+
+
+def test_quantize_mx_properties():
+    rng = np.random.default_rng(13)
+    v = (rng.normal(size=(30, 128)) * rng.uniform(1e-3, 1e3, size=(30, 1))).astype(np.float32)
+    q, sc = oracle.quantize_mx(v)
+    assert q.shape == (30, 128) and sc.shape == (30, 4) and sc.dtype == np.uint8
+    vals = codecs.e4m3_decode(q).reshape(30, 4, 32)
+    # amax / 2^e lies in (224, 448] (the scale is as small as it can be), so
+    # the block's largest code is in [224, 448] (e4m3 rounds (224, 232] to 224)
+    bmax = np.abs(vals).max(axis=2)
+    assert np.all(bmax >= 224) and np.all(bmax <= 448)
+    deq = oracle.dequant_mx(q, sc)
+    X = np.repeat(codecs.e8m0_decode(sc), 32, axis=1)
+    err = np.abs(deq - v)
+    assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, X * 2.0 ** -10) * (1 + 1e-12))
+    # its own output is a fixed point in value (a block whose max rounded down
+    # to 224 X re-quantises with X / 2 and doubled codes)
+    q2, sc2 = oracle.quantize_mx(deq.astype(np.float32))
+    np.testing.assert_array_equal(oracle.dequant_mx(q2, sc2), deq)
+    # blocks are independent: scaling one block by 2^5 moves only its scale
+    v3 = v.copy()
+    v3[:, 32:64] *= np.float32(32.0)
+    q3, sc3 = oracle.quantize_mx(v3)
+    np.testing.assert_array_equal(q3, q)
+    np.testing.assert_array_equal(sc3[:, 1], sc[:, 1] + 5)
+    np.testing.assert_array_equal(np.delete(sc3, 1, axis=1), np.delete(sc, 1, axis=1))
+
+
+def test_dequant_weight_mx_brute_force_and_block_reduction():
+    rng = np.random.default_rng(14)
+    K, N = 256, 384
+    codes = rng.integers(0, 256, size=(K, N), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A
+    sc = rng.integers(100, 150, size=(K // 32, N), dtype=np.uint8)
+    W = oracle.dequant_weight_mx(codes, sc)
+    for (kk, n) in [(0, 0), (31, 5), (32, 5), (255, 383), (100, 200), (64, 130)]:
+        assert W[kk, n] == codecs.E4M3_TABLE[codes[kk, n]] * 2.0 ** (int(sc[kk // 32, n]) - 127)
+    # scales constant over each 128x128 block: the 128x128 block-scaled format
+    blk = rng.integers(110, 140, size=(K // 128, N // 128))
+    sc_mx = np.repeat(np.repeat(blk, 4, axis=0), 128, axis=1).astype(np.uint8)
+    S = np.ldexp(1.0, blk - 127).astype(np.float32)
+    np.testing.assert_array_equal(oracle.dequant_weight_mx(codes, sc_mx), oracle.dequant_weight(codes, S))
+
+
+def test_mx_weight_conversion_round_trip():
+    """The generator's static MX conversion, checked against the oracle's MX
+    quantiser applied along K (the same rule, written independently)."""
+    rng = np.random.default_rng(15)
+    w = (rng.normal(size=(128, 256)) * 0.05).astype(np.float32)
+    w[:32, 7] = 0.0
+    codes, sc = gen.quantize_weight_mx(w)
+    q, s = oracle.quantize_mx(np.ascontiguousarray(w.T))
+    np.testing.assert_array_equal(codes, q.T)
+    np.testing.assert_array_equal(sc, s.T)
+
+
+def _torch_quant_mx(v32):
+    n, K = v32.shape
+    g = v32.double().view(n, K // 32, 32)
+    e = torch.from_numpy(_mx_exponent_frexp(g.abs().amax(dim=2).numpy())).double()
+    X = torch.ldexp(torch.ones(()), e).unsqueeze(2)
+    q = (g / X).float().to(torch.float8_e4m3fn).double()
+    return (q * X).view(n, K)
+
+
+def test_mx_single_expert_reduces_to_dense_swiglu_mlp():
+    layer = gen.custom_layer(256, 384, 1, 1, d_real=200, layer_id=202)
+    inp = gen.make_inputs(layer, T=24, fmt="mx")
+    res = oracle.forward(inp)
+    bf = lambda b: torch.from_numpy(gen.bf16_bits_to_f32(b)).double()
+    x = bf(inp["x"]).float()
+    f = inp["f"]
+
+    def wdeq(codes, sc):
+        w = torch.from_numpy(codes).view(torch.float8_e4m3fn).double()
+        return w * torch.ldexp(torch.ones(()), torch.from_numpy(sc.astype(np.int64) - 127).double()
+                               ).repeat_interleave(32, 0)
+
+    P = _torch_quant_mx(x) @ wdeq(inp["W_gateup"][0], inp["S_gateup"][0]) + bf(inp["b_gateup"][0])
+    h = torch.nn.functional.silu(P[:, :f]) * P[:, f:]
+    dense = _torch_quant_mx(h.float()) @ wdeq(inp["W_down"][0], inp["S_down"][0]) + bf(inp["b_down"][0])
+    np.testing.assert_allclose(res["out64"], dense.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,d,f,E,k", [(8, 128, 128, 4, 2), (9, 256, 128, 6, 6)])
+def test_mx_sparse_block_equals_all_experts_brute_force(T, d, f, E, k):
+    layer = gen.custom_layer(d, f, E, k, layer_id=320 + E)
+    inp = gen.make_inputs(layer, T=T, fmt="mx")
+    res = oracle.forward(inp)
+    xf = gen.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    L = xf @ inp["W_router"].astype(np.float64) + inp["b_router"].astype(np.float64)
+    xdeq = _torch_quant_mx(torch.from_numpy(xf.astype(np.float32))).numpy()
+    out = np.zeros((T, d))
+    for t in range(T):
+        rank = lambda e: sum(1 for e2 in range(E) if L[t, e2] > L[t, e] or (L[t, e2] == L[t, e] and e2 < e))
+        sel = [e for e in range(E) if rank(e) < k]
+        for e in sel:
+            w = math.exp(L[t, e]) / sum(math.exp(L[t, e2]) for e2 in sel)
+            Y = oracle.expert_mlp(xdeq[t:t + 1], inp["W_gateup"][e], inp["S_gateup"][e], inp["b_gateup"][e],
+                                  inp["W_down"][e], inp["S_down"][e], inp["b_down"][e], fmt="mx")
+            out[t] += w * Y[0]
+    np.testing.assert_allclose(res["out64"], out, rtol=1e-12, atol=1e-12 * np.abs(out).max())
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_handworked_block_mx(k):
+    inp = handworked.build(k, fmt="mx")
+    res = oracle.forward(inp)
+    want = handworked.expected(k, fmt="mx")
+    assert list(res["idx"][0]) == ([0] if k == 1 else [0, 1])
+    np.testing.assert_allclose(res["out64"][0], want, rtol=0, atol=1e-12 * np.abs(want).max())
+    assert res["xq"][0, 0] == 0x7E and res["xq"][0, 1] == 0x76 and res["xs"][0, 0] == 127 - 7
