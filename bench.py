@@ -1,13 +1,14 @@
 """Benchmark of the sparse MoE block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1] [--format block128|mx]
 
 A step is one whole forward (router + top-k + softmax + x quantisation,
 routing scan and placement, gate/up grouped FP8 GEMM with SwiGLU and h
 quantisation, down grouped FP8 GEMM, weighted combine) over one batch of
 seeded synthetic input already resident in HBM.  The default workload is the
 decode-shaped gpt-oss-20b-like layer (T=64 tokens, d=2944, f=2944, E=32,
-k=4).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
+k=4) with 128x128 block-scaled FP8 weights (``--format mx``: the MXFP8
+variant, E8M0 scales per 32).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
 GEMM (its duration measured with HIP events inside the timed region, on the
 stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload.
@@ -41,7 +42,8 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # FETCH_SIZE counts the 128-byte fabric reads of gfx950 as 64 bytes (the copy
 # reads as 524312 KiB), WRITE_SIZE reads the copy exactly.  Keyed by the
 # SHA-256 of the GEMM source the counters were taken on: any change to the
-# kernels reports null until they are measured again.
+# kernels reports null until they are measured again.  Keys: workload, or
+# workload-mx for the MXFP8 format.
 TRAFFIC = {
     "c1": {"gemm_sha256": "92db357d303f25dafa9254f5810a78d180033f1a98328fd59fdd1017981ced53",
            "fetch_kib": 271898.225, "write_kib": 765.15625,
@@ -71,28 +73,42 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _scale_bytes(K, N, fmt):
+    """Bytes of the scales of one K x N weight matrix: fp32 per 128x128 block,
+    or one E8M0 byte per 32 K rows per column (MX)."""
+    return (K // 32) * N if fmt == "mx" else 4 * (K // 128) * (N // 128)
+
+
+def _act_scale_bytes(rows, K):
+    """Scales of rows x K quantised activations: fp32 per 128 or E8M0 per 32:
+    the same byte count."""
+    return rows * (K // 32)
+
+
 def gateup_algorithmic(inp, counts):
     """Algorithmic HBM bytes and FP8 flops of one gate/up GEMM launch.
 
-    Bytes: every touched expert's gate/up weights (e4m3 codes, fp32 block
-    scales, bf16 bias) once, the quantised activations of every token once
-    (codes + scales), and the h codes + scales of every routed row once.
+    Bytes: every touched expert's gate/up weights (e4m3 codes, scales, bf16
+    bias) once, the quantised activations of every token once (codes +
+    scales), and the h codes + scales of every routed row once.
     Flops: 2 * rows * d * 2f."""
     T, d, f, k = inp["T"], inp["d"], inp["f"], inp["k"]
+    fmt = inp.get("format", "block128")
     R = T * k
     touched = int(np.count_nonzero(counts))
-    w = touched * (d * 2 * f + 4 * (d // 128) * (2 * f // 128) + 2 * 2 * f)
-    a = T * d + 4 * T * (d // 128)
-    h = R * f + 4 * R * (f // 128)
+    w = touched * (d * 2 * f + _scale_bytes(d, 2 * f, fmt) + 2 * 2 * f)
+    a = T * d + _act_scale_bytes(T, d)
+    h = R * f + _act_scale_bytes(R, f)
     return dict(bytes=w + a + h, flops=2.0 * R * d * 2 * f, touched=touched)
 
 
 def down_algorithmic(inp, counts):
     T, d, f, k = inp["T"], inp["d"], inp["f"], inp["k"]
+    fmt = inp.get("format", "block128")
     R = T * k
     touched = int(np.count_nonzero(counts))
-    w = touched * (f * d + 4 * (f // 128) * (d // 128) + 2 * d)
-    return dict(bytes=w + R * f + 4 * R * (f // 128) + 4 * R * d, flops=2.0 * R * f * d)
+    w = touched * (f * d + _scale_bytes(f, d, fmt) + 2 * d)
+    return dict(bytes=w + R * f + _act_scale_bytes(R, f) + 4 * R * d, flops=2.0 * R * f * d)
 
 
 def cpu_baseline(inp, budget_s=12.0):
@@ -125,6 +141,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS))
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
+    ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),
+                    help="weight format: 128x128 block-scaled FP8 or MXFP8 (E8M0 per 32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, one device-to-device copy of this many MiB "
@@ -138,7 +156,8 @@ def main():
     cfg = gen.CONFIGS[args.workload]
     log(f"[bench] generating {cfg.name} (T={cfg.T}, d={cfg.layer.d}, f={cfg.layer.f}, "
         f"E={cfg.layer.E}, k={cfg.layer.k})")
-    inp = gen.make_inputs(cfg.name)
+    fmt = args.format
+    inp = gen.make_inputs(cfg.name, fmt=fmt)
     dev = torch.device("cuda:0")
     p = moe.device_inputs(inp, dev)
     T, d, f, E, k = inp["T"], inp["d"], inp["f"], inp["E"], inp["k"]
@@ -158,7 +177,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    dbg = moe.forward_debug(x, *w_args, path=args.path)
+    dbg = moe.forward_debug(x, *w_args, path=args.path, fmt=fmt)
     torch.cuda.synchronize()
     counts = np.diff(dbg["offsets"].cpu().numpy())
     del dbg
@@ -166,16 +185,16 @@ def main():
     da = down_algorithmic(inp, counts)
 
     def step(ev=None):
-        moe.forward_stages("router", "place", x, *w_args, out, ws, path=args.path)
+        moe.forward_stages("router", "place", x, *w_args, out, ws, path=args.path, fmt=fmt)
         if ev is not None:
             ev[0].record()
-        moe.forward_stages("gateup", "gateup", x, *w_args, out, ws, path=args.path)
+        moe.forward_stages("gateup", "gateup", x, *w_args, out, ws, path=args.path, fmt=fmt)
         if ev is not None:
             ev[1].record()
-        moe.forward_stages("down", "down", x, *w_args, out, ws, path=args.path)
+        moe.forward_stages("down", "down", x, *w_args, out, ws, path=args.path, fmt=fmt)
         if ev is not None:
             ev[2].record()
-        moe.forward_stages("combine", "combine", x, *w_args, out, ws, path=args.path)
+        moe.forward_stages("combine", "combine", x, *w_args, out, ws, path=args.path, fmt=fmt)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -197,17 +216,20 @@ def main():
     tok_s = T / (ms * 1e-3)
 
     decode = (args.path == "decode") or (args.path == "auto" and T * k <= 32 * E)
+    tkey = args.workload + ("-mx" if fmt == "mx" else "")
     if decode:
         ach = ga["bytes"] / (gate_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(args.workload)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(tkey)}
     else:
         ach = ga["flops"] / (gate_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(args.workload)}
-    roof["kernel"] = ("grouped_gemm_dma_kernel<true, 32, 256>" if decode else
-                      "grouped_gemm_wide_kernel<true>") + " (gate/up + bias + SwiGLU + h quantisation)"
+                "traffic": measured_traffic(tkey)}
+    mxs = "true" if fmt == "mx" else "false"
+    roof["kernel"] = (f"grouped_gemm_dma_kernel<true, 32, 256, {mxs}>" if decode else
+                      f"grouped_gemm_wide_kernel<true, {mxs}>") + \
+        " (gate/up + bias + SwiGLU + h quantisation)"
     roof["avg_ms"] = round(gate_ms, 5)
     roof["algorithmic_bytes"] = ga["bytes"]
     roof["algorithmic_flops"] = ga["flops"]
@@ -219,7 +241,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.layer.name} {cfg.role} T={T} d={d} "
                                f"(real {inp['d_real']}) f={f} E={E} k={k}",
-                   "T": T, "d": d, "f": f, "E": E, "k": k, "path": args.path,
+                   "T": T, "d": d, "f": f, "E": E, "k": k, "path": args.path, "format": fmt,
                    "experts_touched": ga["touched"]},
         "roofline": roof,
         "stages_ms": {"gateup": round(gate_ms, 5), "down": round(down_ms, 5),

@@ -88,6 +88,19 @@ typedef enum {
  * they stay fp32). */
 #define MOE_ROUTE_SOFTMAX_ALL 4u
 #define MOE_GATE_BF16 8u
+/* MOE_FORMAT_MX: the MXFP8 variant ("GPT-OSS on day 0", section
+ * "Quantization": microscaling, the Blackwell format, with the weights
+ * converted statically).  Every 32 consecutive elements along the
+ * contraction share one E8M0 scale (a uint8 e; value 2^(e-127), 0xFF NaN):
+ *   S_gateup   E8M0 [E, d/32, 2f]   scale of W_gateup[e, 32i..32i+31, c]
+ *   S_down     E8M0 [E, f/32, d]    scale of W_down[e, 32i..32i+31, c]
+ * passed through the `const float*` scale arguments (moe_forward_mx takes
+ * them typed).  x and h are quantised per 32 columns: the scale 2^e of a
+ * block is the smallest power of two with amax <= 448 * 2^e (2^-127 for an
+ * all-zero block; no element saturates), q = e4m3_rne(v / 2^e).  The debug
+ * copies xs / hs then hold E8M0 bytes [T, d/32] / [T*k, f/32]: the same
+ * byte counts as the fp32 scales of the default format. */
+#define MOE_FORMAT_MX 16u
 
 /* Bytes of device workspace moe_forward needs for these sizes (0 if the sizes
  * are invalid).  The workspace holds the routing tables, the quantised
@@ -117,11 +130,22 @@ moe_status moe_forward(const void* x, const float* W_router, const float* b_rout
                        size_t workspace_bytes, void* stream);
 
 /* moe_forward with `flags`: a GEMM path (MOE_PATH_*; the paths give the same
- * results to rounding of the fp32 accumulation order) and the gate-weight
- * options MOE_ROUTE_SOFTMAX_ALL and MOE_GATE_BF16. */
+ * results to rounding of the fp32 accumulation order), the gate-weight
+ * options MOE_ROUTE_SOFTMAX_ALL and MOE_GATE_BF16, and the weight format
+ * MOE_FORMAT_MX. */
 moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_router, int32_t k,
                           const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                           const uint8_t* W_down, const float* S_down, const void* b_down,
+                          void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream);
+
+/* moe_forward_ex with MXFP8 weights (flags | MOE_FORMAT_MX):
+ *   X_gateup   E8M0 [E, d/32, 2f]
+ *   X_down     E8M0 [E, f/32, d]
+ * the other arguments and `flags` bits as for moe_forward_ex. */
+moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_router, int32_t k,
+                          const uint8_t* W_gateup, const uint8_t* X_gateup, const void* b_gateup,
+                          const uint8_t* W_down, const uint8_t* X_down, const void* b_down,
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
                           size_t workspace_bytes, uint32_t flags, void* stream);
 

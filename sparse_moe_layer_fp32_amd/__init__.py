@@ -1,7 +1,7 @@
 """Sparse MoE block forward on one MI355X (gfx950): Python binding of the C ABI.
 
 The block (router with bias, top-k, softmax over the selected logits, FP8
-128x128 block-scaled SwiGLU experts with biases, weighted combine) runs in
+SwiGLU experts with biases, 128x128 block-scaled or MXFP8, weighted combine) runs in
 HIP kernels of ``libsparse_moe.so``; this module only checks tensors and
 passes device pointers and the current HIP stream (see ``include/moe.h``).
 There is no CPU fallback: without the built library every call raises.
@@ -19,17 +19,22 @@ LIB_PATH = os.path.join(_PKG, "libsparse_moe.so")
 PATHS = {"auto": 0, "prefill": 1, "decode": 2}
 ROUTINGS = {"topk_softmax": 0, "softmax_topk": 4}   # MOE_ROUTE_SOFTMAX_ALL
 GATE_BF16 = 8                                       # MOE_GATE_BF16
+FORMATS = {"block128": 0, "mx": 16}                 # MOE_FORMAT_MX
 
 
-def flags_of(path="auto", routing="topk_softmax", gate_bf16=False) -> int:
-    """The C ABI's `flags` word: GEMM path, gate-weight rule, bf16 gate weights."""
-    return PATHS[path] | ROUTINGS[routing] | (GATE_BF16 if gate_bf16 else 0)
+def flags_of(path="auto", routing="topk_softmax", gate_bf16=False, fmt="block128") -> int:
+    """The C ABI's `flags` word: GEMM path, gate-weight rule, bf16 gate weights,
+    weight format."""
+    return PATHS[path] | ROUTINGS[routing] | (GATE_BF16 if gate_bf16 else 0) | FORMATS[fmt]
+
+
 BLOCK = 128
+MX_BLOCK = 32
 MAX_EXPERTS = 256
 MAX_TOPK = 8
 
-SYMBOLS = ("moe_workspace_bytes", "moe_forward", "moe_forward_ex", "moe_forward_stages",
-           "moe_forward_debug", "moe_status_string")
+SYMBOLS = ("moe_workspace_bytes", "moe_forward", "moe_forward_ex", "moe_forward_mx",
+           "moe_forward_stages", "moe_forward_debug", "moe_status_string")
 STAGES = {"router": 0, "scan": 1, "place": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -61,6 +66,8 @@ def lib() -> ctypes.CDLL:
     L.moe_forward.argtypes = fwd + [P]
     L.moe_forward_ex.restype = I
     L.moe_forward_ex.argtypes = fwd + [U, P]
+    L.moe_forward_mx.restype = I
+    L.moe_forward_mx.argtypes = fwd + [U, P]
     L.moe_forward_stages.restype = I
     L.moe_forward_stages.argtypes = fwd + [U, I, I, P]
     L.moe_forward_debug.restype = I
@@ -113,8 +120,17 @@ def _stream(device, stream, *tensors):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def scale_shapes(d, f, E, fmt="block128"):
+    """(shape, element bytes) of S_gateup and S_down for a weight format."""
+    if fmt == "mx":
+        return ((E, d // MX_BLOCK, 2 * f), 1), ((E, f // MX_BLOCK, d), 1)
+    if fmt == "block128":
+        return ((E, d // BLOCK, 2 * f // BLOCK), 4), ((E, f // BLOCK, d // BLOCK), 4)
+    raise ValueError(f"unknown weight format {fmt!r}")
+
+
 def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
-          out, workspace):
+          out, workspace, fmt="block128"):
     T, d = x.shape
     E = W_router.shape[1]
     f = W_down.shape[1]
@@ -124,11 +140,12 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
     _expect(x, "x", (T, d), 2, dev)
     _expect(W_router, "W_router", (d, E), 4, dev)
     _expect(b_router, "b_router", (E,), 4, dev)
+    (sg_shape, sg_bytes), (sd_shape, sd_bytes) = scale_shapes(d, f, E, fmt)
     _expect(W_gateup, "W_gateup", (E, d, 2 * f), 1, dev)
-    _expect(S_gateup, "S_gateup", (E, d // BLOCK, 2 * f // BLOCK), 4, dev)
+    _expect(S_gateup, "S_gateup", sg_shape, sg_bytes, dev)
     _expect(b_gateup, "b_gateup", (E, 2 * f), 2, dev)
     _expect(W_down, "W_down", (E, f, d), 1, dev)
-    _expect(S_down, "S_down", (E, f // BLOCK, d // BLOCK), 4, dev)
+    _expect(S_down, "S_down", sd_shape, sd_bytes, dev)
     _expect(b_down, "b_down", (E, d), 2, dev)
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
@@ -144,35 +161,38 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
 
 def forward(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
             out=None, workspace=None, path="auto", stream=None, routing="topk_softmax",
-            gate_bf16=False):
+            gate_bf16=False, fmt="block128"):
     """bf16 [T, d] output of the block; every argument is a device tensor laid
     out as ``include/moe.h`` states (bf16 tensors may be any 2-byte dtype,
-    e4m3 tensors any 1-byte dtype)."""
+    e4m3 and E8M0 tensors any 1-byte dtype).  ``fmt="mx"`` takes MXFP8
+    weights (E8M0 scales per 32 K rows) through ``moe_forward_mx``."""
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
-                             S_down, b_down, out, workspace)
-    _check(lib().moe_forward_ex(*args, flags_of(path, routing, gate_bf16),
-                                _stream(x.device, stream, ws, out)))
+                             S_down, b_down, out, workspace, fmt)
+    entry = lib().moe_forward_mx if fmt == "mx" else lib().moe_forward_ex
+    _check(entry(*args, flags_of(path, routing, gate_bf16), _stream(x.device, stream, ws, out)))
     return out
 
 
 def forward_stages(first, last, x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
                    S_down, b_down, out, workspace, path="auto", stream=None, routing="topk_softmax",
-                   gate_bf16=False):
+                   gate_bf16=False, fmt="block128"):
     """Stages ``first``..``last`` (names of ``STAGES`` or ints) of ``forward`` on a
     caller-kept workspace; all stages must run in order on that workspace."""
     first = STAGES.get(first, first)
     last = STAGES.get(last, last)
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
-                             S_down, b_down, out, workspace)
-    _check(lib().moe_forward_stages(*args, flags_of(path, routing, gate_bf16), int(first), int(last),
+                             S_down, b_down, out, workspace, fmt)
+    _check(lib().moe_forward_stages(*args, flags_of(path, routing, gate_bf16, fmt), int(first), int(last),
                                     _stream(x.device, stream, ws, out)))
     return out
 
 
 def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
-                  path="auto", stream=None, routing="topk_softmax", gate_bf16=False):
+                  path="auto", stream=None, routing="topk_softmax", gate_bf16=False,
+                  fmt="block128"):
     """``forward`` plus the intermediates (routing, permutation, quantised
-    activations and h, per-row expert outputs) as a dict of device tensors."""
+    activations and h, per-row expert outputs) as a dict of device tensors.
+    MX: xs / hs are E8M0 codes [T, d/32] / [T*k, f/32]."""
     T, d = x.shape
     E, f = W_router.shape[1], W_down.shape[1]
     R = T * k
@@ -184,14 +204,16 @@ def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down
                row_token=torch.empty(R, dtype=i32, device=dev),
                row_of=torch.empty((T, k), dtype=i32, device=dev),
                xq=torch.empty((T, d), dtype=u8, device=dev),
-               xs=torch.empty((T, d // BLOCK), dtype=f32, device=dev),
+               xs=(torch.empty((T, d // MX_BLOCK), dtype=u8, device=dev) if fmt == "mx"
+                   else torch.empty((T, d // BLOCK), dtype=f32, device=dev)),
                hq=torch.empty((R, f), dtype=u8, device=dev),
-               hs=torch.empty((R, f // BLOCK), dtype=f32, device=dev),
+               hs=(torch.empty((R, f // MX_BLOCK), dtype=u8, device=dev) if fmt == "mx"
+                   else torch.empty((R, f // BLOCK), dtype=f32, device=dev)),
                y=torch.empty((R, d), dtype=f32, device=dev))
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
-                             S_down, b_down, None, None)
+                             S_down, b_down, None, None, fmt)
     order = ["topk_idx", "topk_w", "offsets", "row_token", "row_of", "xq", "xs", "hq", "hs", "y"]
-    _check(lib().moe_forward_debug(*args, flags_of(path, routing, gate_bf16),
+    _check(lib().moe_forward_debug(*args, flags_of(path, routing, gate_bf16, fmt),
                                    _stream(dev, stream, ws, out, *dbg.values()),
                                    *[_ptr(dbg[n]) for n in order]))
     dbg["out"] = out
@@ -199,25 +221,29 @@ def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down
 
 
 def device_inputs(inp: dict, device="cuda"):
-    """Host arrays of ``inputs.make_inputs`` -> device tensors in the C-ABI dtypes."""
+    """Host arrays of ``inputs.make_inputs`` -> device tensors in the C-ABI dtypes
+    (the weight-format name under "fmt")."""
     import numpy as np
 
     def t(a, dtype):
         return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).to(device)
 
+    fmt = inp.get("format", "block128")
+    sdt = torch.uint8 if fmt == "mx" else torch.float32
     return dict(
         x=t(inp["x"], torch.bfloat16), W_router=t(inp["W_router"], torch.float32),
         b_router=t(inp["b_router"], torch.float32), k=int(inp["k"]),
-        W_gateup=t(inp["W_gateup"], torch.uint8), S_gateup=t(inp["S_gateup"], torch.float32),
+        W_gateup=t(inp["W_gateup"], torch.uint8), S_gateup=t(inp["S_gateup"], sdt),
         b_gateup=t(inp["b_gateup"], torch.bfloat16), W_down=t(inp["W_down"], torch.uint8),
-        S_down=t(inp["S_down"], torch.float32), b_down=t(inp["b_down"], torch.bfloat16))
+        S_down=t(inp["S_down"], sdt), b_down=t(inp["b_down"], torch.bfloat16), fmt=fmt)
 
 
 class MoeBlock:
     """Device-resident layer parameters plus a reusable workspace."""
 
     def __init__(self, params: dict):
-        self.p = {k: v for k, v in params.items() if k != "x"}
+        self.p = {k: v for k, v in params.items() if k not in ("x", "fmt")}
+        self.fmt = params.get("fmt", "block128")
         self._ws = None
 
     def workspace(self, T):
@@ -233,4 +259,4 @@ class MoeBlock:
         return forward(x, p["W_router"], p["b_router"], p["k"], p["W_gateup"], p["S_gateup"],
                        p["b_gateup"], p["W_down"], p["S_down"], p["b_down"], out=out,
                        workspace=self.workspace(x.shape[0]), path=path, stream=stream,
-                       routing=routing, gate_bf16=gate_bf16)
+                       routing=routing, gate_bf16=gate_bf16, fmt=self.fmt)

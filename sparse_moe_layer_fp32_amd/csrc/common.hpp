@@ -41,6 +41,23 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// ----------------------------------------------------------------------------- MX scales
+// E8M0 code (e + 127, at least 0) of the MX scale 2^e of a block whose largest
+// magnitude is amax >= 0: the smallest e with amax <= 448 * 2^e.  With
+// amax = m 2^p (1 <= m < 2) and 448 = 1.75 * 2^8, e = p - 8 when m <= 1.75
+// and p - 7 otherwise: integer work on the fp32 bits, exact for every input
+// (zero and subnormals give code 0, the smallest scale 2^-127).
+__device__ __forceinline__ uint32_t mx_code(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int c = static_cast<int>(b >> 23) - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return c > 0 ? static_cast<uint32_t>(c) : 0u;
+}
+
+// 1 / 2^e = 2^(127 - code) for an MX code from mx_code (code <= 248).
+__device__ __forceinline__ float mx_inv_scale(uint32_t code) {
+  return __uint_as_float((254u - code) << 23);
+}
+
 // ----------------------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -78,6 +95,16 @@ __device__ __forceinline__ void transpose4x4(uint32_t r0, uint32_t r1, uint32_t 
 // returns rows 4*(l/16)+i, i<4, of column l%16.
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The same with E8M0 block scales applied by the matrix core (32-deep K
+// blocks).  Lane l passes in byte 0 of sa / sb the scale of A row (B column)
+// l%16 for K block l/16, i.e. K 32(l/16)..+31.  Its data bytes 0-15 are
+// K 16(l/16)..+15 and bytes 16-31 are K 64 + 16(l/16)..+15, so K block b
+// sits in lane groups 2(b%2) and 2(b%2)+1 at bytes 16(b/2)..+15 (measured on
+// gfx950 with single nonzero bytes and distinct per-lane scales).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_mx(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // ----------------------------------------------------------------------------- misc

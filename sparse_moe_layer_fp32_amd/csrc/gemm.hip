@@ -65,17 +65,23 @@ namespace {
 // kernel states itself, and nothing drains the ring at a tile boundary.
 constexpr int DMA_WAVES = 8;
 constexpr int DMA_SS = DMA_WAVES * 256;              // side area: wave w's load lands at 256w
+constexpr int SIDE_AS = 0, SIDE_BIAS = 512, SIDE_BS = 1024;
+// MX side area: the E8M0 weight scales of the K block's four 32-deep groups,
+// group g (loaded by wave 4 + g) at SIDE_BS + MX_PITCH g.  A wave's load
+// always lands 256 bytes; the extra 16 put the groups on distinct LDS banks.
+constexpr int MX_PITCH = 272;
 // Tiles: 128 rows (prefill: waves of 64 rows) or 32 rows (decode, bound by
 // streaming the weights: waves of 16 rows), by 256 B columns (waves of 64)
 // or, for the decode down projection, 128 (waves of 32).  A stage is
 // A [BM][128], B [128][BNP] and the side area: 50 KB for prefill.
-template <int BM, int BNP>
+template <int BM, int BNP, bool MX>
 struct DmaShape {
   static constexpr int MB = BM / 32;                 // 16-row blocks per wave
   static constexpr int NB = BNP / 64;                // 16-column blocks per wave
   static constexpr int SA = BM * kBlock;
   static constexpr int SB = kBlock * BNP;
-  static constexpr int STAGE = SA + SB + DMA_SS;
+  static constexpr int SS = MX ? SIDE_BS + 4 * MX_PITCH : DMA_SS;
+  static constexpr int STAGE = SA + SB + SS;
   static constexpr int A_PER = BM >= 64 ? BM / 64 : 1;        // A chunks (1 KB) per loading wave
   static constexpr int A_WAVES = BM / 8 / A_PER;              // waves that load A
   static constexpr int B_PER = BNP / 64;                      // B chunks per wave
@@ -84,7 +90,6 @@ struct DmaShape {
   static_assert(BM == 32 || BM == 128, "row tile");
   static_assert(BNP == 128 || BNP == 256, "column tile");
 };
-constexpr int SIDE_AS = 0, SIDE_BIAS = 512, SIDE_BS = 1024;
 constexpr uint32_t kOob = 0x80000000u;               // buffer offset that reads as zero
 constexpr int kRsrcWord3 = 0x00020000;               // raw buffer, gfx9 family
 
@@ -96,9 +101,13 @@ typedef __attribute__((address_space(4))) int32_t const_i32;
 // measured on gfx950 with the SQ_LDS_BANK_CONFLICT counter, where the keys
 // r & 7 and (r >> 1) & 7 cost one extra cycle per read cycle.
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 2) & 1) | ((r & 3) << 1); }
-template <int SEGS>
+// With 16 segments per K row the key's bit 3 comes from the K-row bit that
+// tells the lane groups 0 and 1 apart in the fragment reads: bit 5 for K rows
+// 32g + 8r + j, bit 4 for the MX order 64(r/2) + 16g + 8(r%2) + j.
+template <int SEGS, bool MX = false>
 __device__ __forceinline__ int swz_b(int kr) {
-  return SEGS == 16 ? (kr & 7) | (((kr >> 5) & 1) << 3) : (kr & 7);
+  if (SEGS != 16) return kr & 7;
+  return MX ? (kr & 7) | (((kr >> 4) & 1) << 3) : (kr & 7) | (((kr >> 5) & 1) << 3);
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] | vmcnt[5:4] << 14)
@@ -127,7 +136,20 @@ __device__ __forceinline__ v4i dma_rsrc(const void* p, uint32_t bytes) {
 // s_waitcnt + s_barrier pairs order these loads against the reads; a wait
 // the compiler adds for its own memory operations only waits longer.  M0 is
 // restored.
+// PIN: the descriptor is uniform, but in some kernels the register allocator
+// copies it to VGPRs, which the scalar asm operand cannot take; readfirstlane
+// pins it to SGPRs there (elsewhere it would only perturb the allocation).
+template <bool PIN>
+__device__ __forceinline__ v4i sgpr4(v4i r) {
+  if constexpr (PIN) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+  }
+  return r;
+}
+template <bool PIN = false>
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
+  rsrc = sgpr4<PIN>(rsrc);
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
@@ -136,7 +158,9 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
       : "s"(lds), "v"(voff), "s"(rsrc)
       : "memory");
 }
+template <bool PIN = false>
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff) {
+  rsrc = sgpr4<PIN>(rsrc);
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
@@ -160,10 +184,11 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& g, int L) {
   return DmaTile{v[0], v[1], v[2], v[3]};
 }
 
-template <bool GATED, int BM, int BNP>
+template <bool GATED, int BM, int BNP, bool MX>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
-  using S = DmaShape<BM, BNP>;
+  using S = DmaShape<BM, BNP, MX>;
   static_assert(!GATED || BNP == 256, "gated tiles: 128 gate + 128 up columns");
+  static_assert(!MX || BM == 32, "MX decode tiles: one 16-row block per wave");
   constexpr int DMA_SA = S::SA, DMA_SB = S::SB, DMA_STAGE = S::STAGE;
   constexpr int MB = S::MB, NB = S::NB;             // 16x16 blocks per wave
   constexpr int WR = 16 * MB;                       // rows per wave
@@ -172,7 +197,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];  // the three ring stages
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE];
-  __shared__ float smax[GATED ? 4 * BM : 1];        // gated epilogue: row maxima per wave column
+  __shared__ float smax[(GATED && !MX) ? 4 * BM : 1];  // gated epilogue: row maxima per wave column
   __shared__ int32_t rtok[GATED ? 2 : 1][GATED ? DMA_WAVES * 64 : 1];  // row tokens, 2 tiles
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -191,11 +216,16 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   if (L0 >= hi) return;
 
   const v4i rA = dma_rsrc(g.A, g.A_bytes);
-  // side-area load of this wave: A row scales, bias, weight-block scales or zeros
+  // side-area load of this wave: A row scales, bias, weight scales or zeros.
+  // MX: waves 4-7 load the E8M0 weight scales of K groups 0-3 (rows 4 kb + g
+  // of [E][K/32][N]); block-scaled: wave 4 the two block scales of the K block.
+  const uint32_t bs_bytes = MX ? (uint32_t)g.E * (uint32_t)(K / 32) * (uint32_t)N
+                               : 4u * (uint32_t)g.E * nkb * nsb;
   const v4i rSide = wave < 2   ? dma_rsrc(g.As, g.As_bytes)
                     : wave < 4 ? dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N)
-                               : dma_rsrc(g.Bs, 4u * (uint32_t)g.E * nkb * nsb);
-  const int side_step = wave < 2 ? 4 : (wave == 4 ? 4 * nsb : 0);  // bytes per K block
+                               : dma_rsrc(g.Bs, bs_bytes);
+  const int side_step = wave < 2 ? 4 : wave < 4 ? 0 : MX ? 4 * N : (wave == 4 ? 4 * nsb : 0);
+  const uint32_t side_dst = (MX && wave >= 4) ? SIDE_BS + MX_PITCH * (wave - 4) : 256 * wave;
 
   // ---- load cursor: tile tl (index Ll), K block kbl; the next tile prefetched
   int Ll = L0, kbl = 0, rb = 0;
@@ -237,7 +267,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 #pragma unroll
     for (int q = 0; q < S::B_PER; ++q) {
       const int kr = (1024 / BNP) * (S::B_PER * wave + q) + lane / S::SEGS;
-      const int s = (lane % S::SEGS) ^ swz_b<S::SEGS>(kr);
+      const int s = (lane % S::SEGS) ^ swz_b<S::SEGS, MX>(kr);
       const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
       boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
     }
@@ -248,6 +278,11 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     } else if (wave < 4) {  // bias: 128 columns (bf16 pairs) per wave
       const int c = (GATED ? (wave == 2 ? n0 : g.f + n0) : n0 + 128 * (wave - 2)) + 2 * lane;
       if (c < N) soff = 2u * ((uint32_t)t.e * (uint32_t)N + (uint32_t)c);
+    } else if constexpr (MX) {  // wave 4 + q: E8M0 scales of K group q, tile columns 4 lane..
+      const int c = 4 * lane;
+      const int gc = GATED ? (c < 128 ? n0 + c : g.f + n0 + c - 128) : n0 + c;
+      if (c < BNP && gc < N)
+        soff = ((uint32_t)t.e * (uint32_t)(K / 32) + (uint32_t)(wave - 4)) * (uint32_t)N + (uint32_t)gc;
     } else if (wave == 4 && lane < 2) {  // the two weight-block scales of the K block
       const int sb = GATED ? (lane == 0 ? n0 : g.f + n0) / kBlock : n0 / kBlock + lane;
       if (sb < nsb) soff = 4u * ((uint32_t)t.e * (uint32_t)nkb * (uint32_t)nsb + (uint32_t)sb);
@@ -263,11 +298,11 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     if (S::A_WAVES == DMA_WAVES || wave < S::A_WAVES)
 #pragma unroll
       for (int q = 0; q < S::A_PER; ++q)
-        dma16(rA, sbase + (S::A_PER * wave + q) * 1024, aoff[q] + ka);
+        dma16<MX>(rA, sbase + (S::A_PER * wave + q) * 1024, aoff[q] + ka);
 #pragma unroll
     for (int q = 0; q < S::B_PER; ++q)
-      dma16(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
-    dma4(rSide, sbase + DMA_SA + DMA_SB + 256 * wave, soff + (uint32_t)(kbl * side_step));
+      dma16<MX>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
+    dma4<MX>(rSide, sbase + DMA_SA + DMA_SB + side_dst, soff + (uint32_t)(kbl * side_step));
     ++kbl;
   };
   // After a tile's last K block has been issued the cursor moves to its next
@@ -295,13 +330,16 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   };
 
   // ---- per-lane LDS read offsets (stage-relative)
-  // activations: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1 (swizzled)
+  // activations: row 64*wm + 16*mb + l16, 32 bytes = segments 2gq, 2gq+1
+  // (MX K order: gq, gq + 4), swizzled
   const int a_row = (wm * WR + l16) * kBlock;
-  const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
-  const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
-  // weights: transposing reads of K rows 32gq + 8r + l16/2, half l16 & 1 of a segment
-  const int b_row = (32 * gq + (l16 >> 1)) * BNP + 8 * (l16 & 1);
-  const int b_swz = swz_b<S::SEGS>(32 * gq + (l16 >> 1));  // the same for the 4 reads
+  const int a_pos0 = 16 * ((MX ? gq : 2 * gq) ^ swz_a(l16));
+  const int a_pos1 = 16 * ((MX ? gq + 4 : 2 * gq + 1) ^ swz_a(l16));
+  // weights: transposing reads r = 0..3 of K rows b_kr(r) + b_kg, half l16 & 1
+  // of a segment: K rows 8r + 32gq + l16/2 (MX: 64(r/2) + 8(r%2) + 16gq + l16/2)
+  const int b_kg = (MX ? 16 : 32) * gq + (l16 >> 1);
+  const int b_row = b_kg * BNP + 8 * (l16 & 1);
+  const int b_swz = swz_b<S::SEGS, MX>(b_kg);  // the same for the 4 reads
   // tile segment of column block nb: gated 2wn + nb (gate) and 8 + 2wn + nb - 2 (up),
   // plain NB wn + nb; stored at segment ^ b_swz
   const int b_base = 16 * ((GATED ? 2 * wn : NB * wn) ^ b_swz);
@@ -318,7 +356,46 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // ---- compute side: tile tc, K block kbc; the next tile prefetched
   DmaTile tc = tl, tcn = tln;
   int Lcn = Lln, kbc = 0;
-  float acc[MB][NB][4];  // scalars, not vectors: no register-quad constraint in the loop
+  // block-scaled: promoted sums, scalars (no register-quad constraint in the loop);
+  // MX: the matrix cores accumulate in macc, copied to acc for the epilogue
+  float acc[MB][NB][4];
+  v4f macc[MX ? MB : 1][MX ? NB : 1];
+
+  auto compute_mx = [&](const uint8_t* base) {
+    const uint8_t* sA = base;
+    const uint8_t* sB = base + DMA_SA;
+    if (kbc == 0) {  // accumulators start from the bias
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint2 w = *reinterpret_cast<const uint2*>(base + bias_pos(nb));
+        const v4f bv = v4f{bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
+                           bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) macc[mb][nb] = bv;
+      }
+    }
+    // E8M0 scales: byte gq (K group) of row 16 wm + l16's dword; weight column
+    // 16 seg + l16 of K group gq
+    const int xsc = static_cast<int>(*reinterpret_cast<const uint32_t*>(base + s_pos) >> (8 * gq));
+    const uint8_t* wsc = base + DMA_SA + DMA_SB + SIDE_BS + MX_PITCH * gq + l16;
+    const v4i lo4 = *reinterpret_cast<const v4i*>(sA + a_row + a_pos0);
+    const v4i hi4 = *reinterpret_cast<const v4i*>(sA + a_row + a_pos1);
+    const v8i xf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      v8i wf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(sB + b_row + (64 * (r >> 1) + 8 * (r & 1)) * BNP +
+                                                     (b_base ^ (16 * b_seg(nb)))));
+        wf[2 * r] = t[0];
+        wf[2 * r + 1] = t[1];
+      }
+      const int ws = wsc[16 * ((GATED ? 2 * wn : NB * wn) + b_seg(nb))];
+      macc[0][nb] = mfma_fp8_16x16x128_mx(wf, xf, macc[0][nb], ws, xsc);
+    }
+  };
 
   auto compute = [&](const uint8_t* base) {
     const uint8_t* sA = base;
@@ -377,6 +454,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // columns past N go to offsets past the buffers, which drops them).
   auto epilogue = [&](const DmaTile& t) {
     const int n0 = t.nt * (GATED ? kBlock : BNP);
+    if constexpr (MX) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][nb][i] = macc[mb][nb][i];
+    }
     if constexpr (GATED) {
       // h = silu(gate) * up on registers: h column 32wn + 16j + 4gq + i
       float h[MB][2][4];
@@ -398,40 +483,64 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
       }
-      // row maxima over the four wave columns through LDS.  The previous
-      // tile's readers are past at least one ring barrier; a bare s_barrier
-      // (no memory fence) leaves the next tile's stage loads in flight.
-      if (gq == 0)
+      if constexpr (MX) {
+        // the wave's 32 h columns of a row are one MX block: no exchange
+        const __amdgpu_buffer_rsrc_t rH =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rHs =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * WR + 16 * mb + l16] = pmax[mb];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      const __amdgpu_buffer_rsrc_t rH =
-          __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rHs =
-          __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * WR + 16 * mb + l16;
+          const uint32_t code = mx_code(pmax[mb]);
+          const float inv = mx_inv_scale(code);
+          const bool ok = r < t.valid;
+          const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = wm * WR + 16 * mb + l16;
-        const float amax =
-            fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
-        const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-        const float inv = 1.0f / s;
-        const bool ok = r < t.valid;
-        const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float q[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] * inv, -kFp8Max), kFp8Max);
-          __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
-                                                ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                f32x4_to_e4m3(h[mb][j][0] * inv, h[mb][j][1] * inv, h[mb][j][2] * inv, h[mb][j][3] * inv),
+                rH, ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          const uint32_t so = (uint32_t)(t.row0 + r) * (uint32_t)(g.f / 32) + 4 * t.nt + wn;
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rHs,
+                                               (ok && gq == 0) ? (int)so : (int)kOob, 0, 0);
         }
-        const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
-                                              (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+      } else {
+        // row maxima over the four wave columns through LDS.  The previous
+        // tile's readers are past at least one ring barrier; a bare s_barrier
+        // (no memory fence) leaves the next tile's stage loads in flight.
+        if (gq == 0)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) smax[wn * BM + wm * WR + 16 * mb + l16] = pmax[mb];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const __amdgpu_buffer_rsrc_t rH =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rHs =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * WR + 16 * mb + l16;
+          const float amax =
+              fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
+          const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+          const float inv = 1.0f / s;
+          const bool ok = r < t.valid;
+          const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float q[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] * inv, -kFp8Max), kFp8Max);
+            __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
+                                                  ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          }
+          const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
+                                                (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+        }
       }
     } else {
       const __amdgpu_buffer_rsrc_t rY =
@@ -484,7 +593,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   auto step = [&](const uint8_t* cur, uint8_t* next2) -> bool {
     wait_stage(pend);
     issue(next2);
-    compute(cur);
+    if constexpr (MX) compute_mx(cur);
+    else compute(cur);
     pend = advance();
     if (++kbc < nkb) return true;
     epilogue(tc);
@@ -541,17 +651,18 @@ constexpr int W_SIDE_BIAS = 1024, W_SIDE_BS = 1536;
 constexpr int W_AQ = W_SA / 1024 / DMA_WAVES;       // A chunks (1 KB) per wave: 3
 constexpr int W_BQ = W_SB / 1024 / DMA_WAVES;       // B chunks per wave: 4
 
-template <bool GATED>
+template <bool GATED, bool MX>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(GemmArgs g) {
   constexpr int MB = W_HALF / 16, NB = 4;            // 16 x 16 blocks per wave: 6 x 4
   constexpr int RT = GATED ? 1 : 0;                  // row-token loads per A-cursor tile move
   constexpr int ST = GATED ? MB * 3 : MB * NB;       // epilogue stores per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t sa0[W_ASTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa1[W_ASTAGE];
+  constexpr int ASTAGE = MX ? W_SA + W_SIDE_BS + 4 * MX_PITCH : W_ASTAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[ASTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[W_SB];
   __shared__ __attribute__((aligned(1024))) uint8_t sb1[W_SB];
   __shared__ __attribute__((aligned(1024))) uint8_t sb2[W_SB];
-  __shared__ float smax[GATED ? 4 * WM_ROWS : 1];    // row maxima per wave column
+  __shared__ float smax[(GATED && !MX) ? 4 * WM_ROWS : 1];  // row maxima per wave column
   __shared__ int32_t rtok[GATED ? 2 : 1][GATED ? DMA_WAVES * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -569,17 +680,23 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   if (L0 >= hi) return;
 
   const v4i rA = dma_rsrc(g.A, g.A_bytes);
-  const v4i rSide = wave < 4   ? dma_rsrc(g.As, g.As_bytes)
-                    : wave < 6 ? dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N)
-                               : dma_rsrc(g.Bs, 4u * (uint32_t)g.E * nkb * nsb);
-  const int side_step = wave < 4 ? 4 : (wave == 6 ? 4 * nsb : 0);
+  // side loads: waves 0-3 the A row scales; block-scaled: waves 4, 5 the bias,
+  // wave 6 the two weight-block scales; MX: waves 4-7 the E8M0 weight scales
+  // of K groups 0-3 and waves 4, 5 the bias with a second load
+  const v4i rBias = dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N);
+  const uint32_t bs_bytes = MX ? (uint32_t)g.E * (uint32_t)(K / 32) * (uint32_t)N
+                               : 4u * (uint32_t)g.E * nkb * nsb;
+  const v4i rSide = wave < 4 ? dma_rsrc(g.As, g.As_bytes)
+                    : (wave < 6 && !MX) ? rBias : dma_rsrc(g.Bs, bs_bytes);
+  const int side_step = wave < 4 ? 4 : MX ? 4 * N : (wave == 6 ? 4 * nsb : 0);
+  const uint32_t side_dst = (MX && wave >= 4) ? W_SIDE_BS + MX_PITCH * (wave - 4) : 256 * wave;
 
   // ---- A cursor (activations + side area, one K block ahead of compute)
   int La = L0, kba = 0, rb = 0;
   int Lan = La + nslots;
   DmaTile ta = dma_tile(g, La), tan = ta;
   if (Lan < hi) tan = dma_tile(g, Lan);
-  uint32_t aoff[W_AQ], soff;
+  uint32_t aoff[W_AQ], soff, soff2 = kOob;
   // ---- B cursor (weights, two K blocks ahead of compute)
   int Lb = L0, kbb = 0;
   DmaTile tb = ta;
@@ -610,9 +727,19 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       const int r = W_HALF * (i >> 7) + 16 * mb + ((i >> 3) & 15);
       if (mb < MB && r < t.valid)
         soff = (uint32_t)(GATED ? rtok[buf][r] : t.row0 + r) * (uint32_t)nkb * 4u;
-    } else if (wave < 6) {  // bias: 128 tile columns (bf16 pairs) per wave
-      const int c = (GATED ? (wave == 4 ? n0 : g.f + n0) : n0 + 128 * (wave - 4)) + 2 * lane;
-      if (c < N) soff = 2u * ((uint32_t)t.e * (uint32_t)N + (uint32_t)c);
+    } else if (MX || wave < 6) {
+      if (wave < 6) {  // bias: 128 tile columns (bf16 pairs) per wave
+        const int c = (GATED ? (wave == 4 ? n0 : g.f + n0) : n0 + 128 * (wave - 4)) + 2 * lane;
+        uint32_t& o = MX ? soff2 : soff;
+        o = kOob;
+        if (c < N) o = 2u * ((uint32_t)t.e * (uint32_t)N + (uint32_t)c);
+      }
+      if constexpr (MX) {  // wave 4 + q: E8M0 scales of K group q, tile columns 4 lane..
+        const int c = 4 * lane;
+        const int gc = GATED ? (c < 128 ? n0 + c : g.f + n0 + c - 128) : n0 + c;
+        if (gc < N)
+          soff = ((uint32_t)t.e * (uint32_t)(K / 32) + (uint32_t)(wave - 4)) * (uint32_t)N + (uint32_t)gc;
+      }
     } else if (wave == 6 && lane < 2) {
       const int sb = GATED ? (lane == 0 ? n0 : g.f + n0) / kBlock : n0 / kBlock + lane;
       if (sb < nsb) soff = 4u * ((uint32_t)t.e * (uint32_t)nkb * (uint32_t)nsb + (uint32_t)sb);
@@ -624,7 +751,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 #pragma unroll
     for (int q = 0; q < W_BQ; ++q) {  // chunk W_BQ wave + q: K rows 4 chunk + lane / 16
       const int kr = 4 * (W_BQ * wave + q) + (lane >> 4);
-      const int s = (lane & 15) ^ swz_b<16>(kr);
+      const int s = (lane & 15) ^ swz_b<16, MX>(kr);
       const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
       boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
     }
@@ -638,19 +765,27 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   // last tile (the offsets then point past the buffers and the loads land as
   // zeros in a stage no one reads), so the in-flight count is the same on
   // every path.
+  auto a_load = [&](uint32_t sbase, int q) {
+    dma16(rA, sbase + (W_AQ * wave + q) * 1024, aoff[q] + (uint32_t)kba * kBlock);
+  };
+  auto side_load = [&](uint32_t sbase) {
+    dma4(rSide, sbase + W_SA + side_dst, soff + (uint32_t)(kba * side_step));
+    if (MX && (wave == 4 || wave == 5)) dma4(rBias, sbase + W_SA + W_SIDE_BIAS + 256 * (wave - 4), soff2);
+  };
+  auto b_load = [&](uint32_t sbase, int q) {
+    dma16(rB, sbase + (W_BQ * wave + q) * 1024, boff[q] + (uint32_t)kbb * kBlock * (uint32_t)N);
+  };
   auto issue_a = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
-    const uint32_t ka = (uint32_t)kba * kBlock;
 #pragma unroll
-    for (int q = 0; q < W_AQ; ++q) dma16(rA, sbase + (W_AQ * wave + q) * 1024, aoff[q] + ka);
-    dma4(rSide, sbase + W_SA + 256 * wave, soff + (uint32_t)(kba * side_step));
+    for (int q = 0; q < W_AQ; ++q) a_load(sbase, q);
+    side_load(sbase);
     ++kba;
   };
   auto issue_b = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
-    const uint32_t kb = (uint32_t)kbb * kBlock * (uint32_t)N;
 #pragma unroll
-    for (int q = 0; q < W_BQ; ++q) dma16(rB, sbase + (W_BQ * wave + q) * 1024, boff[q] + kb);
+    for (int q = 0; q < W_BQ; ++q) b_load(sbase, q);
     ++kbb;
   };
   // Cursor moves after a tile's last K block has been issued.
@@ -685,7 +820,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     } else {
 #pragma unroll
       for (int q = 0; q < W_AQ; ++q) aoff[q] = kOob;
-      soff = kOob;
+      soff = soff2 = kOob;
     }
     // the previous readers of rtok[rb ^ 1] are past a ring barrier
     rt_load(tan, Lan < hi, rb ^ 1);
@@ -693,27 +828,72 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   };
 
   // ---- per-lane LDS read offsets
+  // (the MX K order reads segments gq, gq + 4 and K rows 64(r/2) + 8(r%2) + 16gq + l16/2)
   const int a_row = (wm * W_HALF + l16) * kBlock;
-  const int a_pos0 = 16 * ((2 * gq) ^ swz_a(l16));
-  const int a_pos1 = 16 * ((2 * gq + 1) ^ swz_a(l16));
-  const int b_row = (32 * gq + (l16 >> 1)) * WN_COLS + 8 * (l16 & 1);
-  const int b_swz = swz_b<16>(32 * gq + (l16 >> 1));
+  const int a_pos0 = 16 * ((MX ? gq : 2 * gq) ^ swz_a(l16));
+  const int a_pos1 = 16 * ((MX ? gq + 4 : 2 * gq + 1) ^ swz_a(l16));
+  const int b_kg = (MX ? 16 : 32) * gq + (l16 >> 1);
+  const int b_row = b_kg * WN_COLS + 8 * (l16 & 1);
+  const int b_swz = swz_b<16, MX>(b_kg);
   // tile B segment of block nb: gated gate 2wn + nb, up 8 + 2wn + nb - 2; plain 4wn + nb
-  auto b_off = [&](int nb) -> int {
-    const int seg = GATED ? (nb < 2 ? 2 * wn + nb : 8 + 2 * wn + nb - 2) : 4 * wn + nb;
-    return b_row + 16 * (seg ^ b_swz);
+  auto b_tseg = [&](int nb) -> int {
+    return GATED ? (nb < 2 ? 2 * wn + nb : 8 + 2 * wn + nb - 2) : 4 * wn + nb;
   };
+  auto b_off = [&](int nb) -> int { return b_row + 16 * (b_tseg(nb) ^ b_swz); };
   const int s_pos = W_SA + (wm * 128 + 8 * l16) * 4;
 
   DmaTile tc = ta;
   int Lc = L0, kbc = 0;
+  // block-scaled: promoted sums; MX: the matrix cores accumulate in macc
+  // (copied to acc for the epilogue)
   float acc[MB][NB][4];
+  v4f macc[MX ? MB : 1][MX ? NB : 1];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (MX) macc[mb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
+    }
+
+  auto compute_mx = [&](const uint8_t* abase, const uint8_t* bbase) {
+    if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
+    // E8M0 scales: byte gq (K group) of the dwords of rows 96 wm + 16 mb + l16,
+    // stored at dword 128 wm + 8 l16 + mb; weight column 16 seg + l16 of group gq
+    const v4u sl = *reinterpret_cast<const v4u*>(abase + s_pos);
+    const uint2 sh = *reinterpret_cast<const uint2*>(abase + s_pos + 16);
+    int xsc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      xsc[mb] = static_cast<int>((mb < 4 ? sl[mb] : (mb == 4 ? sh.x : sh.y)) >> (8 * gq));
+    const uint8_t* wsc = abase + W_SA + W_SIDE_BS + MX_PITCH * gq + l16;
+    int wsv[NB];
+    v8i wf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      wsv[nb] = wsc[16 * b_tseg(nb)];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i*)(bbase + b_off(nb) +
+                                                     (64 * (r >> 1) + 8 * (r & 1)) * WN_COLS));
+        wf[nb][2 * r] = t[0];
+        wf[nb][2 * r + 1] = t[1];
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
+      const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
+      const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
+      const v8i xf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        macc[mb][nb] = mfma_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
+      }
+    }
+  };
 
   auto compute = [&](const uint8_t* abase, const uint8_t* bbase) {
     if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
@@ -761,6 +941,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   auto epilogue = [&](const DmaTile& t, const uint8_t* abase) {
     const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
     const uint8_t* sbias = abase + W_SA + W_SIDE_BIAS;
+    if constexpr (MX) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][nb][i] = macc[mb][nb][i];
+    }
     if constexpr (GATED) {
       float bg[2][4], bu[2][4];
 #pragma unroll
@@ -791,40 +979,65 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
       }
-      // row maxima over the four wave columns through LDS.  The previous
-      // tile's readers are past at least one ring barrier; a bare s_barrier
-      // (no memory fence) leaves the stage loads in flight.
-      if (gq == 0)
+      if constexpr (MX) {
+        // the wave's 32 h columns of a row are one MX block: no exchange, no barrier
+        const __amdgpu_buffer_rsrc_t rH =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rHs =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) smax[wn * WM_ROWS + wm * W_HALF + 16 * mb + l16] = pmax[mb];
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      const __amdgpu_buffer_rsrc_t rH =
-          __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rHs =
-          __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * W_HALF + 16 * mb + l16;
+          const uint32_t code = mx_code(pmax[mb]);
+          const float inv = mx_inv_scale(code);
+          const bool ok = r < t.valid;
+          const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int r = wm * W_HALF + 16 * mb + l16;
-        const float amax = fmaxf(fmaxf(smax[r], smax[WM_ROWS + r]),
-                                 fmaxf(smax[2 * WM_ROWS + r], smax[3 * WM_ROWS + r]));
-        const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
-        const float inv = 1.0f / s;
-        const bool ok = r < t.valid;
-        const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          float q[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[mb][j][i] * inv, -kFp8Max), kFp8Max);
-          __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
-                                                ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                f32x4_to_e4m3(acc[mb][j][0] * inv, acc[mb][j][1] * inv, acc[mb][j][2] * inv,
+                              acc[mb][j][3] * inv),
+                rH, ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          const uint32_t so = (uint32_t)(t.row0 + r) * (uint32_t)(g.f / 32) + 4 * t.nt + wn;
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), rHs,
+                                               (ok && gq == 0) ? (int)so : (int)kOob, 0, 0);
         }
-        const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
-                                              (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+      } else {
+        // row maxima over the four wave columns through LDS.  The previous
+        // tile's readers are past at least one ring barrier; a bare s_barrier
+        // (no memory fence) leaves the stage loads in flight.
+        if (gq == 0)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) smax[wn * WM_ROWS + wm * W_HALF + 16 * mb + l16] = pmax[mb];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the smax writes are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        const __amdgpu_buffer_rsrc_t rH =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hq, (short)0, g.out_bytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rHs =
+            __builtin_amdgcn_make_buffer_rsrc(g.Hs, (short)0, g.out2_bytes, kRsrcWord3);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * W_HALF + 16 * mb + l16;
+          const float amax = fmaxf(fmaxf(smax[r], smax[WM_ROWS + r]),
+                                   fmaxf(smax[2 * WM_ROWS + r], smax[3 * WM_ROWS + r]));
+          const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+          const float inv = 1.0f / s;
+          const bool ok = r < t.valid;
+          const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            float q[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[mb][j][i] * inv, -kFp8Max), kFp8Max);
+            __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
+                                                  ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
+          }
+          const uint32_t so = 4u * ((uint32_t)(t.row0 + r) * (uint32_t)(g.f / kBlock) + t.nt);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, s), rHs,
+                                                (ok && wn == 0 && gq == 0) ? (int)so : (int)kOob, 0, 0);
+        }
       }
     } else {
       const __amdgpu_buffer_rsrc_t rY =
@@ -852,9 +1065,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (MX) {
+          macc[mb][nb] = v4f{0.f, 0.f, 0.f, 0.f};
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
+          for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
+        }
+      }
   };
 
   // Ring wait: this wave's loads of the A stage about to be read (and, older,
@@ -894,7 +1112,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   auto step = [&](const uint8_t* ca, uint8_t* na, const uint8_t* cb, uint8_t* nb2) -> bool {
     wait_stage(pend);
     issue_a(na);
-    compute(ca, cb);
+    if constexpr (MX) compute_mx(ca, cb);
+    else compute(ca, cb);
     issue_b(nb2);
     pend = advance_a();
     advance_b();
@@ -932,25 +1151,37 @@ int grid_persistent(int max_tiles) {
 
 }  // namespace
 
-hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
+hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+                             hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   static_assert(kGatedPrefill.bm == WM_ROWS && kGatedPrefill.bnp == WN_COLS, "wide tile");
-  if (decode)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, kGatedDecode.bm, kGatedDecode.bnp>), grid, block, 0, stream, a);
+  constexpr int DBM = kGatedDecode.bm, DBN = kGatedDecode.bnp;
+  if (decode && mx)
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, DBM, DBN, true>), grid, block, 0, stream, a);
+  else if (decode)
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, DBM, DBN, false>), grid, block, 0, stream, a);
+  else if (mx)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<true, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<true>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<true, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream) {
+hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+                             hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   static_assert(kPlainPrefill.bm == WM_ROWS && kPlainPrefill.bnp == WN_COLS, "wide tile");
-  if (decode)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, kPlainDecode.bm, kPlainDecode.bnp>), grid, block, 0, stream, a);
+  constexpr int DBM = kPlainDecode.bm, DBN = kPlainDecode.bnp;
+  if (decode && mx)
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, DBM, DBN, true>), grid, block, 0, stream, a);
+  else if (decode)
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, DBM, DBN, false>), grid, block, 0, stream, a);
+  else if (mx)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<false, true>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL(grouped_gemm_wide_kernel<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -24,12 +24,14 @@ constexpr GemmShape kGatedDecode{32, 256};
 constexpr GemmShape kPlainPrefill{192, 256};
 constexpr GemmShape kPlainDecode{32, 128};
 
+// Scales: block-scaled fp32 (As [rows, K/128], Bs [E, K/128, N/128], Hs
+// [R, f/128]) or MX E8M0 bytes (As [rows, K/32], Bs [E, K/32, N], Hs [R, f/32]).
 struct GemmArgs {
   const uint8_t* A;            // e4m3 activations: x codes [T,K] (gated) or h codes [R,K] (plain)
-  const float* As;             // their scales [rows, K/128]
+  const void* As;              // their scales
   const int32_t* row_token;    // gated: token of each permuted row
   const uint8_t* B;            // e4m3 weights [E, K, N]
-  const float* Bs;             // block scales [E, K/128, N/128]
+  const void* Bs;              // weight scales
   const uint16_t* bias;        // bf16 [E, N]
   const int32_t* counts;       // rows per expert [E]
   const int32_t* offsets;      // first row per expert [E+1]
@@ -39,8 +41,8 @@ struct GemmArgs {
   int A_bytes, As_bytes;       // sizes of A and As (buffer bounds; reads past them give 0)
   int rows_bytes;              // 4 * R: size of row_token
   int out_bytes, out2_bytes;   // gated: sizes of Hq and Hs; plain: size of Y
-  uint8_t* Hq;                 // gated outputs: h codes [R, f] and scales [R, f/128]
-  float* Hs;
+  uint8_t* Hq;                 // gated outputs: h codes [R, f] and their scales
+  void* Hs;
   float* Y;                    // plain output [R, N]
 };
 
@@ -62,9 +64,11 @@ struct SmallRoute {
 constexpr int kGateSoftmaxAll = 1;
 constexpr int kGateBf16 = 2;
 
+// mx: x is quantised per 32 columns with E8M0 scales (xs bytes [T, d/32]);
+// otherwise per 128 columns with fp32 scales (xs floats [T, d/128]).
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
-                         int k, int gate_mode, float* partial, int32_t* topk_idx, float* topk_w,
-                         int32_t* hist, uint8_t* xq, float* xs, const SmallRoute* sr,
+                         int k, int gate_mode, bool mx, float* partial, int32_t* topk_idx,
+                         float* topk_w, int32_t* hist, uint8_t* xq, void* xs, const SmallRoute* sr,
                          hipStream_t stream);
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
@@ -83,8 +87,11 @@ hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base,
 hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
                           int k, uint16_t* out, hipStream_t stream);
 
-// max_tiles bounds the tile count so the grid covers every tile.
-hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream);
-hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int max_tiles, hipStream_t stream);
+// max_tiles bounds the tile count so the grid covers every tile; mx selects
+// the MXFP8 kernels (E8M0 scales applied by the matrix cores).
+hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+                             hipStream_t stream);
+hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+                             hipStream_t stream);
 
 }  // namespace moe

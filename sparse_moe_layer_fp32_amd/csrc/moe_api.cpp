@@ -103,10 +103,11 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                               int32_t first_stage, int32_t last_stage, void* stream_) {
   const moe_status sz = check_sizes(T, d, f, E, k);
   if (sz != MOE_OK) return sz;
-  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16)) != 0u ||
+  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX)) != 0u ||
       (flags & MOE_PATH_MASK) == MOE_PATH_MASK)
     return MOE_ERR_FLAGS;
   const uint32_t path = flags & MOE_PATH_MASK;
+  const bool mx = (flags & MOE_FORMAT_MX) != 0u;
   const int gate_mode = ((flags & MOE_ROUTE_SOFTMAX_ALL) ? moe::kGateSoftmaxAll : 0) |
                         ((flags & MOE_GATE_BF16) ? moe::kGateBf16 : 0);
   if (first_stage < 0 || last_stage >= MOE_NUM_STAGES || first_stage > last_stage)
@@ -138,9 +139,9 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   int32_t* row_of = reinterpret_cast<int32_t*>(at(l.row_of));
   int32_t* row_token = reinterpret_cast<int32_t*>(at(l.row_token));
   uint8_t* xq = at(l.xq);
-  float* xs = reinterpret_cast<float*>(at(l.xs));
+  void* xs = at(l.xs);  // fp32 [T, d/128] or E8M0 [T, d/32]: the same bytes
   uint8_t* hq = at(l.hq);
-  float* hs = reinterpret_cast<float*>(at(l.hs));
+  void* hs = at(l.hs);
   float* y = reinterpret_cast<float*>(at(l.y));
 
   const int R = T * k;
@@ -164,7 +165,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         const moe::SmallRoute sr{counts,  offsets, tile_off0, tile_off1, tiles0, tiles1, row_of,
                                  row_token, gs.bm,   nt_g,      max_g,     ps.bm,  nt_p,   max_p};
         err = moe::launch_router(static_cast<const uint16_t*>(x), W_router, b_router, T, d, E, k,
-                                 gate_mode, partial, topk_idx, topk_w, hist, xq, xs,
+                                 gate_mode, mx, partial, topk_idx, topk_w, hist, xq, xs,
                                  small ? &sr : nullptr, stream);
         break;
       }
@@ -207,7 +208,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.Hs = hs;
         g.A_bytes = (int)((int64_t)T * d);
         g.As_bytes = (int)(4 * (int64_t)T * (d / moe::kBlock));
-        err = moe::launch_gemm_gated(g, decode, max_g, stream);
+        err = moe::launch_gemm_gated(g, decode, mx, max_g, stream);
         break;
       }
       case MOE_STAGE_DOWN: {
@@ -231,7 +232,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.Y = y;
         p.A_bytes = (int)((int64_t)R * f);
         p.As_bytes = (int)(4 * (int64_t)R * (f / moe::kBlock));
-        err = moe::launch_gemm_plain(p, decode, max_p, stream);
+        err = moe::launch_gemm_plain(p, decode, mx, max_p, stream);
         break;
       }
       case MOE_STAGE_COMBINE:
@@ -260,6 +261,18 @@ moe_status moe_forward(const void* x, const float* W_router, const float* b_rout
                        size_t workspace_bytes, void* stream) {
   return moe_forward_ex(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
                         b_down, out, T, d, f, E, workspace, workspace_bytes, MOE_PATH_AUTO, stream);
+}
+
+moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_router, int32_t k,
+                          const uint8_t* W_gateup, const uint8_t* X_gateup, const void* b_gateup,
+                          const uint8_t* W_down, const uint8_t* X_down, const void* b_down,
+                          void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
+                          size_t workspace_bytes, uint32_t flags, void* stream) {
+  return moe_forward_stages(x, W_router, b_router, k, W_gateup,
+                            reinterpret_cast<const float*>(X_gateup), b_gateup, W_down,
+                            reinterpret_cast<const float*>(X_down), b_down, out, T, d, f, E,
+                            workspace, workspace_bytes, flags | MOE_FORMAT_MX, 0,
+                            MOE_NUM_STAGES - 1, stream);
 }
 
 moe_status moe_forward_debug(const void* x, const float* W_router, const float* b_router,

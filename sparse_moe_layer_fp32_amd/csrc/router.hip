@@ -1,12 +1,13 @@
-// Router + top-k + softmax, fused with the per-token 1x128 e4m3 activation
-// quantisation (both read x once).
+// Router + top-k + softmax, fused with the per-token e4m3 activation
+// quantisation, 1x128 fp32-scaled or 1x32 MX (both read x once).
 //
 // "GPT-OSS on day 0", section "MoE": the routing kernel scores the experts,
 // keeps the top-k and takes the softmax over the selected experts only (the
 // max-subtracted form of section "Sink attention").  Section "GPT-OSS on
 // Hopper" fixes FP8 with 128x128 block scaling; activations are quantised per
 // token per 128 columns so that every 128-deep K block of the expert GEMMs has
-// one activation scale per row.
+// one activation scale per row.  Its section "Quantization" names MXFP8
+// microscaling for Blackwell: there every 32 columns get an E8M0 scale.
 //
 // Design: every wave owns 16 tokens.  The logits run on the bf16 matrix
 // cores with each fp32 router weight split into three exact bf16 parts, so
@@ -151,15 +152,15 @@ constexpr int w_fill(int nbw) { return nbw <= 4 ? kBlock : nbw <= 8 ? kBlock / 2
 // then across groups).  The workgroup converts the W_router rows of its K
 // range into three K-contiguous bf16 planes in LDS (the MFMA's B operand);
 // the x fragments (A operand, 8 consecutive bf16 per lane) come straight from
-// memory.  The same registers feed the per-token 1x128 e4m3 quantisation of x.
+// memory.  The same registers feed the per-token e4m3 quantisation of x.
 // One split: top-k + softmax + tile histogram in place; several: partial
 // logits [split][T][E] for router_finish_kernel.
 template <int NBW>
 __global__ __launch_bounds__(256) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ br,
-    int T, int d, int E, int k, int gate_mode, int groups_per_split, float* __restrict__ partial,
-    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ hist,
-    uint8_t* __restrict__ xq, float* __restrict__ xs) {
+    int T, int d, int E, int k, int gate_mode, int mx, int groups_per_split,
+    float* __restrict__ partial, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ hist, uint8_t* __restrict__ xq, void* __restrict__ xs) {
   constexpr int EP = NBW * 16;                   // experts padded to 16
   constexpr int KC = w_fill(NBW);                // W rows per fill
   constexpr int PITCH = 2 * KC + 16;             // bytes per expert row of a plane
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(256) void router_kernel(
     load_w(g0 * kBlock);
   }
   for (int g = g0; g < g1; ++g) {
-    // ---- 1x128 quantisation of x for the wave's 16 tokens: row l16's 128
+    // ---- quantisation of x for the wave's 16 tokens: row l16's 128
     // values sit in the four lanes l16 + 16 gq
     {
       float v[32];
@@ -247,7 +248,29 @@ __global__ __launch_bounds__(256) void router_kernel(
       am = fmaxf(am, __shfl_xor(am, 16));
       am = fmaxf(am, __shfl_xor(am, 32));
       const float s = am > 0.f ? am / kFp8Max : 1.0f;
-      if (xt < T) {
+      if (mx) {
+        // MXFP8: columns 32c..32c+31 of the group are one block, held 8 per
+        // lane by the four lanes l16 + 16 gq; E8M0 codes of the 4 blocks -> one dword
+        uint32_t codes = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          float bm = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(v[8 * c + i]));
+          bm = fmaxf(bm, __shfl_xor(bm, 16));
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          const uint32_t code = mx_code(bm);
+          const float inv = mx_inv_scale(code);
+          if (xt < T)
+            *reinterpret_cast<uint2*>(xq + (size_t)xt * d + g * kBlock + 32 * c + 8 * gq) = make_uint2(
+                f32x4_to_e4m3(v[8 * c] * inv, v[8 * c + 1] * inv, v[8 * c + 2] * inv, v[8 * c + 3] * inv),
+                f32x4_to_e4m3(v[8 * c + 4] * inv, v[8 * c + 5] * inv, v[8 * c + 6] * inv,
+                              v[8 * c + 7] * inv));
+          codes |= code << (8 * c);
+        }
+        if (xt < T && gq == 0)
+          reinterpret_cast<uint32_t*>(xs)[(size_t)xt * ngroups + g] = codes;
+      } else if (xt < T) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           float q[8];
@@ -256,7 +279,7 @@ __global__ __launch_bounds__(256) void router_kernel(
           *reinterpret_cast<uint2*>(xq + (size_t)xt * d + g * kBlock + 32 * c + 8 * gq) =
               make_uint2(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), f32x4_to_e4m3(q[4], q[5], q[6], q[7]));
         }
-        if (gq == 0) xs[(size_t)xt * ngroups + g] = s;
+        if (gq == 0) reinterpret_cast<float*>(xs)[(size_t)xt * ngroups + g] = s;
       }
     }
     v4f part[NBW];
@@ -559,15 +582,15 @@ __global__ __launch_bounds__(512) void route_small_kernel(
 
 template <int NBW>
 hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br, int T, int d,
-                             int E, int k, int gate_mode, int nsplit, float* partial, int32_t* topk_idx,
-                             float* topk_w, int32_t* hist, uint8_t* xq, float* xs,
+                             int E, int k, int gate_mode, bool mx, int nsplit, float* partial,
+                             int32_t* topk_idx, float* topk_w, int32_t* hist, uint8_t* xq, void* xs,
                              const SmallRoute* sr, hipStream_t stream) {
   const int tiles = ceil_div(T, RT_TT);
   const int ngroups = d / kBlock;
   const int gps = ceil_div(ngroups, nsplit);
   const int ns = ceil_div(ngroups, gps);
   hipLaunchKernelGGL((router_kernel<NBW>), dim3(tiles, ns), dim3(256), 0, stream, x, Wr, br, T, d,
-                     E, k, gate_mode, gps, partial, topk_idx, topk_w, hist, xq, xs);
+                     E, k, gate_mode, mx ? 1 : 0, gps, partial, topk_idx, topk_w, hist, xq, xs);
   if (sr != nullptr)
     hipLaunchKernelGGL((route_small_kernel<NBW>), dim3(1), dim3(512), 0, stream, partial, ns, ns == 1,
                        br, T, E, k, gate_mode, topk_idx, topk_w, sr->counts, sr->offsets, sr->tile_off0,
@@ -594,15 +617,15 @@ int router_splits(int T, int d) {
 }
 
 hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, int T, int d, int E,
-                         int k, int gate_mode, float* partial, int32_t* topk_idx, float* topk_w,
-                         int32_t* hist, uint8_t* xq, float* xs, const SmallRoute* sr,
+                         int k, int gate_mode, bool mx, float* partial, int32_t* topk_idx,
+                         float* topk_w, int32_t* hist, uint8_t* xq, void* xs, const SmallRoute* sr,
                          hipStream_t stream) {
   const int nsplit = router_splits(T, d);
   switch (ceil_div(E, 16)) {
 #define MOE_ROUTER_CASE(n)                                                                     \
   case n:                                                                                      \
-    return launch_router_nbw<n>(x, Wr, br, T, d, E, k, gate_mode, nsplit, partial, topk_idx, topk_w, hist, \
-                                xq, xs, sr, stream);
+    return launch_router_nbw<n>(x, Wr, br, T, d, E, k, gate_mode, mx, nsplit, partial, topk_idx, \
+                                topk_w, hist, xq, xs, sr, stream);
     MOE_ROUTER_CASE(1)
     MOE_ROUTER_CASE(2)
     MOE_ROUTER_CASE(3)

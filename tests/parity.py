@@ -5,7 +5,8 @@ Gates (written here, used by every GPU parity test):
   permuted row order and the row of every (token, expert) pair are
   bit-identical; gate weights agree per expert to rtol 1e-5 + atol 1e-6
   (fp32 logits on the GPU vs fp64 in the oracle);
-* activation quantisation: x codes and scales are bit-identical;
+* activation quantisation: x codes and scales (fp32 per 128 columns, or E8M0
+  per 32 columns for the MXFP8 format) are bit-identical;
 * output: with o the oracle's unrounded fp64 output and g the GPU's bf16,
   over the real (unpadded) columns,
       max|g - o| <= 2e-2 * RMS(o)   and   sum|g - o| / sum|o| <= 5e-3.
@@ -108,7 +109,19 @@ def _e4m3_spacing(q):
 H_CODE_SLACK = 0.5
 
 
-def check_h_decisions(dbg: dict, ref: dict):
+# The scales are decisions too: an fp32 scale agrees with the oracle's to
+# H_SCALE_RTOL; an E8M0 code must be the MX code of an amax within H_SCALE_RTOL
+# of the exact block amax.  For MX the code slack is kept in absolute terms,
+# H_CODE_SLACK units of the 128-column group's amax/448, since the GEMM's
+# accumulation error does not depend on how h is quantised afterwards.
+H_SCALE_RTOL = 5e-4
+
+
+def _fmt(inp_or_ref) -> str:
+    return inp_or_ref.get("format", "block128")
+
+
+def check_h_decisions(dbg: dict, ref: dict, fmt: str = "block128"):
     """Every GPU h code is an admissible rounding of the oracle's exact h; the
     scales agree to the accumulation error.  Returns the number of codes that
     differ from the oracle's own decisions (reported, not gated)."""
@@ -117,12 +130,23 @@ def check_h_decisions(dbg: dict, ref: dict):
     n_diff = n = 0
     for e, it in ref["experts"].items():
         rows = it["rows"]
-        np.testing.assert_allclose(hs[rows], it["hs"], rtol=5e-4, err_msg=f"h scales expert {e}")
+        h = it["h"]
         qg = codecs.e4m3_decode(hq[rows])
-        sg = np.repeat(hs[rows].astype(np.float64), 128, axis=1)
-        qx = it["h"] / sg                                   # exact h in the GPU's code units
-        bad = np.abs(qg - qx) > _e4m3_spacing(qg) + H_CODE_SLACK
-        assert not bad.any(), (f"h codes expert {e}: gpu {qg[bad][:8]} exact {qx[bad][:8]}")
+        if fmt == "mx":
+            amax = np.abs(h).reshape(len(rows), -1, 32).max(axis=2)
+            lo = orc.mx_scale_exponent(amax * (1 - H_SCALE_RTOL)) + 127
+            hi = orc.mx_scale_exponent(amax * (1 + H_SCALE_RTOL)) + 127
+            c = hs[rows].astype(np.int64)
+            assert np.all((c >= lo) & (c <= hi)), f"h E8M0 scales expert {e}"
+            sg = np.repeat(codecs.e8m0_decode(hs[rows]), 32, axis=1)
+            unit = np.repeat(np.abs(h).reshape(len(rows), -1, 128).max(axis=2) / 448.0, 128, axis=1)
+        else:
+            np.testing.assert_allclose(hs[rows], it["hs"], rtol=H_SCALE_RTOL,
+                                       err_msg=f"h scales expert {e}")
+            sg = unit = np.repeat(hs[rows].astype(np.float64), 128, axis=1)
+        # |GPU value - exact h| within one code spacing plus the slack
+        bad = np.abs(qg * sg - h) > _e4m3_spacing(qg) * sg + H_CODE_SLACK * unit
+        assert not bad.any(), (f"h codes expert {e}: gpu {qg[bad][:8]} exact {(h / sg)[bad][:8]}")
         n_diff += int((hq[rows] != it["hq"]).sum())
         n += hq[rows].size
     return n_diff, n
@@ -132,14 +156,15 @@ def check_down_stage(dbg: dict, ref: dict, inp: dict, d_real: int):
     """The down GEMM output of every evaluated row equals its definition applied
     to the GPU's own (validated) h codes: deq(hq, hs) @ deq(W_down) + b_down,
     within the FP8 MFMA accumulation error (2^-10 of the sum of |terms|)."""
+    _, deq, wdeq = orc.FORMATS[_fmt(inp)]
     hq = dbg["hq"].cpu().numpy()
     hs = dbg["hs"].cpu().numpy()
     y = dbg["y"].cpu().numpy()
     worst = 0.0
     for e, it in ref["experts"].items():
         rows = it["rows"]
-        hdeq = orc.dequant_groups(hq[rows], hs[rows])
-        W = orc.dequant_weight(inp["W_down"][e], inp["S_down"][e])
+        hdeq = deq(hq[rows], hs[rows])
+        W = wdeq(inp["W_down"][e], inp["S_down"][e])
         want = hdeq @ W + codecs.bf16_decode(inp["b_down"][e])
         bound = 2.0 ** -10 * (np.abs(hdeq) @ np.abs(W)) + 1e-6
         err = np.abs(y[rows] - want)
@@ -168,6 +193,7 @@ def decision_adjusted_reference(dbg: dict, ref: dict, inp: dict):
     """The oracle's output with its h decisions replaced by the GPU's validated
     ones (the only freedom the method leaves): out + sum_j w_j (deq(hq_gpu) -
     deq(hq_oracle)) @ deq(W_down), per evaluated token."""
+    _, deq, wdeq = orc.FORMATS[_fmt(inp)]
     hq = dbg["hq"].cpu().numpy()
     hs = dbg["hs"].cpu().numpy()
     tok = ref["tokens"]
@@ -176,10 +202,10 @@ def decision_adjusted_reference(dbg: dict, ref: dict, inp: dict):
     row_token = ref["row_token"]
     for e, it in ref["experts"].items():
         rows = it["rows"]
-        delta = orc.dequant_groups(hq[rows], hs[rows]) - orc.dequant_groups(it["hq"], it["hs"])
+        delta = deq(hq[rows], hs[rows]) - deq(it["hq"], it["hs"])
         if not delta.any():
             continue
-        W = orc.dequant_weight(inp["W_down"][e], inp["S_down"][e])
+        W = wdeq(inp["W_down"][e], inp["S_down"][e])
         dY = delta @ W
         for i, r in enumerate(rows):
             t = int(row_token[r])
