@@ -45,12 +45,18 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "92db357d303f25dafa9254f5810a78d180033f1a98328fd59fdd1017981ced53",
-           "fetch_kib": 271898.225, "write_kib": 765.15625,
-           "copy_fetch_kib": 524313.6875, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "92db357d303f25dafa9254f5810a78d180033f1a98328fd59fdd1017981ced53",
-           "fetch_kib": 887459.0, "write_kib": 103982.48125,
-           "copy_fetch_kib": 524306.25, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
+           "fetch_kib": 271903.450, "write_kib": 765.163,
+           "copy_fetch_kib": 524311.6875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
+           "fetch_kib": 872689.162, "write_kib": 103987.106,
+           "copy_fetch_kib": 524306.625, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
+              "fetch_kib": 280254.938, "write_kib": 765.112,
+              "copy_fetch_kib": 524307.375, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
+              "fetch_kib": 952815.550, "write_kib": 103731.919,
+              "copy_fetch_kib": 524307.75, "copy_write_kib": 1048576.0},
 }
 
 
