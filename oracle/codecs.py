@@ -9,8 +9,11 @@ type is OCP E4M3 ("fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities, NaN = S.1111.111, largest finite 448, smallest
 subnormal 2^-9.  The MXFP8 variant (the post's section "Quantization" on
 Blackwell: microscaling) adds the OCP E8M0 scale: 8 exponent bits with bias
-127, no sign and no mantissa, code 0xFF = NaN.  Everything here is written
-from those definitions.
+127, no sign and no mantissa, code 0xFF = NaN.  The FP4 weights (the post's
+section "GPT-OSS on Hopper": the checkpoints ship in MXFP4) use the OCP E2M1
+element: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, no
+infinities or NaN, magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Everything here is
+written from those definitions.
 """
 from __future__ import annotations
 
@@ -71,6 +74,51 @@ def e8m0_decode(codes: np.ndarray) -> np.ndarray:
     c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     v = np.ldexp(1.0, c - E8M0_BIAS)
     return np.where(c == 0xFF, np.nan, v)
+
+
+def _e2m1_value(code: int) -> float:
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return sign * (m / 2.0)                      # subnormal: 0 or 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+#: value of every e2m1 code 0..15, fp64 (exact)
+E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E2M1_POS = E2M1_TABLE[:8]                           # 0, 0.5, 1, 1.5, 2, 3, 4, 6
+assert np.all(np.diff(_E2M1_POS) > 0)
+
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes (0..15, any integer dtype) -> fp64 values."""
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8) & 0xF]
+
+
+def e2m1_encode_rne(v: np.ndarray) -> np.ndarray:
+    """Values -> nearest e2m1 code, ties to the even mantissa; magnitudes above 6
+    saturate to 6; the sign of zero is kept."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 6.0)
+    # nearest of the 8 magnitudes; on a tie the lower index wins only if its code is even
+    d = np.abs(a[..., None] - _E2M1_POS)
+    best = d.argmin(axis=-1)
+    dmin = d.min(axis=-1)
+    nxt = np.minimum(best + 1, 7)
+    tie = np.take_along_axis(d, nxt[..., None], axis=-1)[..., 0] == dmin
+    best = np.where(tie & (nxt != best) & (best % 2 == 1), nxt, best)
+    return (best.astype(np.uint8) | np.where(np.signbit(v), 0x8, 0).astype(np.uint8)).astype(np.uint8)
+
+
+def unpack_fp4_k(packed: np.ndarray) -> np.ndarray:
+    """[K/2, N] bytes, two 4-bit codes per byte along K (low nibble = even K)
+    -> [K, N] codes."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((2 * p.shape[0],) + p.shape[1:], dtype=np.uint8)
+    out[0::2] = p & 0xF
+    out[1::2] = p >> 4
+    return out
 
 
 def bf16_decode(bits: np.ndarray) -> np.ndarray:

@@ -31,7 +31,10 @@ MXFP8 variant (``inp["format"] == "mx"``; the post's section
 "Quantization" names microscaling as the Blackwell format, with the weights
 converted statically): steps 6 and 8 quantise per row per 32 columns with a
 power-of-two E8M0 scale, and the weights carry one E8M0 scale per 32 rows
-of K per column; everything else is unchanged.
+of K per column; everything else is unchanged.  MXFP4 weights
+(``"mxfp4"``; the post's section "GPT-OSS on Hopper" says the checkpoints ship
+in MXFP4): the weights are E2M1 with the same E8M0 scale blocks, two codes per
+byte along K; the activations are MXFP8 as above.
 
 Readings of points the pages leave open are listed in the repository's
 design notes; each is marked "reading:" below where it is taken.
@@ -46,7 +49,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .codecs import E8M0_BIAS, bf16_decode, e4m3_decode, e4m3_encode_rne, e8m0_decode
+from .codecs import (E8M0_BIAS, bf16_decode, e2m1_decode, e4m3_decode, e4m3_encode_rne, e8m0_decode,
+                     unpack_fp4_k)
 
 GROUP = 128
 MX_GROUP = 32
@@ -203,10 +207,20 @@ def dequant_weight_mx(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
             * e8m0_decode(scales)[:, None, :]).reshape(K, N)
 
 
+def dequant_weight_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """One expert's MXFP4 matrix: e2m1 codes packed two per byte along K
+    ([K/2, N], low nibble = even K) times E8M0 scales [K/32, N] -> fp64 [K, N]."""
+    codes = unpack_fp4_k(packed)
+    K, N = codes.shape
+    return (e2m1_decode(codes).reshape(K // MX_GROUP, MX_GROUP, N)
+            * e8m0_decode(scales)[:, None, :]).reshape(K, N)
+
+
 #: quantise activations, dequantise them, dequantise one expert's weights
 FORMATS = {
     "block128": (quantize_groups, dequant_groups, dequant_weight),
     "mx": (quantize_mx, dequant_mx, dequant_weight_mx),
+    "mxfp4": (quantize_mx, dequant_mx, dequant_weight_mxfp4),
 }
 
 
@@ -263,7 +277,7 @@ def forward(inp: dict, tokens=None, keep=False):
     """The whole block. ``tokens`` (optional) restricts the expert work and the
     output to a subset of tokens; routing and permutation cover all tokens.
 
-    ``inp["format"]`` (optional): "block128" (default) or "mx".
+    ``inp["format"]`` (optional): "block128" (default), "mx" or "mxfp4".
 
     Returns a dict: out64 [len(tokens), d] fp64 (unrounded), routing arrays,
     xq/xs for the evaluated tokens, and (with ``keep``) per-row intermediates.

@@ -7,10 +7,14 @@ three input-preparation jobs:
 
 * draws every tensor from its own NumPy ``SeedSequence`` sub-stream, so any
   tensor (and any single expert's weights) is reproducible on its own;
-* converts expert weights to FP8 e4m3 with one fp32 scale per 128x128 block,
-  the static weight conversion of the serving scheme the "GPT-OSS on day 0"
-  post picks (section "Kernels for GPT-OSS", FP8 128x128 block scaling);
-  the e4m3 rounding is PyTorch's ``float8_e4m3fn`` cast, a library routine;
+* converts expert weights statically, as the "GPT-OSS on day 0" post's
+  serving formats need: FP8 e4m3 with one fp32 scale per 128x128 block
+  (section "GPT-OSS on Hopper"), or MXFP8 with one E8M0 power-of-two scale
+  per 32 rows of K per column (section "Quantization": microscaling, weights
+  converted statically), both rounded by PyTorch's ``float8_e4m3fn`` cast (a
+  library routine), or MXFP4 (section "GPT-OSS on Hopper": the checkpoints
+  ship in MXFP4): E2M1 codes with the same scale blocks, rounded here by a
+  nearest-value search, packed two per byte along K;
 * conditions the router inputs: rows of ``x`` whose k-th and (k+1)-th fp64
   router logits lie within ``MARGIN`` are redrawn, so the top-k set of every
   token is unambiguous at fp32 accuracy; for the skewed-load layer the router
@@ -137,6 +141,40 @@ def quantize_weight_mx(w: np.ndarray):
     return codes, (e + 127).to(torch.uint8).numpy()
 
 
+_E2M1_MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _e2m1_round(q: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code (ties to the even code), sign in bit 3; |q| <= 6."""
+    a = np.abs(q)
+    lo = np.clip(np.searchsorted(_E2M1_MAGS, a, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    dlo, dhi = a - _E2M1_MAGS[lo], _E2M1_MAGS[hi] - a
+    up = (dhi < dlo) | ((dhi == dlo) & (lo % 2 == 1))
+    idx = np.where(up & (hi != lo), hi, lo).astype(np.uint8)
+    return idx | np.where(np.signbit(q), 8, 0).astype(np.uint8)
+
+
+def quantize_weight_mxfp4(w: np.ndarray):
+    """Static MXFP4 conversion of one expert matrix ``w`` [K, N] (fp32).
+
+    One E8M0 scale 2^e per 32 consecutive K rows of a column, e the smallest
+    exponent with amax <= 6 * 2^e (amax = m * 2^p with m in [0.5, 1):
+    e = p - 3 if m <= 0.75, else p - 2), 2^-127 for an all-zero block; codes =
+    E2M1 nearest of w / 2^e, two per byte along K (low nibble = even K).
+    Returns (packed uint8 [K/2, N], E8M0 codes uint8 [K/32, N]).
+    """
+    K, N = w.shape
+    t = np.asarray(w, np.float64).reshape(K // MX_BLOCK, MX_BLOCK, N)
+    amax = np.abs(t).max(axis=1)
+    m, p = np.frexp(amax)
+    e = np.where(m <= 0.75, p - 3, p - 2)
+    e = np.clip(np.where(amax > 0, e, -127), -127, 127)
+    codes = _e2m1_round(t / np.ldexp(1.0, e)[:, None, :]).reshape(K, N)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def _draw_router(layer: Layer, seed: int):
     d, dr, E = layer.d, layer.d_real, layer.E
     Wr = np.zeros((d, E), np.float32)
@@ -224,7 +262,7 @@ def _expert_weights(layer: Layer, seed: int, e: int, fmt: str = "block128"):
     wdn = np.zeros((f, d), np.float32)
     wdn[:, :dr] = _rng(seed, layer.layer_id, _T_WDN, e).standard_normal((f, dr), dtype=np.float32)
     wdn[:, :dr] *= np.float32(1.0 / np.sqrt(f))
-    conv = quantize_weight_mx if fmt == "mx" else quantize_weight_blocks
+    conv = {"mx": quantize_weight_mx, "mxfp4": quantize_weight_mxfp4}.get(fmt, quantize_weight_blocks)
     return conv(wgu), conv(wdn)
 
 
@@ -234,9 +272,10 @@ _WEIGHT_CACHE: dict = {}
 def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache: bool = True,
                  fmt: str = "block128"):
     """All layer parameters as NumPy arrays (FP8 codes as uint8, bf16 as uint16 bits).
-    ``fmt``: "block128" (fp32 scales per 128x128 block) or "mx" (E8M0 scales
-    per 32 K rows per column); the underlying fp32 draws are the same."""
-    if fmt not in ("block128", "mx"):
+    ``fmt``: "block128" (fp32 scales per 128x128 block), "mx" (E8M0 scales
+    per 32 K rows per column) or "mxfp4" (E2M1 codes packed two per byte
+    along K, the same E8M0 scales); the underlying fp32 draws are the same."""
+    if fmt not in ("block128", "mx", "mxfp4"):
         raise ValueError(f"unknown weight format {fmt!r}")
     key = (layer, seed, fmt)
     if cache and key in _WEIGHT_CACHE:
@@ -245,9 +284,10 @@ def make_weights(layer: Layer, seed: int = 0, workers: int | None = None, cache:
     Wr, br = _draw_router(layer, seed)
     if layer.router == "zipf":
         br = _calibrate_zipf_bias(layer, seed, Wr)
-    Wgu = np.empty((E, d, 2 * f), np.uint8)
-    Wdn = np.empty((E, f, d), np.uint8)
-    if fmt == "mx":
+    kp = 2 if fmt == "mxfp4" else 1      # K rows per stored byte row
+    Wgu = np.empty((E, d // kp, 2 * f), np.uint8)
+    Wdn = np.empty((E, f // kp, d), np.uint8)
+    if fmt in ("mx", "mxfp4"):
         Sgu = np.empty((E, d // MX_BLOCK, 2 * f), np.uint8)
         Sdn = np.empty((E, f // MX_BLOCK, d), np.uint8)
     else:
@@ -285,7 +325,8 @@ def make_inputs(cfg, seed: int = 0, T: int | None = None, margin=MARGIN, fmt: st
     W_gateup (e4m3 [E,d,2f]), S_gateup, b_gateup (bf16 bits [E,2f]), W_down
     (e4m3 [E,f,d]), S_down, b_down (bf16 bits [E,d]).  Scales: "block128"
     fp32 [E,d/128,2f/128] and [E,f/128,d/128]; "mx" E8M0 uint8 [E,d/32,2f]
-    and [E,f/32,d].
+    and [E,f/32,d]; "mxfp4" the same scales with W_gateup [E,d/2,2f] and
+    W_down [E,f/2,d] holding two E2M1 codes per byte along K.
     """
     if isinstance(cfg, str):
         c = CONFIGS[cfg]

@@ -45,9 +45,14 @@ def build(k: int, fmt: str = "block128") -> dict:
         Wdn[1] = 0x38
     else:
         bdn[1, 3] = 1.0
-    if fmt == "mx":  # the same power-of-two scales as E8M0 codes per 32 K rows per column
+    if fmt in ("mx", "mxfp4"):  # the same power-of-two scales as E8M0 codes per 32 K rows per column
         Sgu = np.full((E, d // 32, 2 * f), 127, np.uint8)
         Sdn = np.stack([np.full((f // 32, d), 126, np.uint8), np.full((f // 32, d), 127, np.uint8)])
+    if fmt == "mxfp4":  # every weight above is an E2M1 value: re-code, pack two per byte along K
+        e4m3_to_e2m1 = {0x00: 0x0, 0x38: 0x2, 0x40: 0x4, 0x30: 0x1, 0xB0: 0x9}
+        pack = lambda w: (np.vectorize(e4m3_to_e2m1.get)(w[:, 0::2]) |
+                          (np.vectorize(e4m3_to_e2m1.get)(w[:, 1::2]) << 4)).astype(np.uint8)
+        Wgu, Wdn = pack(Wgu), pack(Wdn)
     return dict(T=1, d=d, d_real=d, f=f, E=E, k=k, x=_bf16(x), W_router=Wr, b_router=br,
                 W_gateup=Wgu, S_gateup=Sgu, b_gateup=_bf16(bgu), W_down=Wdn, S_down=Sdn,
                 b_down=_bf16(bdn), format=fmt)
@@ -55,7 +60,7 @@ def build(k: int, fmt: str = "block128") -> dict:
 
 def expected(k: int, fmt: str = "block128") -> np.ndarray:
     fx = load()
-    exp = fx["mx"]["expected"] if fmt == "mx" else fx["expected"]
+    exp = fx["mx"]["expected"] if fmt in ("mx", "mxfp4") else fx["expected"]
     out = np.zeros(128)
     for i, v in exp[f"k{k}"].items():
         out[int(i)] = v

@@ -514,3 +514,90 @@ def test_handworked_block_mx(k):
     assert list(res["idx"][0]) == ([0] if k == 1 else [0, 1])
     np.testing.assert_allclose(res["out64"][0], want, rtol=0, atol=1e-12 * np.abs(want).max())
     assert res["xq"][0, 0] == 0x7E and res["xq"][0, 1] == 0x76 and res["xs"][0, 0] == 127 - 7
+
+
+# ------------------------------------------------------------------ MXFP4 weights
+def test_e2m1_decode_format_points():
+    fx = json.load(open(os.path.join(GOLD, "e2m1_points.json")))
+    for code, val in fx["points"].items():
+        got = codecs.E2M1_TABLE[int(code, 16)]
+        assert got == val and math.copysign(1, got) == math.copysign(1, val), code
+    # every E2M1 value is an e4m3 value (the reduction the pins below rely on)
+    assert np.all(np.isin(codecs.E2M1_TABLE, codecs.E4M3_TABLE))
+
+
+def _brute_e2m1(v):
+    """Nearest E2M1 code by exhaustive search over the 8 magnitudes; a tie goes
+    to the even code (mantissa bit 0); the sign bit follows v."""
+    a = min(abs(v), 6.0)
+    best = min(range(8), key=lambda c: (abs(codecs.E2M1_TABLE[c] - a), c % 2))
+    return best | (8 if math.copysign(1, v) < 0 else 0)
+
+
+def test_e2m1_encoder_vs_brute_force():
+    mags = codecs.E2M1_TABLE[:8]
+    mids = (mags[1:] + mags[:-1]) / 2
+    vals = np.concatenate([mags, mids, np.nextafter(mids, 0), np.nextafter(mids, 10), [6.5, 100.0, 1e-9],
+                           np.random.default_rng(16).uniform(0, 7, 500)])
+    vals = np.concatenate([vals, -vals])
+    got = codecs.e2m1_encode_rne(vals)
+    want = np.array([_brute_e2m1(float(v)) for v in vals], np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_unpack_fp4_order():
+    packed = np.array([[0x42, 0x09], [0xF1, 0x70]], np.uint8)      # [K/2 = 2, N = 2]
+    codes = codecs.unpack_fp4_k(packed)
+    np.testing.assert_array_equal(codes, [[0x2, 0x9], [0x4, 0x0], [0x1, 0x0], [0xF, 0x7]])
+
+
+def _fp4_as_mx(packed, scales):
+    """The same weights as MX e4m3 codes (exact: every E2M1 value is an e4m3 value)."""
+    vals = codecs.e2m1_decode(codecs.unpack_fp4_k(packed))
+    return codecs.e4m3_encode_rne(vals), scales
+
+
+def test_dequant_weight_mxfp4_reduces_to_mx():
+    rng = np.random.default_rng(17)
+    packed = rng.integers(0, 256, size=(64, 256), dtype=np.uint8)    # K = 128
+    sc = rng.integers(110, 140, size=(4, 256), dtype=np.uint8)
+    W = oracle.dequant_weight_mxfp4(packed, sc)
+    np.testing.assert_array_equal(W, oracle.dequant_weight_mx(*_fp4_as_mx(packed, sc)))
+    assert W[1, 0] == codecs.E2M1_TABLE[packed[0, 0] >> 4] * 2.0 ** (int(sc[0, 0]) - 127)
+    assert W[33, 7] == codecs.E2M1_TABLE[packed[16, 7] >> 4] * 2.0 ** (int(sc[1, 7]) - 127)
+
+
+def test_mxfp4_weight_conversion_vs_oracle_codec():
+    """The generator's static MXFP4 conversion against the oracle's E2M1 encoder
+    with the scale found by search: the smallest 2^e with amax <= 6 * 2^e."""
+    rng = np.random.default_rng(18)
+    w = (rng.normal(size=(128, 64)) * 0.05).astype(np.float32)
+    w[32:64, 3] = 0.0
+    packed, sc = gen.quantize_weight_mxfp4(w)
+    for b in range(4):
+        for n in range(64):
+            blk = w[32 * b:32 * b + 32, n].astype(np.float64)
+            am = np.abs(blk).max()
+            e = next(e for e in range(-127, 128) if am <= 6.0 * 2.0 ** e)
+            assert sc[b, n] == e + 127, (b, n)
+            codes = codecs.e2m1_encode_rne(blk / 2.0 ** e)
+            np.testing.assert_array_equal(codecs.unpack_fp4_k(packed)[32 * b:32 * b + 32, n], codes)
+
+
+def test_mxfp4_forward_equals_mx_with_the_same_weights():
+    layer = gen.custom_layer(256, 128, 5, 2, layer_id=330)
+    inp = gen.make_inputs(layer, T=20, fmt="mxfp4")
+    mx = dict(inp, format="mx")
+    for key in ("W_gateup", "W_down"):
+        mx[key] = np.stack([_fp4_as_mx(inp[key][e], None)[0] for e in range(inp["E"])])
+    a, b = oracle.forward(inp)["out64"], oracle.forward(mx)["out64"]
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_handworked_block_mxfp4(k):
+    inp = handworked.build(k, fmt="mxfp4")
+    assert inp["W_gateup"].shape == (2, 64, 256) and inp["W_gateup"][0, 0, 0] == 0x42
+    res = oracle.forward(inp)
+    want = handworked.expected(k, fmt="mxfp4")
+    np.testing.assert_allclose(res["out64"][0], want, rtol=0, atol=1e-12 * np.abs(want).max())
