@@ -1,6 +1,6 @@
 """Benchmark of the sparse MoE block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1] [--format block128|mx]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1] [--format block128|mx|mxfp4]
 
 A step is one whole forward (router + top-k + softmax + x quantisation,
 routing scan and placement, gate/up grouped FP8 GEMM with SwiGLU and h
@@ -8,7 +8,7 @@ quantisation, down grouped FP8 GEMM, weighted combine) over one batch of
 seeded synthetic input already resident in HBM.  The default workload is the
 decode-shaped gpt-oss-20b-like layer (T=64 tokens, d=2944, f=2944, E=32,
 k=4) with 128x128 block-scaled FP8 weights (``--format mx``: the MXFP8
-variant, E8M0 scales per 32).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
+variant, E8M0 scales per 32; ``--format mxfp4``: E2M1 weights with those scales).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
 GEMM (its duration measured with HIP events inside the timed region, on the
 stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload.
@@ -82,7 +82,12 @@ def log(*a):
 def _scale_bytes(K, N, fmt):
     """Bytes of the scales of one K x N weight matrix: fp32 per 128x128 block,
     or one E8M0 byte per 32 K rows per column (MX)."""
-    return (K // 32) * N if fmt == "mx" else 4 * (K // 128) * (N // 128)
+    return (K // 32) * N if fmt in ("mx", "mxfp4") else 4 * (K // 128) * (N // 128)
+
+
+def _weight_bytes(K, N, fmt):
+    """Bytes of one K x N weight matrix's elements: e4m3, or two E2M1 per byte."""
+    return K * N // 2 if fmt == "mxfp4" else K * N
 
 
 def _act_scale_bytes(rows, K):
@@ -102,7 +107,7 @@ def gateup_algorithmic(inp, counts):
     fmt = inp.get("format", "block128")
     R = T * k
     touched = int(np.count_nonzero(counts))
-    w = touched * (d * 2 * f + _scale_bytes(d, 2 * f, fmt) + 2 * 2 * f)
+    w = touched * (_weight_bytes(d, 2 * f, fmt) + _scale_bytes(d, 2 * f, fmt) + 2 * 2 * f)
     a = T * d + _act_scale_bytes(T, d)
     h = R * f + _act_scale_bytes(R, f)
     return dict(bytes=w + a + h, flops=2.0 * R * d * 2 * f, touched=touched)
@@ -113,7 +118,7 @@ def down_algorithmic(inp, counts):
     fmt = inp.get("format", "block128")
     R = T * k
     touched = int(np.count_nonzero(counts))
-    w = touched * (f * d + _scale_bytes(f, d, fmt) + 2 * d)
+    w = touched * (_weight_bytes(f, d, fmt) + _scale_bytes(f, d, fmt) + 2 * d)
     return dict(bytes=w + R * f + _act_scale_bytes(R, f) + 4 * R * d, flops=2.0 * R * f * d)
 
 
@@ -148,7 +153,7 @@ def main():
     ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS))
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),
-                    help="weight format: 128x128 block-scaled FP8 or MXFP8 (E8M0 per 32)")
+                    help="weight format: 128x128 block-scaled FP8, MXFP8 (E8M0 per 32) or MXFP4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, one device-to-device copy of this many MiB "
@@ -222,7 +227,7 @@ def main():
     tok_s = T / (ms * 1e-3)
 
     decode = (args.path == "decode") or (args.path == "auto" and T * k <= 32 * E)
-    tkey = args.workload + ("-mx" if fmt == "mx" else "")
+    tkey = args.workload + ("" if fmt == "block128" else "-" + fmt)
     if decode:
         ach = ga["bytes"] / (gate_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -232,9 +237,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / FP8_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(tkey)}
-    mxs = "true" if fmt == "mx" else "false"
-    roof["kernel"] = (f"grouped_gemm_dma_kernel<true, 32, 256, {mxs}>" if decode else
-                      f"grouped_gemm_wide_kernel<true, {mxs}>") + \
+    tf = {"block128": "false, false", "mx": "true, false", "mxfp4": "true, true"}[fmt]
+    roof["kernel"] = (f"grouped_gemm_dma_kernel<true, 32, 256, {tf}>" if decode else
+                      f"grouped_gemm_wide_kernel<true, {tf}>") + \
         " (gate/up + bias + SwiGLU + h quantisation)"
     roof["avg_ms"] = round(gate_ms, 5)
     roof["algorithmic_bytes"] = ga["bytes"]

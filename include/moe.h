@@ -65,7 +65,8 @@ typedef enum {
   MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_bytes */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
   MOE_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError)           */
-  MOE_ERR_FLAGS = -7        /* unknown bits in `flags`, path 3, or a bad stage range */
+  MOE_ERR_FLAGS = -7        /* unknown bits in `flags`, path 3, MOE_WEIGHTS_FP4 without
+                               MOE_FORMAT_MX, or a bad stage range */
 } moe_status;
 
 #define MOE_MAX_EXPERTS 256
@@ -101,6 +102,17 @@ typedef enum {
  * copies xs / hs then hold E8M0 bytes [T, d/32] / [T*k, f/32]: the same
  * byte counts as the fp32 scales of the default format. */
 #define MOE_FORMAT_MX 16u
+/* MOE_WEIGHTS_FP4 (only together with MOE_FORMAT_MX; MOE_FORMAT_MXFP4 sets
+ * both): MXFP4 weights, the format the gpt-oss checkpoints ship in ("GPT-OSS
+ * on day 0", section "GPT-OSS on Hopper").  Elements are OCP E2M1 (sign,
+ * 2 exponent bits with bias 1, 1 mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}),
+ * two per byte along K, the even K in the low nibble:
+ *   W_gateup   [E, d/2, 2f] bytes    W_down   [E, f/2, d] bytes
+ * with the E8M0 scales of MOE_FORMAT_MX ([E, d/32, 2f], [E, f/32, d]).  x and
+ * h stay MXFP8 (e4m3 per 32 columns), so every MFMA multiplies E2M1 weights
+ * by e4m3 activations. */
+#define MOE_WEIGHTS_FP4 32u
+#define MOE_FORMAT_MXFP4 (MOE_FORMAT_MX | MOE_WEIGHTS_FP4)
 
 /* Bytes of device workspace moe_forward needs for these sizes (0 if the sizes
  * are invalid).  The workspace holds the routing tables, the quantised
@@ -142,7 +154,8 @@ moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_r
 /* moe_forward_ex with MXFP8 weights (flags | MOE_FORMAT_MX):
  *   X_gateup   E8M0 [E, d/32, 2f]
  *   X_down     E8M0 [E, f/32, d]
- * the other arguments and `flags` bits as for moe_forward_ex. */
+ * the other arguments and `flags` bits as for moe_forward_ex (MOE_WEIGHTS_FP4
+ * selects MXFP4 weights). */
 moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_router, int32_t k,
                           const uint8_t* W_gateup, const uint8_t* X_gateup, const void* b_gateup,
                           const uint8_t* W_down, const uint8_t* X_down, const void* b_down,

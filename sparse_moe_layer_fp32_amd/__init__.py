@@ -1,7 +1,8 @@
 """Sparse MoE block forward on one MI355X (gfx950): Python binding of the C ABI.
 
 The block (router with bias, top-k, softmax over the selected logits, FP8
-SwiGLU experts with biases, 128x128 block-scaled or MXFP8, weighted combine) runs in
+SwiGLU experts with biases, 128x128 block-scaled FP8, MXFP8 or MXFP4 weights,
+weighted combine) runs in
 HIP kernels of ``libsparse_moe.so``; this module only checks tensors and
 passes device pointers and the current HIP stream (see ``include/moe.h``).
 There is no CPU fallback: without the built library every call raises.
@@ -19,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libsparse_moe.so")
 PATHS = {"auto": 0, "prefill": 1, "decode": 2}
 ROUTINGS = {"topk_softmax": 0, "softmax_topk": 4}   # MOE_ROUTE_SOFTMAX_ALL
 GATE_BF16 = 8                                       # MOE_GATE_BF16
-FORMATS = {"block128": 0, "mx": 16}                 # MOE_FORMAT_MX
+FORMATS = {"block128": 0, "mx": 16, "mxfp4": 48}    # MOE_FORMAT_MX, MOE_FORMAT_MXFP4
+MX_FORMATS = ("mx", "mxfp4")
 
 
 def flags_of(path="auto", routing="topk_softmax", gate_bf16=False, fmt="block128") -> int:
@@ -122,7 +124,7 @@ def _stream(device, stream, *tensors):
 
 def scale_shapes(d, f, E, fmt="block128"):
     """(shape, element bytes) of S_gateup and S_down for a weight format."""
-    if fmt == "mx":
+    if fmt in MX_FORMATS:
         return ((E, d // MX_BLOCK, 2 * f), 1), ((E, f // MX_BLOCK, d), 1)
     if fmt == "block128":
         return ((E, d // BLOCK, 2 * f // BLOCK), 4), ((E, f // BLOCK, d // BLOCK), 4)
@@ -133,7 +135,7 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
           out, workspace, fmt="block128"):
     T, d = x.shape
     E = W_router.shape[1]
-    f = W_down.shape[1]
+    f = W_down.shape[1] * (2 if fmt == "mxfp4" else 1)
     dev = x.device
     if dev.type != "cuda":
         raise ValueError("x must be a GPU tensor")
@@ -141,10 +143,11 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
     _expect(W_router, "W_router", (d, E), 4, dev)
     _expect(b_router, "b_router", (E,), 4, dev)
     (sg_shape, sg_bytes), (sd_shape, sd_bytes) = scale_shapes(d, f, E, fmt)
-    _expect(W_gateup, "W_gateup", (E, d, 2 * f), 1, dev)
+    kp = 2 if fmt == "mxfp4" else 1                  # K rows per stored byte row
+    _expect(W_gateup, "W_gateup", (E, d // kp, 2 * f), 1, dev)
     _expect(S_gateup, "S_gateup", sg_shape, sg_bytes, dev)
     _expect(b_gateup, "b_gateup", (E, 2 * f), 2, dev)
-    _expect(W_down, "W_down", (E, f, d), 1, dev)
+    _expect(W_down, "W_down", (E, f // kp, d), 1, dev)
     _expect(S_down, "S_down", sd_shape, sd_bytes, dev)
     _expect(b_down, "b_down", (E, d), 2, dev)
     if out is None:
@@ -165,11 +168,12 @@ def forward(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_do
     """bf16 [T, d] output of the block; every argument is a device tensor laid
     out as ``include/moe.h`` states (bf16 tensors may be any 2-byte dtype,
     e4m3 and E8M0 tensors any 1-byte dtype).  ``fmt="mx"`` takes MXFP8
-    weights (E8M0 scales per 32 K rows) through ``moe_forward_mx``."""
+    weights (E8M0 scales per 32 K rows) and ``fmt="mxfp4"`` MXFP4 weights (two
+    E2M1 codes per byte along K) through ``moe_forward_mx``."""
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
                              S_down, b_down, out, workspace, fmt)
-    entry = lib().moe_forward_mx if fmt == "mx" else lib().moe_forward_ex
-    _check(entry(*args, flags_of(path, routing, gate_bf16), _stream(x.device, stream, ws, out)))
+    entry = lib().moe_forward_mx if fmt in MX_FORMATS else lib().moe_forward_ex
+    _check(entry(*args, flags_of(path, routing, gate_bf16, fmt), _stream(x.device, stream, ws, out)))
     return out
 
 
@@ -194,7 +198,7 @@ def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down
     activations and h, per-row expert outputs) as a dict of device tensors.
     MX: xs / hs are E8M0 codes [T, d/32] / [T*k, f/32]."""
     T, d = x.shape
-    E, f = W_router.shape[1], W_down.shape[1]
+    E, f = W_router.shape[1], W_down.shape[1] * (2 if fmt == "mxfp4" else 1)
     R = T * k
     dev = x.device
     i32, f32, u8 = torch.int32, torch.float32, torch.uint8
@@ -204,10 +208,10 @@ def forward_debug(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down
                row_token=torch.empty(R, dtype=i32, device=dev),
                row_of=torch.empty((T, k), dtype=i32, device=dev),
                xq=torch.empty((T, d), dtype=u8, device=dev),
-               xs=(torch.empty((T, d // MX_BLOCK), dtype=u8, device=dev) if fmt == "mx"
+               xs=(torch.empty((T, d // MX_BLOCK), dtype=u8, device=dev) if fmt in MX_FORMATS
                    else torch.empty((T, d // BLOCK), dtype=f32, device=dev)),
                hq=torch.empty((R, f), dtype=u8, device=dev),
-               hs=(torch.empty((R, f // MX_BLOCK), dtype=u8, device=dev) if fmt == "mx"
+               hs=(torch.empty((R, f // MX_BLOCK), dtype=u8, device=dev) if fmt in MX_FORMATS
                    else torch.empty((R, f // BLOCK), dtype=f32, device=dev)),
                y=torch.empty((R, d), dtype=f32, device=dev))
     args, out, ws, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
@@ -229,7 +233,7 @@ def device_inputs(inp: dict, device="cuda"):
         return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).to(device)
 
     fmt = inp.get("format", "block128")
-    sdt = torch.uint8 if fmt == "mx" else torch.float32
+    sdt = torch.uint8 if fmt in MX_FORMATS else torch.float32
     return dict(
         x=t(inp["x"], torch.bfloat16), W_router=t(inp["W_router"], torch.float32),
         b_router=t(inp["b_router"], torch.float32), k=int(inp["k"]),
@@ -248,8 +252,8 @@ class MoeBlock:
 
     def workspace(self, T):
         p = self.p
-        need = workspace_bytes(T, p["W_router"].shape[0], p["W_down"].shape[1],
-                               p["W_router"].shape[1], p["k"])
+        f = p["W_down"].shape[1] * (2 if self.fmt == "mxfp4" else 1)
+        need = workspace_bytes(T, p["W_router"].shape[0], f, p["W_router"].shape[1], p["k"])
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(max(need, 1), dtype=torch.uint8, device=p["W_router"].device)
         return self._ws

@@ -107,6 +107,14 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128_mx(v8i a, v8i b, v4f c, int sa
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// A in E2M1 (FP4), B in e4m3, E8M0 scales as above.  Lane l's 16 A bytes
+// (a[0..3]; a[4..7] are ignored) are K 32(l/16)..+31 in order, low nibble
+// first, so its scale covers exactly its own data (measured on gfx950 like
+// the layout above).
+__device__ __forceinline__ v4f mfma_fp4_fp8_16x16x128_mx(v8i a, v8i b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+}
+
 // ----------------------------------------------------------------------------- misc
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 

@@ -74,17 +74,18 @@ constexpr int MX_PITCH = 272;
 // streaming the weights: waves of 16 rows), by 256 B columns (waves of 64)
 // or, for the decode down projection, 128 (waves of 32).  A stage is
 // A [BM][128], B [128][BNP] and the side area: 50 KB for prefill.
-template <int BM, int BNP, bool MX>
+template <int BM, int BNP, bool MX, bool FP4>
 struct DmaShape {
   static constexpr int MB = BM / 32;                 // 16-row blocks per wave
   static constexpr int NB = BNP / 64;                // 16-column blocks per wave
+  static constexpr int KR = FP4 ? kBlock / 2 : kBlock;  // stored weight rows per K block
   static constexpr int SA = BM * kBlock;
-  static constexpr int SB = kBlock * BNP;
+  static constexpr int SB = KR * BNP;
   static constexpr int SS = MX ? SIDE_BS + 4 * MX_PITCH : DMA_SS;
   static constexpr int STAGE = SA + SB + SS;
   static constexpr int A_PER = BM >= 64 ? BM / 64 : 1;        // A chunks (1 KB) per loading wave
   static constexpr int A_WAVES = BM / 8 / A_PER;              // waves that load A
-  static constexpr int B_PER = BNP / 64;                      // B chunks per wave
+  static constexpr int B_PER = SB / 1024 / DMA_WAVES;         // B chunks per wave
   static constexpr int SEGS = BNP / 16;                       // 16-byte segments per K row
   static constexpr int LOADS_MIN = (A_WAVES == DMA_WAVES ? A_PER : 0) + B_PER + 1;  // fewest per wave
   static_assert(BM == 32 || BM == 128, "row tile");
@@ -184,9 +185,11 @@ __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& g, int L) {
   return DmaTile{v[0], v[1], v[2], v[3]};
 }
 
-template <bool GATED, int BM, int BNP, bool MX>
+// FP4 (with MX): E2M1 weights packed two per byte along K, K/2 stored rows.
+template <bool GATED, int BM, int BNP, bool MX, bool FP4>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
-  using S = DmaShape<BM, BNP, MX>;
+  using S = DmaShape<BM, BNP, MX, FP4>;
+  static_assert(MX || !FP4, "FP4 weights come with E8M0 scales");
   static_assert(!GATED || BNP == 256, "gated tiles: 128 gate + 128 up columns");
   static_assert(!MX || BM == 32, "MX decode tiles: one 16-row block per wave");
   constexpr int DMA_SA = S::SA, DMA_SB = S::SB, DMA_STAGE = S::STAGE;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   v4i rB;
   auto setup = [&](const DmaTile& t, int buf) {
     const int n0 = t.nt * (GATED ? kBlock : BNP);
-    rB = dma_rsrc(g.B + (size_t)t.e * K * N, (uint32_t)K * (uint32_t)N);
+    rB = dma_rsrc(g.B + (size_t)t.e * S::KR * nkb * N, (uint32_t)(S::KR * nkb) * (uint32_t)N);
 #pragma unroll
     for (int q = 0; q < S::A_PER; ++q) {  // A: 1 KB chunk c = rows 8c..8c+7; wave w: A_PER chunks
       const int r = 8 * (S::A_PER * wave + q) + (lane >> 3);
@@ -294,7 +297,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // reads): the in-flight count is the same on every path.
   auto issue = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
-    const uint32_t ka = (uint32_t)kbl * kBlock, kb = ka * (uint32_t)N;
+    const uint32_t ka = (uint32_t)kbl * kBlock, kb = (uint32_t)kbl * S::KR * (uint32_t)N;
     if (S::A_WAVES == DMA_WAVES || wave < S::A_WAVES)
 #pragma unroll
       for (int q = 0; q < S::A_PER; ++q)
@@ -383,17 +386,19 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     const v8i xf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      v8i wf;
+      // FP4: two reads, stored rows 16gq + 8r + l16/2 (K 32gq.. in order)
+      v8i wf = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < (FP4 ? 2 : 4); ++r) {
+        const int rr = FP4 ? 8 * r : 64 * (r >> 1) + 8 * (r & 1);
         const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(sB + b_row + (64 * (r >> 1) + 8 * (r & 1)) * BNP +
-                                                     (b_base ^ (16 * b_seg(nb)))));
+            (__attribute__((address_space(3))) v2i*)(sB + b_row + rr * BNP + (b_base ^ (16 * b_seg(nb)))));
         wf[2 * r] = t[0];
         wf[2 * r + 1] = t[1];
       }
       const int ws = wsc[16 * ((GATED ? 2 * wn : NB * wn) + b_seg(nb))];
-      macc[0][nb] = mfma_fp8_16x16x128_mx(wf, xf, macc[0][nb], ws, xsc);
+      if constexpr (FP4) macc[0][nb] = mfma_fp4_fp8_16x16x128_mx(wf, xf, macc[0][nb], ws, xsc);
+      else macc[0][nb] = mfma_fp8_16x16x128_mx(wf, xf, macc[0][nb], ws, xsc);
     }
   };
 
@@ -645,23 +650,26 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 // across tile boundaries (the next tile's first blocks load while the
 // current tile ends).
 constexpr int WM_ROWS = 192, WN_COLS = 256, W_HALF = WM_ROWS / 2;
-constexpr int W_SA = WM_ROWS * kBlock, W_SB = kBlock * WN_COLS, W_SIDE = 2048;
+constexpr int W_SA = WM_ROWS * kBlock, W_SIDE = 2048;
 constexpr int W_ASTAGE = W_SA + W_SIDE;
 constexpr int W_SIDE_BIAS = 1024, W_SIDE_BS = 1536;
 constexpr int W_AQ = W_SA / 1024 / DMA_WAVES;       // A chunks (1 KB) per wave: 3
-constexpr int W_BQ = W_SB / 1024 / DMA_WAVES;       // B chunks per wave: 4
 
-template <bool GATED, bool MX>
+template <bool GATED, bool MX, bool FP4>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(GemmArgs g) {
+  static_assert(MX || !FP4, "FP4 weights come with E8M0 scales");
+  constexpr int KR = FP4 ? kBlock / 2 : kBlock;      // stored weight rows per K block
+  constexpr int SB = KR * WN_COLS;
+  constexpr int BQ = SB / 1024 / DMA_WAVES;          // B chunks (1 KB) per wave
   constexpr int MB = W_HALF / 16, NB = 4;            // 16 x 16 blocks per wave: 6 x 4
   constexpr int RT = GATED ? 1 : 0;                  // row-token loads per A-cursor tile move
   constexpr int ST = GATED ? MB * 3 : MB * NB;       // epilogue stores per wave
   constexpr int ASTAGE = MX ? W_SA + W_SIDE_BS + 4 * MX_PITCH : W_ASTAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[ASTAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb0[W_SB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb1[W_SB];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb2[W_SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[SB];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb2[SB];
   __shared__ float smax[(GATED && !MX) ? 4 * WM_ROWS : 1];  // row maxima per wave column
   __shared__ int32_t rtok[GATED ? 2 : 1][GATED ? DMA_WAVES * 64 : 1];
 
@@ -700,7 +708,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   // ---- B cursor (weights, two K blocks ahead of compute)
   int Lb = L0, kbb = 0;
   DmaTile tb = ta;
-  uint32_t boff[W_BQ];
+  uint32_t boff[BQ];
   v4i rB;
 
   auto rt_load = [&](const DmaTile& t, bool live, int buf) {
@@ -747,10 +755,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   };
   auto setup_b = [&](const DmaTile& t) {
     const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
-    rB = dma_rsrc(g.B + (size_t)t.e * K * N, (uint32_t)K * (uint32_t)N);
+    rB = dma_rsrc(g.B + (size_t)t.e * KR * nkb * N, (uint32_t)(KR * nkb) * (uint32_t)N);
 #pragma unroll
-    for (int q = 0; q < W_BQ; ++q) {  // chunk W_BQ wave + q: K rows 4 chunk + lane / 16
-      const int kr = 4 * (W_BQ * wave + q) + (lane >> 4);
+    for (int q = 0; q < BQ; ++q) {  // chunk BQ wave + q: stored rows 4 chunk + lane / 16
+      const int kr = 4 * (BQ * wave + q) + (lane >> 4);
       const int s = (lane & 15) ^ swz_b<16, MX>(kr);
       const int gc = GATED ? (s < 8 ? n0 + 16 * s : g.f + n0 + 16 * (s - 8)) : n0 + 16 * s;
       boff[q] = gc < N ? (uint32_t)kr * (uint32_t)N + (uint32_t)gc : kOob;
@@ -773,7 +781,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     if (MX && (wave == 4 || wave == 5)) dma4(rBias, sbase + W_SA + W_SIDE_BIAS + 256 * (wave - 4), soff2);
   };
   auto b_load = [&](uint32_t sbase, int q) {
-    dma16(rB, sbase + (W_BQ * wave + q) * 1024, boff[q] + (uint32_t)kbb * kBlock * (uint32_t)N);
+    dma16(rB, sbase + (BQ * wave + q) * 1024, boff[q] + (uint32_t)kbb * KR * (uint32_t)N);
   };
   auto issue_a = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
@@ -785,7 +793,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   auto issue_b = [&](uint8_t* base) {
     const uint32_t sbase = lds_addr(base);
 #pragma unroll
-    for (int q = 0; q < W_BQ; ++q) b_load(sbase, q);
+    for (int q = 0; q < BQ; ++q) b_load(sbase, q);
     ++kbb;
   };
   // Cursor moves after a tile's last K block has been issued.
@@ -798,7 +806,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       setup_b(tb);
     } else {
 #pragma unroll
-      for (int q = 0; q < W_BQ; ++q) boff[q] = kOob;
+      for (int q = 0; q < BQ; ++q) boff[q] = kOob;
     }
   };
   auto advance_a = [&]() -> int {
@@ -873,11 +881,12 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       wsv[nb] = wsc[16 * b_tseg(nb)];
+      wf[nb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < (FP4 ? 2 : 4); ++r) {  // FP4: stored rows 16gq + 8r + l16/2
+        const int rr = FP4 ? 8 * r : 64 * (r >> 1) + 8 * (r & 1);
         const v2i t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i*)(bbase + b_off(nb) +
-                                                     (64 * (r >> 1) + 8 * (r & 1)) * WN_COLS));
+            (__attribute__((address_space(3))) v2i*)(bbase + b_off(nb) + rr * WN_COLS));
         wf[nb][2 * r] = t[0];
         wf[nb][2 * r + 1] = t[1];
       }
@@ -890,7 +899,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       const v8i xf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        macc[mb][nb] = mfma_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
+        if constexpr (FP4) macc[mb][nb] = mfma_fp4_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
+        else macc[mb][nb] = mfma_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
       }
     }
   };
@@ -1076,13 +1086,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   };
 
   // Ring wait: this wave's loads of the A stage about to be read (and, older,
-  // of the B stage) are done; younger are the next B stage's W_BQ loads and
+  // of the B stage) are done; younger are the next B stage's BQ loads and
   // `pend` row-token loads and epilogue stores.  Then a bare s_barrier.
   auto wait_stage = [&](int pend) {
-    if (pend == 0) wait_vmcnt<W_BQ>();
-    else if (pend == RT) wait_vmcnt<W_BQ + RT>();
-    else if (pend == ST) wait_vmcnt<W_BQ + ST>();
-    else if (pend == RT + ST) wait_vmcnt<W_BQ + RT + ST>();
+    if (pend == 0) wait_vmcnt<BQ>();
+    else if (pend == RT) wait_vmcnt<BQ + RT>();
+    else if (pend == ST) wait_vmcnt<BQ + ST>();
+    else if (pend == RT + ST) wait_vmcnt<BQ + RT + ST>();
     else wait_vmcnt<0>();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -1149,40 +1159,40 @@ int grid_persistent(int max_tiles) {
   return std::min(cus[dev], grid_for(max_tiles));
 }
 
-}  // namespace
-
-hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, bool mx, int max_tiles,
-                             hipStream_t stream) {
+template <bool GATED, int DBM, int DBN>
+hipError_t launch_gemm(const GemmArgs& a, bool decode, int fmt, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
-  static_assert(kGatedPrefill.bm == WM_ROWS && kGatedPrefill.bnp == WN_COLS, "wide tile");
-  constexpr int DBM = kGatedDecode.bm, DBN = kGatedDecode.bnp;
-  if (decode && mx)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, DBM, DBN, true>), grid, block, 0, stream, a);
-  else if (decode)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<true, DBM, DBN, false>), grid, block, 0, stream, a);
-  else if (mx)
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<true, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<true, false>), grid, block, 0, stream, a);
+  if (decode) {
+    if (fmt == kFmtMxFp4)
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, true>), grid, block, 0, stream, a);
+    else if (fmt == kFmtMx)
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, false, false>), grid, block, 0, stream, a);
+  } else {
+    if (fmt == kFmtMxFp4)
+      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, true>), grid, block, 0, stream, a);
+    else if (fmt == kFmtMx)
+      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, false, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+}  // namespace
+
+hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int fmt, int max_tiles,
                              hipStream_t stream) {
-  if (max_tiles <= 0) return hipSuccess;
-  const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
+  static_assert(kGatedPrefill.bm == WM_ROWS && kGatedPrefill.bnp == WN_COLS, "wide tile");
+  return launch_gemm<true, kGatedDecode.bm, kGatedDecode.bnp>(a, decode, fmt, max_tiles, stream);
+}
+
+hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int fmt, int max_tiles,
+                             hipStream_t stream) {
   static_assert(kPlainPrefill.bm == WM_ROWS && kPlainPrefill.bnp == WN_COLS, "wide tile");
-  constexpr int DBM = kPlainDecode.bm, DBN = kPlainDecode.bnp;
-  if (decode && mx)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, DBM, DBN, true>), grid, block, 0, stream, a);
-  else if (decode)
-    hipLaunchKernelGGL((grouped_gemm_dma_kernel<false, DBM, DBN, false>), grid, block, 0, stream, a);
-  else if (mx)
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<false, true>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((grouped_gemm_wide_kernel<false, false>), grid, block, 0, stream, a);
-  return hipGetLastError();
+  return launch_gemm<false, kPlainDecode.bm, kPlainDecode.bnp>(a, decode, fmt, max_tiles, stream);
 }
 
 }  // namespace moe

@@ -30,7 +30,7 @@ struct GemmArgs {
   const uint8_t* A;            // e4m3 activations: x codes [T,K] (gated) or h codes [R,K] (plain)
   const void* As;              // their scales
   const int32_t* row_token;    // gated: token of each permuted row
-  const uint8_t* B;            // e4m3 weights [E, K, N]
+  const uint8_t* B;            // weights [E, K, N] e4m3 (FP4: [E, K/2, N], two E2M1 per byte)
   const void* Bs;              // weight scales
   const uint16_t* bias;        // bf16 [E, N]
   const int32_t* counts;       // rows per expert [E]
@@ -87,11 +87,15 @@ hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base,
 hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
                           int k, uint16_t* out, hipStream_t stream);
 
-// max_tiles bounds the tile count so the grid covers every tile; mx selects
-// the MXFP8 kernels (E8M0 scales applied by the matrix cores).
-hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+// Weight formats of the grouped GEMMs: 128x128 block-scaled FP8, MXFP8 (E8M0
+// scales applied by the matrix cores), MXFP4 (E2M1 weights packed two per
+// byte along K with E8M0 scales, MXFP8 activations).
+constexpr int kFmtBlock = 0, kFmtMx = 1, kFmtMxFp4 = 2;
+
+// max_tiles bounds the tile count so the grid covers every tile.
+hipError_t launch_gemm_gated(const GemmArgs& a, bool decode, int fmt, int max_tiles,
                              hipStream_t stream);
-hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, bool mx, int max_tiles,
+hipError_t launch_gemm_plain(const GemmArgs& a, bool decode, int fmt, int max_tiles,
                              hipStream_t stream);
 
 }  // namespace moe

@@ -103,11 +103,14 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                               int32_t first_stage, int32_t last_stage, void* stream_) {
   const moe_status sz = check_sizes(T, d, f, E, k);
   if (sz != MOE_OK) return sz;
-  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX)) != 0u ||
-      (flags & MOE_PATH_MASK) == MOE_PATH_MASK)
+  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX |
+                 MOE_WEIGHTS_FP4)) != 0u ||
+      (flags & MOE_PATH_MASK) == MOE_PATH_MASK ||
+      ((flags & MOE_WEIGHTS_FP4) != 0u && (flags & MOE_FORMAT_MX) == 0u))
     return MOE_ERR_FLAGS;
   const uint32_t path = flags & MOE_PATH_MASK;
   const bool mx = (flags & MOE_FORMAT_MX) != 0u;
+  const int fmt = (flags & MOE_WEIGHTS_FP4) ? moe::kFmtMxFp4 : mx ? moe::kFmtMx : moe::kFmtBlock;
   const int gate_mode = ((flags & MOE_ROUTE_SOFTMAX_ALL) ? moe::kGateSoftmaxAll : 0) |
                         ((flags & MOE_GATE_BF16) ? moe::kGateBf16 : 0);
   if (first_stage < 0 || last_stage >= MOE_NUM_STAGES || first_stage > last_stage)
@@ -208,7 +211,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.Hs = hs;
         g.A_bytes = (int)((int64_t)T * d);
         g.As_bytes = (int)(4 * (int64_t)T * (d / moe::kBlock));
-        err = moe::launch_gemm_gated(g, decode, mx, max_g, stream);
+        err = moe::launch_gemm_gated(g, decode, fmt, max_g, stream);
         break;
       }
       case MOE_STAGE_DOWN: {
@@ -232,7 +235,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.Y = y;
         p.A_bytes = (int)((int64_t)R * f);
         p.As_bytes = (int)(4 * (int64_t)R * (f / moe::kBlock));
-        err = moe::launch_gemm_plain(p, decode, mx, max_p, stream);
+        err = moe::launch_gemm_plain(p, decode, fmt, max_p, stream);
         break;
       }
       case MOE_STAGE_COMBINE:

@@ -132,7 +132,7 @@ def check_h_decisions(dbg: dict, ref: dict, fmt: str = "block128"):
         rows = it["rows"]
         h = it["h"]
         qg = codecs.e4m3_decode(hq[rows])
-        if fmt == "mx":
+        if fmt in ("mx", "mxfp4"):
             amax = np.abs(h).reshape(len(rows), -1, 32).max(axis=2)
             lo = orc.mx_scale_exponent(amax * (1 - H_SCALE_RTOL)) + 127
             hi = orc.mx_scale_exponent(amax * (1 + H_SCALE_RTOL)) + 127

@@ -73,7 +73,7 @@ def call(T=64, d=256, f=256, E=8, k=2, ws=None, flags=0, null=None, misalign=Non
     (dict(d=0), ERR_SHAPE), (dict(k=0), ERR_UNSUP), (dict(k=9, E=16), ERR_UNSUP),
     (dict(k=5, E=4), ERR_UNSUP), (dict(E=257), ERR_UNSUP), (dict(T=1 << 27, k=4), ERR_UNSUP),
     (dict(d=8320), ERR_UNSUP), (dict(f=8320), ERR_UNSUP), (dict(T=1 << 20, d=4096, k=1), ERR_UNSUP),
-    (dict(flags=3), ERR_FLAGS), (dict(flags=32), ERR_FLAGS), (dict(flags=3 | 4), ERR_FLAGS),
+    (dict(flags=3), ERR_FLAGS), (dict(flags=32), ERR_FLAGS), (dict(flags=64), ERR_FLAGS), (dict(flags=3 | 4), ERR_FLAGS),
     (dict(flags=1 << 31), ERR_FLAGS), (dict(ws=100), ERR_WS), (dict(null=0), ERR_NULL),
     (dict(null=9), ERR_NULL), (dict(null=10), ERR_NULL), (dict(misalign=3), ERR_ALIGN),
     (dict(misalign=0), ERR_ALIGN), (dict(stages=(3, 2)), ERR_FLAGS), (dict(stages=(0, 6)), ERR_FLAGS),
@@ -94,7 +94,7 @@ def test_gate_options_are_accepted_flags():
 
 def test_mx_format_flag_and_entry():
     # MOE_FORMAT_MX is a valid bit on every entry; moe_forward_mx checks like moe_forward_ex
-    for fl in (16, 16 | 1, 16 | 2 | 4 | 8):
+    for fl in (16, 16 | 1, 16 | 2 | 4 | 8, 48, 48 | 2):
         assert call(T=0, null=0, flags=fl) == OK
         assert call(T=0, null=0, flags=fl, stages=(0, 5)) == OK
     assert call(T=0, null=0, entry="mx") == OK
@@ -104,6 +104,8 @@ def test_mx_format_flag_and_entry():
     assert call(flags=3, entry="mx") == ERR_FLAGS
     assert call(ws=100, entry="mx") == ERR_WS
     assert moe.flags_of("prefill", fmt="mx") == 1 | 16
+    assert moe.flags_of("decode", fmt="mxfp4") == 2 | 16 | 32
+    assert call(T=0, null=0, entry="mx", flags=32) == OK          # FP4 bit: MX is implied by the entry
     assert moe.scale_shapes(256, 384, 8, "mx") == (((8, 8, 768), 1), ((8, 12, 256), 1))
     with pytest.raises(KeyError):
         moe.flags_of(fmt="nvfp4")

@@ -1,8 +1,8 @@
 """HIP path vs the CPU oracle, element by element, through the C ABI (GPU only).
 
 Small cases run the oracle on every token and cover both GEMM paths (large
-row tiles and small row tiles) and both weight formats (128x128 block-scaled
-and MXFP8), ragged expert tails, padded hidden sizes, column tails, k = 1,
+row tiles and small row tiles) and the three weight formats (128x128
+block-scaled FP8, MXFP8, MXFP4), ragged expert tails, padded hidden sizes, column tails, k = 1,
 k = E and E = 256, k = 8.  Full-size workloads check the
 routing, permutation and x quantisation on every token and the expert rows
 and outputs on a seeded sample of tokens, in the launch configuration the
@@ -35,7 +35,7 @@ def run_debug(inp, path):
     return dbg
 
 
-FMTS = ["block128", "mx"]
+FMTS = ["block128", "mx", "mxfp4"]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -53,7 +53,7 @@ def test_handworked_block(k, path, fmt):
     xq = dbg["xq"].cpu().numpy()[0]
     assert xq[0] == 0x7E and xq[1] == 0x76 and np.all(xq[2:] == 0)
     xs = dbg["xs"].cpu().numpy()[0]
-    if fmt == "mx":
+    if fmt != "block128":
         assert xs[0] == 127 - 7 and np.all(xs[1:] == 0)       # 2^-7, then all-zero blocks
     else:
         assert xs[0] == 2.0 ** -7
@@ -170,7 +170,7 @@ def test_empty_batch_and_stage_split():
 
 
 FULL = [(c, "block128") for c in ["c1", "c2", "c3", "c4a", "c4b"]] + \
-       [(c, "mx") for c in ["c1", "c2", "c4b"]]
+       [(c, "mx") for c in ["c1", "c2", "c4b"]] + [(c, "mxfp4") for c in ["c1", "c2", "c4a"]]
 
 
 @pytest.mark.timeout(900)
