@@ -45,18 +45,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
-           "fetch_kib": 271903.450, "write_kib": 765.163,
-           "copy_fetch_kib": 524311.6875, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
-           "fetch_kib": 872689.162, "write_kib": 103987.106,
-           "copy_fetch_kib": 524306.625, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
-              "fetch_kib": 280254.938, "write_kib": 765.112,
-              "copy_fetch_kib": 524307.375, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "2c9ac7d6b4ffc1252ee5f71f2dcb2f4edbfb2e765b2730f2b2dfdd757142d21d",
-              "fetch_kib": 952815.550, "write_kib": 103731.919,
-              "copy_fetch_kib": 524307.75, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 271898.888, "write_kib": 765.125,
+        "copy_fetch_kib": 524310.6875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 884534.600, "write_kib": 104047.631,
+        "copy_fetch_kib": 524314.125, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 280253.037, "write_kib": 765.106,
+        "copy_fetch_kib": 524306.3125, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 949854.062, "write_kib": 103639.875,
+        "copy_fetch_kib": 524314.5625, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 144735.250, "write_kib": 765.094,
+        "copy_fetch_kib": 524312.625, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "1df603dbc629d801b9d44283ee02a8c3b8772ed7ec110f078988aa57f3f37339",
+        "fetch_kib": 583062.775, "write_kib": 103704.169,
+        "copy_fetch_kib": 524306.8125, "copy_write_kib": 1048576.0},
 }
 
 
