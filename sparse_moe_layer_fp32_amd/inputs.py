@@ -345,3 +345,49 @@ def digest(inputs: dict) -> dict:
     """SHA-256 of every array in an input set (for reproducibility records)."""
     return {k: hashlib.sha256(np.ascontiguousarray(v).tobytes()).hexdigest()
             for k, v in sorted(inputs.items()) if isinstance(v, np.ndarray)}
+
+
+# ----------------------------------------------------------------------------- attention with sinks
+_T_AQ, _T_AK, _T_AV, _T_ASINK, _T_ALEN = range(20, 25)
+
+
+@dataclass(frozen=True)
+class AttnShape:
+    """GQA attention shape: query heads, key/value heads, head dim."""
+    name: str
+    Hq: int
+    Hkv: int
+    D: int = 64
+
+
+GPT_OSS_ATTN = AttnShape("gpt-oss-like", 64, 8, 64)
+
+
+def attn_sinks(shape: AttnShape, seed: int = 0) -> np.ndarray:
+    """Per-head sink logits, fp32 ~ N(0, 1) (learned values of a few units)."""
+    return (_rng(seed, _T_ASINK, shape.Hq).standard_normal(shape.Hq, dtype=np.float32)).astype(np.float32)
+
+
+def make_attn_prefill(shape: AttnShape, S: int, seed: int = 0) -> dict:
+    """One sequence: q [S, Hq, D], k and v [S, Hkv, D] (bf16 bits, token major),
+    sinks [Hq] fp32, sm_scale = 1/sqrt(D).  q, k ~ N(0, 1), v ~ N(0, 1)."""
+    r = lambda t, shp: to_bf16_bits(_rng(seed, t, S, shape.Hq).standard_normal(shp, dtype=np.float32))
+    return dict(kind="prefill", S=S, Hq=shape.Hq, Hkv=shape.Hkv, D=shape.D,
+                q=r(_T_AQ, (S, shape.Hq, shape.D)), k=r(_T_AK, (S, shape.Hkv, shape.D)),
+                v=r(_T_AV, (S, shape.Hkv, shape.D)), sinks=attn_sinks(shape, seed),
+                sm_scale=float(1.0 / np.sqrt(shape.D)))
+
+
+def make_attn_decode(shape: AttnShape, B: int, Lmax: int, seed: int = 0, ragged: bool = True) -> dict:
+    """B sequences, one query each: q [B, Hq, D]; caches [B, Hkv, Lmax, D]
+    (heads major, tokens contiguous); kv_len [B] in [1, Lmax] (uniform over
+    [Lmax/2, Lmax] when ragged, else Lmax)."""
+    r = lambda t, shp: to_bf16_bits(_rng(seed, t, B, Lmax).standard_normal(shp, dtype=np.float32))
+    if ragged:
+        kv_len = _rng(seed, _T_ALEN, B, Lmax).integers(max(1, Lmax // 2), Lmax + 1, size=B).astype(np.int32)
+    else:
+        kv_len = np.full(B, Lmax, np.int32)
+    return dict(kind="decode", B=B, Lmax=Lmax, Hq=shape.Hq, Hkv=shape.Hkv, D=shape.D,
+                q=r(_T_AQ, (B, shape.Hq, shape.D)), k=r(_T_AK, (B, shape.Hkv, Lmax, shape.D)),
+                v=r(_T_AV, (B, shape.Hkv, Lmax, shape.D)), kv_len=kv_len, sinks=attn_sinks(shape, seed),
+                sm_scale=float(1.0 / np.sqrt(shape.D)))
