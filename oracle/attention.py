@@ -37,19 +37,21 @@ def sink_softmax_attend(s: np.ndarray, sink: float, v: np.ndarray) -> np.ndarray
     return (p @ np.asarray(v, np.float64)) / denom
 
 
-def prefill(q_bits, k_bits, v_bits, sinks, sm_scale):
+def prefill(q_bits, k_bits, v_bits, sinks, sm_scale, rows=None):
     """Causal GQA prefill of one sequence.  q [S, Hq, D], k and v [S, Hkv, D]
-    as bf16 bits, sinks [Hq] fp32 -> out [S, Hq, D] fp64."""
+    as bf16 bits, sinks [Hq] fp32 -> out [len(rows), Hq, D] fp64 for the
+    query positions ``rows`` (default: all S)."""
     q, k, v = bf16_decode(q_bits), bf16_decode(k_bits), bf16_decode(v_bits)
     S, Hq, D = q.shape
     Hkv = k.shape[1]
     G = Hq // Hkv
-    out = np.zeros((S, Hq, D))
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), Hq, D))
     for h in range(Hq):
         kh, vh = k[:, h // G], v[:, h // G]
-        scores = (q[:, h] @ kh.T) * float(sm_scale)         # [S, S]
-        for i in range(S):
-            out[i, h] = sink_softmax_attend(scores[i, :i + 1], float(sinks[h]), vh[:i + 1])
+        scores = (q[rows, h] @ kh.T) * float(sm_scale)      # [rows, S]
+        for n, i in enumerate(rows):
+            out[n, h] = sink_softmax_attend(scores[n, :i + 1], float(sinks[h]), vh[:i + 1])
     return out
 
 

@@ -36,7 +36,8 @@ MAX_EXPERTS = 256
 MAX_TOPK = 8
 
 SYMBOLS = ("moe_workspace_bytes", "moe_forward", "moe_forward_ex", "moe_forward_mx",
-           "moe_forward_stages", "moe_forward_debug", "moe_status_string")
+           "moe_forward_stages", "moe_forward_debug", "moe_status_string",
+           "attn_sink_prefill", "attn_sink_decode_workspace_bytes", "attn_sink_decode")
 STAGES = {"router": 0, "scan": 1, "place": 2, "gateup": 3, "down": 4, "combine": 5}
 
 
@@ -76,6 +77,13 @@ def lib() -> ctypes.CDLL:
     L.moe_forward_debug.argtypes = fwd + [U, P] + [P] * 10
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [I]
+    F = ctypes.c_float
+    L.attn_sink_prefill.restype = I
+    L.attn_sink_prefill.argtypes = [P, P, P, P, P, I, I, I, I, F, P]
+    L.attn_sink_decode_workspace_bytes.restype = S
+    L.attn_sink_decode_workspace_bytes.argtypes = [I, I, I]
+    L.attn_sink_decode.restype = I
+    L.attn_sink_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, P, S, P]
     _lib = L
     return L
 
@@ -264,3 +272,68 @@ class MoeBlock:
                        p["b_gateup"], p["W_down"], p["S_down"], p["b_down"], out=out,
                        workspace=self.workspace(x.shape[0]), path=path, stream=stream,
                        routing=routing, gate_bf16=gate_bf16, fmt=self.fmt)
+
+
+# ----------------------------------------------------------------------------- attention with sinks
+def attn_prefill(q, k, v, sinks, sm_scale=None, out=None, stream=None):
+    """Causal GQA attention with per-head sinks over one sequence
+    (``include/attention.h``): q [S, Hq, D], k and v [S, Hkv, D] (2-byte
+    dtypes, bf16 bits), sinks [Hq] fp32 -> out [S, Hq, D] bf16."""
+    S, Hq, D = q.shape
+    Hkv = k.shape[1]
+    dev = q.device
+    _expect(q, "q", (S, Hq, D), 2, dev)
+    _expect(k, "k", (S, Hkv, D), 2, dev)
+    _expect(v, "v", (S, Hkv, D), 2, dev)
+    _expect(sinks, "sinks", (Hq,), 4, dev)
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", (S, Hq, D), 2, dev)
+    scale = float(1.0 / D ** 0.5 if sm_scale is None else sm_scale)
+    _check(lib().attn_sink_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(out), S, Hq, Hkv, D,
+                                   scale, _stream(dev, stream, out)))
+    return out
+
+
+def attn_decode_workspace_bytes(B, Hq, Lmax) -> int:
+    return int(lib().attn_sink_decode_workspace_bytes(B, Hq, Lmax))
+
+
+def attn_decode(q, k_cache, v_cache, kv_len, sinks, sm_scale=None, out=None, workspace=None,
+                stream=None):
+    """One query per sequence over an HND KV cache: q [B, Hq, D], caches
+    [B, Hkv, Lmax, D], kv_len [B] int32, sinks [Hq] fp32 -> out [B, Hq, D] bf16."""
+    B, Hq, D = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    dev = q.device
+    _expect(q, "q", (B, Hq, D), 2, dev)
+    _expect(k_cache, "k_cache", (B, Hkv, Lmax, D), 2, dev)
+    _expect(v_cache, "v_cache", (B, Hkv, Lmax, D), 2, dev)
+    _expect(kv_len, "kv_len", (B,), 4, dev)
+    _expect(sinks, "sinks", (Hq,), 4, dev)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _expect(out, "out", (B, Hq, D), 2, dev)
+    need = attn_decode_workspace_bytes(B, Hq, Lmax)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    scale = float(1.0 / D ** 0.5 if sm_scale is None else sm_scale)
+    _check(lib().attn_sink_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(sinks),
+                                  _ptr(out), B, Hq, Hkv, D, Lmax, scale, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream(dev, stream, out, workspace)))
+    return out
+
+
+def attn_device_inputs(inp: dict, device="cuda"):
+    """Host arrays of ``inputs.make_attn_prefill`` / ``make_attn_decode`` -> device tensors."""
+    import numpy as np
+
+    def t(a, dtype):
+        return torch.from_numpy(np.ascontiguousarray(a)).view(dtype).to(device)
+
+    d = dict(q=t(inp["q"], torch.bfloat16), k=t(inp["k"], torch.bfloat16), v=t(inp["v"], torch.bfloat16),
+             sinks=t(inp["sinks"], torch.float32), sm_scale=inp["sm_scale"])
+    if "kv_len" in inp:
+        d["kv_len"] = t(inp["kv_len"], torch.int32)
+    return d

@@ -1,0 +1,404 @@
+// GQA attention with per-head sinks on the gfx950 matrix cores.
+//
+// "GPT-OSS on day 0", section "Sink attention": every head has a learned sink
+// value that joins the scaled scores inside the softmax; the softmax runs
+// online (the max-subtracted form, with the running maximum seeded by the
+// sink and the running sum by its term), and when the keys are split into
+// several parts the sink must be counted in the first part only.  Section
+// "GPT-OSS on Hopper": the attention is GQA.  The sink has no value vector:
+// it only adds exp(sink - M) to the denominator.
+//
+// Both kernels compute S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (keys are
+// the MFMA rows, queries its columns), so a query's scores sit in one lane
+// column: lane (l16, g) holds keys 4g..4g+3 of every 16-key tile for query
+// l16, and the softmax reductions are in-lane plus two shuffles.  P stays in
+// registers as the B operand of O^T = V^T P^T: for 32 keys 32p.. the lane's
+// eight values are keys 32p + 4g + j and 32p + 16 + 4g + j (j < 4), and the
+// matching A operand (V^T) comes from two ds_read_b64_tr_b16 reads of V rows
+// 32p + 4g.. and 32p + 16 + 4g.. (lane i of a 16-lane group receives column
+// i of the four rows its group addressed).  Scores are scaled by
+// sm_scale * log2(e) and exponentiated with exp2.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "attention.hpp"
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int AD = 64;          // head dim
+constexpr int ABK = 64;         // keys per block
+constexpr int APITCH = 144;     // LDS bytes per key row (128 + 16: rows on distinct banks)
+constexpr float kLog2e = 1.44269504088896341f;
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4f mfma_bf16(uint4 a, uint4 b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b),
+                                                 c, 0, 0, 0);
+}
+
+// two fp32 -> packed bf16 pair (round to nearest even), low half first
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+__device__ __forceinline__ uint2 tr16(const uint8_t* p) {
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// ---------------------------------------------------------------------------
+// Prefill: one workgroup = HW query heads sharing one key/value head times
+// 64 * (8 / HW) query rows; wave w owns head h0 + w % HW and 64 rows.  The
+// K and V blocks of 64 keys go through LDS once for all eight waves (double
+// buffered: the next block is loaded to registers while the current one is
+// used).  Causal: a block is used by the waves whose rows reach it; the
+// block on the diagonal masks key > query.
+template <int HW>
+__global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ k,
+                                                           const uint16_t* __restrict__ v,
+                                                           const float* __restrict__ sinks,
+                                                           uint16_t* __restrict__ out, int S, int Hq,
+                                                           int Hkv, float scale2) {
+  constexpr int QB = 64 * (8 / HW);                  // query rows per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t kl[2][ABK * APITCH];
+  __shared__ __attribute__((aligned(16))) uint8_t vl[2][ABK * APITCH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int G = Hq / Hkv;
+  const int qb = gridDim.x - 1 - blockIdx.x;        // longest (last) query blocks first
+  const int h0 = blockIdx.y * HW;
+  const int kvh = h0 / G;
+  const int h = h0 + wave % HW;
+  const int row0 = qb * QB + 64 * (wave / HW);      // this wave's first query row
+  const int wg_last = min(S, (qb + 1) * QB) - 1;    // last query row of the workgroup
+  const int nblk = wg_last / ABK + 1;               // key blocks the workgroup needs
+
+  // Q^T fragments (B operand): query row0 + 16 qt + l16, dims 32 c + 8 g .. + 7
+  uint4 qf[4][2];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const int r = row0 + 16 * qt + l16;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      qf[qt][c] = r < S ? *reinterpret_cast<const uint4*>(q + ((size_t)r * Hq + h) * AD + 32 * c + 8 * g)
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // running max (log2 domain) per query column, per-lane partial sums, O^T
+  float m[4], l[4];
+  v4f o[4][4];  // [dt][qt]: dims 16 dt + 4 g + i, query 16 qt + l16
+  const float sink2 = sinks[h] * kLog2e;
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    m[qt] = sink2;                 // the sink seeds the running maximum ...
+    l[qt] = g == 0 ? 1.0f : 0.0f;  // ... and contributes exp2(0) = 1 to the sum (once per query)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // block loader: thread t moves 16 bytes of K and of V (key t / 8, bytes 16 (t % 8))
+  const int lkey = tid >> 3, lchunk = tid & 7;
+  uint4 kr, vr;
+  auto load = [&](int kb) {
+    const int key = kb * ABK + lkey;
+    if (key < S) {
+      const size_t off = ((size_t)key * Hkv + kvh) * AD + 8 * lchunk;
+      kr = *reinterpret_cast<const uint4*>(k + off);
+      vr = *reinterpret_cast<const uint4*>(v + off);
+    } else {
+      kr = vr = make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store = [&](int buf) {
+    *reinterpret_cast<uint4*>(&kl[buf][lkey * APITCH + 16 * lchunk]) = kr;
+    *reinterpret_cast<uint4*>(&vl[buf][lkey * APITCH + 16 * lchunk]) = vr;
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int buf = kb & 1;
+    if (kb + 1 < nblk) load(kb + 1);
+    const int key0 = kb * ABK;
+    if (key0 <= row0 + 63 && row0 < S) {  // some of this wave's rows see the block
+      const uint8_t* kb_l = kl[buf];
+      const uint8_t* vb_l = vl[buf];
+      // two 32-key halves, each its own online-softmax step (fewer live scores)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int kh0 = key0 + 32 * p;
+        if (kh0 > row0 + 63) break;  // the wave's rows see none of this half
+        // S^T tiles: keys kh0 + 16 kt + 4 g + i, query 16 qt + l16
+        v4f s[2][4];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const uint8_t* pk = kb_l + (32 * p + 16 * kt + l16) * APITCH + 16 * g;
+          const uint4 a0 = *reinterpret_cast<const uint4*>(pk);
+          const uint4 a1 = *reinterpret_cast<const uint4*>(pk + 64);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) {
+            s[kt][qt] = mfma_bf16(a0, qf[qt][0], v4f{0.f, 0.f, 0.f, 0.f});
+            s[kt][qt] = mfma_bf16(a1, qf[qt][1], s[kt][qt]);
+          }
+        }
+        const bool diag = kh0 + 31 > row0;  // the half reaches past the wave's first row
+        uint4 pb[4];
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          const int qi = row0 + 16 * qt + l16;
+          float bm = -INFINITY;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float x = s[kt][qt][i] * scale2;
+              if (diag && kh0 + 16 * kt + 4 * g + i > qi) x = -INFINITY;
+              s[kt][qt][i] = x;
+              bm = fmaxf(bm, x);
+            }
+          bm = fmaxf(bm, __shfl_xor(bm, 16));
+          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          const float mn = fmaxf(m[qt], bm);
+          const float alpha = exp2f(m[qt] - mn);
+          m[qt] = mn;
+          float pr[2][4];
+          float sum = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pr[kt][i] = exp2f(s[kt][qt][i] - mn);
+              sum += pr[kt][i];
+            }
+          l[qt] = l[qt] * alpha + sum;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+          // B operand of the PV MFMA: keys kh0 + 4 g + j, then kh0 + 16 + 4 g + j
+          pb[qt] = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
+                              pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
+        }
+        // O^T += V^T P^T: lanes of group g address key rows 32p + 4g + i/4 (and +16),
+        // dims 16 dt + 4 (i % 4)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const uint8_t* pv = vb_l + (32 * p + 4 * g + (l16 >> 2)) * APITCH + 2 * (16 * dt + 4 * (l16 & 3));
+          const uint2 lo = tr16(pv);
+          const uint2 hi = tr16(pv + 16 * APITCH);
+          const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt) o[dt][qt] = mfma_bf16(a, pb[qt], o[dt][qt]);
+        }
+      }
+    }
+    if (kb + 1 < nblk) {
+      // buffer buf ^ 1 was last read for block kb - 1, before the previous barrier
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // out[query][h][d] = O^T[d][query] / sum; the four lanes of a query hold partial sums
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    float lt = l[qt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int r = row0 + 16 * qt + l16;
+    if (r >= S) continue;
+    uint16_t* po = out + ((size_t)r * Hq + h) * AD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<uint2*>(po + 16 * dt) =
+          make_uint2(pack_bf16(o[dt][qt][0] * inv, o[dt][qt][1] * inv),
+                     pack_bf16(o[dt][qt][2] * inv, o[dt][qt][3] * inv));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode: one wave per (sequence b, key/value head, split of kSplitKeys keys);
+// its G <= 16 query heads form the 16 MFMA columns (the rest are zero).  K
+// fragments come straight from the cache (a lane reads 16 bytes of one key
+// row); each 64-key block of V is staged in the wave's own LDS slice for the
+// transposing reads.  The split's running max, partial sum and O go to the
+// workspace; split 0 starts from the sink (max = sink, sum = 1), the others
+// from an empty softmax (max = -inf, sum = 0).
+__global__ __launch_bounds__(256) void attn_decode_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ kv_len, const float* __restrict__ sinks, float* __restrict__ part,
+    int B, int Hq, int Hkv, int Lmax, int nsplit, float scale2) {
+  __shared__ __attribute__((aligned(16))) uint8_t vl[4][ABK * APITCH];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int unit = blockIdx.x * 4 + wave;           // (b, kvh, split), split fastest
+  const int split = unit % nsplit;
+  const int kvh = (unit / nsplit) % Hkv;
+  const int b = unit / (nsplit * Hkv);
+  if (b >= B) return;
+  const int G = Hq / Hkv;
+  const int n = min(max(kv_len[b], 0), Lmax);      // lengths outside [0, Lmax] are clamped
+  const int k0 = split * kSplitKeys, k1 = min(n, k0 + kSplitKeys);
+  const int h = kvh * G + l16;                      // query head of column l16
+  const bool hv = l16 < G;
+
+  uint4 qf[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+    qf[c] = hv ? *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h) * AD + 32 * c + 8 * g)
+               : make_uint4(0u, 0u, 0u, 0u);
+  const float sink2 = hv ? sinks[h] * kLog2e : 0.f;
+  float m = split == 0 ? sink2 : -INFINITY;
+  float l = (split == 0 && g == 0) ? 1.0f : 0.0f;
+  v4f o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const size_t cache_base = ((size_t)b * Hkv + kvh) * (size_t)Lmax * AD;
+  uint8_t* vw = vl[wave];
+  for (int key0 = k0; key0 < k1; key0 += ABK) {
+    // V block -> LDS (key rows key0 .., 8 x 16 bytes per lane); rows past k1 are zero
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 8 * j + (lane >> 3), chunk = lane & 7;
+      const int key = key0 + row;
+      const uint4 val = key < k1 ? *reinterpret_cast<const uint4*>(vc + cache_base + (size_t)key * AD + 8 * chunk)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+      *reinterpret_cast<uint4*>(vw + row * APITCH + 16 * chunk) = val;
+    }
+    // S^T: keys key0 + 16 kt + 4 g + i, query column l16
+    v4f s[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = key0 + 16 * kt + l16;
+      uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
+      if (key < k1) {
+        const uint16_t* pk = kc + cache_base + (size_t)key * AD + 8 * g;
+        a0 = *reinterpret_cast<const uint4*>(pk);
+        a1 = *reinterpret_cast<const uint4*>(pk + 32);
+      }
+      s[kt] = mfma_bf16(a0, qf[0], v4f{0.f, 0.f, 0.f, 0.f});
+      s[kt] = mfma_bf16(a1, qf[1], s[kt]);
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = s[kt][i] * scale2;
+        if (key0 + 16 * kt + 4 * g + i >= k1) x = -INFINITY;
+        s[kt][i] = x;
+        bm = fmaxf(bm, x);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);                  // finite: the block has a valid key
+    const float alpha = exp2f(m - mn);
+    m = mn;
+    float sum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(s[kt][i] - mn);
+        s[kt][i] = p;
+        sum += p;
+      }
+    l = l * alpha + sum;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): this wave's V rows are in LDS
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const uint4 pb = make_uint4(pack_bf16(s[2 * p][0], s[2 * p][1]), pack_bf16(s[2 * p][2], s[2 * p][3]),
+                                  pack_bf16(s[2 * p + 1][0], s[2 * p + 1][1]),
+                                  pack_bf16(s[2 * p + 1][2], s[2 * p + 1][3]));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint8_t* pv = vw + (32 * p + 4 * g + (l16 >> 2)) * APITCH + 2 * (16 * dt + 4 * (l16 & 3));
+        const uint2 lo = tr16(pv);
+        const uint2 hi = tr16(pv + 16 * APITCH);
+        o[dt] = mfma_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);             // the reads are done before the next block's writes
+  }
+  // partials: [b][h][split] = {O[64], m, l, -, -}; the four lanes of a head add their sums
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!hv) return;
+  float* pp = part + (((size_t)b * Hq + h) * nsplit + split) * kPartFloats;
+  if (g == 0) {
+    pp[AD] = m;
+    pp[AD + 1] = l;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    *reinterpret_cast<v4f*>(pp + 16 * dt + 4 * g) = o[dt];
+}
+
+// out[b][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits
+// that hold keys (M = max_s m_s, finite: split 0 carries the sink).
+__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ kv_len,
+                                                          uint16_t* __restrict__ out, int Hq, int Lmax,
+                                                          int nsplit) {
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const int b = bh / Hq;
+  const int used = (min(max(kv_len[b], 0), Lmax) + kSplitKeys - 1) / kSplitKeys;
+  const int ns = used < 1 ? 1 : used;               // split 0 always holds the sink
+  const float* pp = part + (size_t)bh * nsplit * kPartFloats;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[s * kPartFloats + AD]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = exp2f(pp[s * kPartFloats + AD] - M);
+    den += w * pp[s * kPartFloats + AD + 1];
+    num += w * pp[s * kPartFloats + d];
+  }
+  out[(size_t)bh * AD + d] = f32_to_bf16(num / den);
+}
+
+}  // namespace
+
+int attn_decode_splits(int Lmax) { return Lmax <= 0 ? 1 : (Lmax + kSplitKeys - 1) / kSplitKeys; }
+
+hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const float* sinks, uint16_t* out, int S, int Hq, int Hkv,
+                               float sm_scale, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  const int HW = G >= 8 ? 8 : G;                    // heads per workgroup
+  const int QB = 64 * (8 / HW);
+  const dim3 grid(ceil_div(S, QB), Hq / HW), block(512);
+  const float scale2 = sm_scale * kLog2e;
+  switch (HW) {
+    case 8: hipLaunchKernelGGL(attn_prefill_kernel<8>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                              const int32_t* kv_len, const float* sinks, uint16_t* out, float* part,
+                              int B, int Hq, int Hkv, int Lmax, float sm_scale, hipStream_t stream) {
+  const int nsplit = attn_decode_splits(Lmax);
+  const int units = B * Hkv * nsplit;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(ceil_div(units, 4)), dim3(256), 0, stream, q, kc, vc, kv_len,
+                     sinks, part, B, Hq, Hkv, Lmax, nsplit, sm_scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(AD), 0, stream, part, kv_len, out, Hq, Lmax,
+                     nsplit);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -9,15 +9,17 @@ import pytest
 import sparse_moe_layer_fp32_amd as moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "attention.h")]
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*((?:moe|attn)_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -121,3 +123,50 @@ def test_workspace_size_formula_matches_header_estimate():
     est = T * (d + k * (f + 4 * d + 8))
     got = moe.workspace_bytes(T, d, f, E, k)
     assert 0.9 * est < got < 1.2 * est
+
+
+# ------------------------------------------------------------------ attention with sinks
+def attn_prefill_call(S=64, Hq=8, Hkv=2, D=64, null=None, misalign=None):
+    ptrs = [FAKE + 4096 * i for i in range(5)]
+    if null is not None:
+        ptrs[null] = None
+    if misalign is not None:
+        ptrs[misalign] += 4
+    q, k, v, sk, out = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    return moe.lib().attn_sink_prefill(q, k, v, sk, out, S, Hq, Hkv, D, 0.125, None)
+
+
+def attn_decode_call(B=4, Hq=8, Hkv=2, D=64, Lmax=300, ws=None, null=None, misalign=None):
+    ptrs = [FAKE + 4096 * i for i in range(7)]
+    if null is not None:
+        ptrs[null] = None
+    if misalign is not None:
+        ptrs[misalign] += 4
+    q, kc, vc, kl, sk, out, wsp = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    if ws is None:
+        ws = moe.attn_decode_workspace_bytes(B, Hq, Lmax)
+    return moe.lib().attn_sink_decode(q, kc, vc, kl, sk, out, B, Hq, Hkv, D, Lmax, 0.125, wsp, ws, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=128), ERR_UNSUP), (dict(Hq=6, Hkv=4), ERR_SHAPE), (dict(Hkv=0), ERR_SHAPE), (dict(S=-1), ERR_SHAPE),
+    (dict(Hq=24, Hkv=8), ERR_UNSUP), (dict(Hq=12, Hkv=2), ERR_UNSUP), (dict(null=3), ERR_NULL),
+    (dict(misalign=0), ERR_ALIGN), (dict(S=0, null=0), OK),
+])
+def test_attn_prefill_argument_errors(kw, want):
+    assert attn_prefill_call(**kw) == want
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(D=32), ERR_UNSUP), (dict(Hq=9), ERR_SHAPE), (dict(Hq=64, Hkv=2), ERR_UNSUP), (dict(Lmax=0), ERR_SHAPE),
+    (dict(ws=100), ERR_WS), (dict(null=3), ERR_NULL), (dict(null=6), ERR_NULL), (dict(misalign=2), ERR_ALIGN),
+    (dict(B=0, null=0), OK),
+])
+def test_attn_decode_argument_errors(kw, want):
+    assert attn_decode_call(**kw) == want
+
+
+def test_attn_decode_workspace_size():
+    assert moe.attn_decode_workspace_bytes(4, 8, 256) == 4 * 8 * 1 * 68 * 4
+    assert moe.attn_decode_workspace_bytes(4, 8, 257) == 4 * 8 * 2 * 68 * 4
+    assert moe.attn_decode_workspace_bytes(4, 8, 0) == 0
