@@ -1,6 +1,7 @@
 """Benchmark of the sparse MoE block forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1] [--format block128|mx|mxfp4]
+    python bench.py --workload attn_prefill | attn_decode
 
 A step is one whole forward (router + top-k + softmax + x quantisation,
 routing scan and placement, gate/up grouped FP8 GEMM with SwiGLU and h
@@ -12,6 +13,11 @@ variant, E8M0 scales per 32; ``--format mxfp4``: E2M1 weights with those scales)
 GEMM (its duration measured with HIP events inside the timed region, on the
 stream it runs on) and the CPU oracle timed on a bounded sample of the same
 workload.
+
+``--workload attn_prefill`` / ``attn_decode`` time the attention with per-head
+sinks instead (gpt-oss shape: 64 query heads, 8 key/value heads, head dim
+64): causal prefill of one 8192-token sequence, and one decode step of 64
+sequences over KV caches of up to 4096 tokens (seeded ragged lengths).
 """
 from __future__ import annotations
 
@@ -33,6 +39,8 @@ from sparse_moe_layer_fp32_amd import inputs as gen  # noqa: E402
 METRIC = "MoE-layer tokens/s + % of FP8 MFMA peak (prefill) / % HBM BW (decode)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ATTN_METRIC = "attention tokens/s + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
 GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 
 # HBM traffic of one gate/up GEMM launch from rocprofv3 --pmc runs (one run for
@@ -151,12 +159,100 @@ def cpu_baseline(inp, budget_s=12.0):
                       f"{T} tokens, expert math of the sample, fp64 NumPy; {dt:.1f} s)"}
 
 
+def attn_bench(args):
+    """Sink attention: one call per step, HIP events around the timed steps."""
+    from oracle import attention as att
+    shape = gen.GPT_OSS_ATTN
+    dev = torch.device("cuda:0")
+    prefill = args.workload == "attn_prefill"
+    if prefill:
+        S = 8192
+        inp = gen.make_attn_prefill(shape, S, seed=0)
+        p = moe.attn_device_inputs(inp, dev)
+        out = torch.empty((S, shape.Hq, shape.D), dtype=torch.bfloat16, device=dev)
+        run = lambda: moe.attn_prefill(p["q"], p["k"], p["v"], p["sinks"], p["sm_scale"], out=out)
+        tokens = S
+        flops = 4.0 * shape.D * shape.Hq * S * (S + 1) / 2       # QK^T and PV over the causal triangle
+        work = dict(flops=flops)
+    else:
+        B, L = 64, 4096
+        inp = gen.make_attn_decode(shape, B, L, seed=0)
+        p = moe.attn_device_inputs(inp, dev)
+        out = torch.empty((B, shape.Hq, shape.D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(moe.attn_decode_workspace_bytes(B, shape.Hq, L), dtype=torch.uint8, device=dev)
+        run = lambda: moe.attn_decode(p["q"], p["k"], p["v"], p["kv_len"], p["sinks"], p["sm_scale"],
+                                      out=out, workspace=ws)
+        tokens = B
+        kv_bytes = int(inp["kv_len"].astype(np.int64).sum()) * shape.Hkv * shape.D * 2 * 2
+        work = dict(bytes=kv_bytes + 2 * B * shape.Hq * shape.D * 2)  # K, V of the visible keys + q + out
+    log(f"[bench] {args.workload}: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        evs[i][0].record()
+        run()
+        evs[i][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if prefill:
+        ach = work["flops"] / (call_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "attn_prefill_kernel<8>", "avg_ms": round(call_ms, 5), "algorithmic_flops": work["flops"]}
+    else:
+        ach = work["bytes"] / (call_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "attn_decode_kernel + attn_combine_kernel (the whole call)",
+                "avg_ms": round(call_ms, 5), "algorithmic_bytes": work["bytes"]}
+    cfg = ({"workload": f"attn_prefill: causal GQA attention with sinks, S=8192, Hq=64, Hkv=8, D=64",
+            "S": 8192} if prefill else
+           {"workload": f"attn_decode: one query per sequence, B=64, KV up to 4096 (ragged, mean "
+                        f"{float(inp['kv_len'].mean()):.0f}), Hq=64, Hkv=8, D=64", "B": 64, "Lmax": 4096})
+    cfg.update(Hq=shape.Hq, Hkv=shape.Hkv, D=shape.D)
+    res = {"metric": ATTN_METRIC, "value": round(tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg,
+           "roofline": roof}
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            if prefill:
+                rows = np.arange(S - 8, S)                        # the 8 longest rows
+                att.prefill(inp["q"], inp["k"], inp["v"], inp["sinks"], inp["sm_scale"], rows=rows)
+                n = len(rows)
+            else:
+                sl = slice(0, 4)
+                att.decode(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["kv_len"][sl], inp["sinks"], inp["sm_scale"])
+                n = 4
+            reps += 1
+            if time.perf_counter() - t0 >= 10.0 or reps >= 3:
+                break
+        dt = time.perf_counter() - t0
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        res["cpu_baseline"] = {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"{reps} x oracle on {n} " + ("query rows (the last 8 of 8192)" if prefill
+                                                                       else "sequences") + f"; {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS))
+    ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS) + ["attn_decode", "attn_prefill"])
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),
                     help="weight format: 128x128 block-scaled FP8, MXFP8 (E8M0 per 32) or MXFP4")
@@ -169,6 +265,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the MoE block here is "
               "built for a single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("attn"):
+        attn_bench(args)
+        return
 
     cfg = gen.CONFIGS[args.workload]
     log(f"[bench] generating {cfg.name} (T={cfg.T}, d={cfg.layer.d}, f={cfg.layer.f}, "

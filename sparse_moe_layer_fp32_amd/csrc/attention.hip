@@ -42,10 +42,30 @@ __device__ __forceinline__ v4f mfma_bf16(uint4 a, uint4 b, v4f c) {
                                                  c, 0, 0, 0);
 }
 
-// two fp32 -> packed bf16 pair (round to nearest even), low half first
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even), low half first
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
+
+// max / sum over the four lanes l, l^16, l^32, l^48 (one query column of an
+// S^T tile) with the VALU lane swaps (no LDS round trip)
+__device__ __forceinline__ float max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 2^x with the hardware exp (arguments here are <= 0; results below 2^-126 flush to 0)
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ uint2 tr16(const uint8_t* p) {
   const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
@@ -148,25 +168,27 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
             s[kt][qt] = mfma_bf16(a1, qf[qt][1], s[kt][qt]);
           }
         }
-        const bool diag = kh0 + 31 > row0;  // the half reaches past the wave's first row
+        // causal mask on the diagonal only (a uniform branch): key > query -> -inf
+        if (kh0 + 31 > row0) {
+#pragma unroll
+          for (int qt = 0; qt < 4; ++qt)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (kh0 + 16 * kt + 4 * g + i > row0 + 16 * qt + l16) s[kt][qt][i] = -INFINITY;
+        }
         uint4 pb[4];
 #pragma unroll
         for (int qt = 0; qt < 4; ++qt) {
-          const int qi = row0 + 16 * qt + l16;
+          // the maximum on raw scores (scale2 > 0 keeps the order), then p = 2^(s scale2 - m)
           float bm = -INFINITY;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float x = s[kt][qt][i] * scale2;
-              if (diag && kh0 + 16 * kt + 4 * g + i > qi) x = -INFINITY;
-              s[kt][qt][i] = x;
-              bm = fmaxf(bm, x);
-            }
-          bm = fmaxf(bm, __shfl_xor(bm, 16));
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
-          const float mn = fmaxf(m[qt], bm);
-          const float alpha = exp2f(m[qt] - mn);
+            for (int i = 0; i < 4; ++i) bm = fmaxf(bm, s[kt][qt][i]);
+          const float mn = fmaxf(m[qt], max4(bm) * scale2);
+          const float alpha = ex2(m[qt] - mn);
           m[qt] = mn;
           float pr[2][4];
           float sum = 0.f;
@@ -174,12 +196,15 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              pr[kt][i] = exp2f(s[kt][qt][i] - mn);
+              pr[kt][i] = ex2(fmaf(s[kt][qt][i], scale2, -mn));
               sum += pr[kt][i];
             }
-          l[qt] = l[qt] * alpha + sum;
+          l[qt] = fmaf(l[qt], alpha, sum);
+          // O is rescaled only when some query's maximum moved (rare once it settles)
+          if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+            for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+          }
           // B operand of the PV MFMA: keys kh0 + 4 g + j, then kh0 + 16 + 4 g + j
           pb[qt] = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
                               pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
@@ -207,10 +232,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
   // out[query][h][d] = O^T[d][query] / sum; the four lanes of a query hold partial sums
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
-    float lt = l[qt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
+    const float inv = 1.0f / sum4(l[qt]);
     const int r = row0 + 16 * qt + l16;
     if (r >= S) continue;
     uint16_t* po = out + ((size_t)r * Hq + h) * AD + 4 * g;
@@ -291,26 +313,22 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float x = s[kt][i] * scale2;
-        if (key0 + 16 * kt + 4 * g + i >= k1) x = -INFINITY;
-        s[kt][i] = x;
-        bm = fmaxf(bm, x);
+        if (key0 + 16 * kt + 4 * g + i >= k1) s[kt][i] = -INFINITY;  // past the sequence
+        bm = fmaxf(bm, s[kt][i]);
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);                  // finite: the block has a valid key
-    const float alpha = exp2f(m - mn);
+    const float mn = fmaxf(m, max4(bm) * scale2);  // finite: the block has a valid key
+    const float alpha = ex2(m - mn);
     m = mn;
     float sum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(s[kt][i] - mn);
+        const float p = ex2(fmaf(s[kt][i], scale2, -mn));
         s[kt][i] = p;
         sum += p;
       }
-    l = l * alpha + sum;
+    l = fmaf(l, alpha, sum);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     __builtin_amdgcn_s_waitcnt(0xc07f);             // lgkmcnt(0): this wave's V rows are in LDS
@@ -330,8 +348,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     __builtin_amdgcn_s_waitcnt(0xc07f);             // the reads are done before the next block's writes
   }
   // partials: [b][h][split] = {O[64], m, l, -, -}; the four lanes of a head add their sums
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = sum4(l);
   if (!hv) return;
   float* pp = part + (((size_t)b * Hq + h) * nsplit + split) * kPartFloats;
   if (g == 0) {
