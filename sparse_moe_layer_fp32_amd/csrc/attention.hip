@@ -33,6 +33,7 @@ constexpr int AD = 64;          // head dim
 constexpr int ABK = 64;         // keys per block
 constexpr int APITCH = 144;     // LDS bytes per key row (128 + 16: rows on distinct banks)
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr int kAttnQt = 2;      // prefill query tiles (16 rows) per wave: 16 waves of 32 rows
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -74,36 +75,45 @@ __device__ __forceinline__ uint2 tr16(const uint8_t* p) {
 
 // ---------------------------------------------------------------------------
 // Prefill: one workgroup = HW query heads sharing one key/value head times
-// 64 * (8 / HW) query rows; wave w owns head h0 + w % HW and 64 rows.  The
-// K and V blocks of 64 keys go through LDS once for all eight waves (double
-// buffered: the next block is loaded to registers while the current one is
-// used).  Causal: a block is used by the waves whose rows reach it; the
-// block on the diagonal masks key > query.
-template <int HW>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __restrict__ q,
-                                                           const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v,
-                                                           const float* __restrict__ sinks,
-                                                           uint16_t* __restrict__ out, int S, int Hq,
-                                                           int Hkv, float scale2) {
-  constexpr int QB = 64 * (8 / HW);                  // query rows per workgroup
+// 64 * (8 / HW) query rows, in NW = 32 / QT waves of 16 QT rows (wave w: head
+// h0 + w % HW).  The K and V blocks of 64 keys go through LDS once for all
+// waves (double buffered: the next block is loaded to registers while the
+// current one is used).  With QT = 2 a wave needs at most 128 VGPRs, so four
+// waves share a SIMD and hide each other's MFMA, LDS and exp latencies.
+// Causal: a block is used by the waves whose rows reach it; the block on the
+// diagonal masks key > query.
+template <int HW, int QT>
+__global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint16_t* __restrict__ q,
+                                                                      const uint16_t* __restrict__ k,
+                                                                      const uint16_t* __restrict__ v,
+                                                                      const float* __restrict__ sinks,
+                                                                      uint16_t* __restrict__ out, int S,
+                                                                      int Hq, int Hkv, float scale2) {
+  constexpr int NW = 32 / QT;                        // waves
+  constexpr int RW = 16 * QT;                        // query rows per wave
+  constexpr int QB = RW * (NW / HW);                 // query rows per workgroup: 64 * (8 / HW)
+  constexpr int IPT = 2 * ABK * 8 / (64 * NW);       // 16-byte K/V pieces per thread and block
   __shared__ __attribute__((aligned(16))) uint8_t kl[2][ABK * APITCH];
   __shared__ __attribute__((aligned(16))) uint8_t vl[2][ABK * APITCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int G = Hq / Hkv;
-  const int qb = gridDim.x - 1 - blockIdx.x;        // longest (last) query blocks first
-  const int h0 = blockIdx.y * HW;
+  // 1-D grid, longest work first across every head group: workgroup i takes
+  // head group i % (Hq / HW) and query block nqb - 1 - i / (Hq / HW)
+  const int ngrp = Hq / HW;
+  const int nqb = gridDim.x / ngrp;
+  const int qb = nqb - 1 - (int)blockIdx.x / ngrp;
+  const int h0 = ((int)blockIdx.x % ngrp) * HW;
   const int kvh = h0 / G;
   const int h = h0 + wave % HW;
-  const int row0 = qb * QB + 64 * (wave / HW);      // this wave's first query row
+  const int row0 = qb * QB + RW * (wave / HW);      // this wave's first query row
   const int wg_last = min(S, (qb + 1) * QB) - 1;    // last query row of the workgroup
   const int nblk = wg_last / ABK + 1;               // key blocks the workgroup needs
 
   // Q^T fragments (B operand): query row0 + 16 qt + l16, dims 32 c + 8 g .. + 7
-  uint4 qf[4][2];
+  uint4 qf[QT][2];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const int r = row0 + 16 * qt + l16;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -111,59 +121,66 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
                         : make_uint4(0u, 0u, 0u, 0u);
   }
   // running max (log2 domain) per query column, per-lane partial sums, O^T
-  float m[4], l[4];
-  v4f o[4][4];  // [dt][qt]: dims 16 dt + 4 g + i, query 16 qt + l16
+  float m[QT], l[QT];
+  v4f o[4][QT];  // [dt][qt]: dims 16 dt + 4 g + i, query 16 qt + l16
   const float sink2 = sinks[h] * kLog2e;
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     m[qt] = sink2;                 // the sink seeds the running maximum ...
     l[qt] = g == 0 ? 1.0f : 0.0f;  // ... and contributes exp2(0) = 1 to the sum (once per query)
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 
-  // block loader: thread t moves 16 bytes of K and of V (key t / 8, bytes 16 (t % 8))
-  const int lkey = tid >> 3, lchunk = tid & 7;
-  uint4 kr, vr;
-  auto load = [&](int kb) {
-    const int key = kb * ABK + lkey;
-    if (key < S) {
-      const size_t off = ((size_t)key * Hkv + kvh) * AD + 8 * lchunk;
-      kr = *reinterpret_cast<const uint4*>(k + off);
-      vr = *reinterpret_cast<const uint4*>(v + off);
-    } else {
-      kr = vr = make_uint4(0u, 0u, 0u, 0u);
+  // block loader: piece it = tid + 64 NW j: K (it < 512) or V, key (it % 512) / 8,
+  // bytes 16 (it % 8) of its row.  Blocks are loaded two iterations ahead into
+  // two register sets (block b in set b % 2) and written to LDS one ahead.
+  uint4 lr0[IPT], lr1[IPT];
+  auto load = [&](int kb, uint4 (&lr)[IPT]) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int it = tid + 64 * NW * j;
+      const int key = kb * ABK + ((it & 511) >> 3);
+      const uint16_t* src = it < 512 ? k : v;
+      lr[j] = key < S ? *reinterpret_cast<const uint4*>(src + ((size_t)key * Hkv + kvh) * AD + 8 * (it & 7))
+                      : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto store = [&](int buf) {
-    *reinterpret_cast<uint4*>(&kl[buf][lkey * APITCH + 16 * lchunk]) = kr;
-    *reinterpret_cast<uint4*>(&vl[buf][lkey * APITCH + 16 * lchunk]) = vr;
+  auto store = [&](int buf, const uint4 (&lr)[IPT]) {
+#pragma unroll
+    for (int j = 0; j < IPT; ++j) {
+      const int it = tid + 64 * NW * j;
+      uint8_t* dst = (it < 512 ? kl[buf] : vl[buf]) + ((it & 511) >> 3) * APITCH + 16 * (it & 7);
+      *reinterpret_cast<uint4*>(dst) = lr[j];
+    }
   };
 
-  load(0);
-  store(0);
+  load(0, lr0);
+  if (nblk > 1) load(1, lr1);
+  store(0, lr0);
   __syncthreads();
-  for (int kb = 0; kb < nblk; ++kb) {
+  // one key block; block kb's registers (set kb % 2) are free again, so they take block kb + 2
+  auto block = [&](int kb, uint4 (&cur)[IPT], uint4 (&nxt)[IPT]) {
     const int buf = kb & 1;
-    if (kb + 1 < nblk) load(kb + 1);
+    if (kb + 2 < nblk) load(kb + 2, cur);
     const int key0 = kb * ABK;
-    if (key0 <= row0 + 63 && row0 < S) {  // some of this wave's rows see the block
+    if (key0 <= row0 + RW - 1 && row0 < S) {  // some of this wave's rows see the block
       const uint8_t* kb_l = kl[buf];
       const uint8_t* vb_l = vl[buf];
       // two 32-key halves, each its own online-softmax step (fewer live scores)
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int kh0 = key0 + 32 * p;
-        if (kh0 > row0 + 63) break;  // the wave's rows see none of this half
+        if (kh0 > row0 + RW - 1) break;  // the wave's rows see none of this half
         // S^T tiles: keys kh0 + 16 kt + 4 g + i, query 16 qt + l16
-        v4f s[2][4];
+        v4f s[2][QT];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           const uint8_t* pk = kb_l + (32 * p + 16 * kt + l16) * APITCH + 16 * g;
           const uint4 a0 = *reinterpret_cast<const uint4*>(pk);
           const uint4 a1 = *reinterpret_cast<const uint4*>(pk + 64);
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) {
+          for (int qt = 0; qt < QT; ++qt) {
             s[kt][qt] = mfma_bf16(a0, qf[qt][0], v4f{0.f, 0.f, 0.f, 0.f});
             s[kt][qt] = mfma_bf16(a1, qf[qt][1], s[kt][qt]);
           }
@@ -171,16 +188,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
         // causal mask on the diagonal only (a uniform branch): key > query -> -inf
         if (kh0 + 31 > row0) {
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt)
+          for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 if (kh0 + 16 * kt + 4 * g + i > row0 + 16 * qt + l16) s[kt][qt][i] = -INFINITY;
         }
-        uint4 pb[4];
+        uint4 pb[QT];
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
+        for (int qt = 0; qt < QT; ++qt) {
           // the maximum on raw scores (scale2 > 0 keeps the order), then p = 2^(s scale2 - m)
           float bm = -INFINITY;
 #pragma unroll
@@ -218,20 +235,24 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const uint16_t* __res
           const uint2 hi = tr16(pv + 16 * APITCH);
           const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
-          for (int qt = 0; qt < 4; ++qt) o[dt][qt] = mfma_bf16(a, pb[qt], o[dt][qt]);
+          for (int qt = 0; qt < QT; ++qt) o[dt][qt] = mfma_bf16(a, pb[qt], o[dt][qt]);
         }
       }
     }
     if (kb + 1 < nblk) {
       // buffer buf ^ 1 was last read for block kb - 1, before the previous barrier
-      store(buf ^ 1);
+      store(buf ^ 1, nxt);
       __syncthreads();
     }
+  };
+  for (int kb = 0; kb < nblk; kb += 2) {
+    block(kb, lr0, lr1);
+    if (kb + 1 < nblk) block(kb + 1, lr1, lr0);
   }
 
   // out[query][h][d] = O^T[d][query] / sum; the four lanes of a query hold partial sums
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
+  for (int qt = 0; qt < QT; ++qt) {
     const float inv = 1.0f / sum4(l[qt]);
     const int r = row0 + 16 * qt + l16;
     if (r >= S) continue;
@@ -392,13 +413,14 @@ hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint1
   const int G = Hq / Hkv;
   const int HW = G >= 8 ? 8 : G;                    // heads per workgroup
   const int QB = 64 * (8 / HW);
-  const dim3 grid(ceil_div(S, QB), Hq / HW), block(512);
+  constexpr int QT = kAttnQt;
+  const dim3 grid(ceil_div(S, QB) * (Hq / HW)), block(64 * (32 / QT));
   const float scale2 = sm_scale * kLog2e;
   switch (HW) {
-    case 8: hipLaunchKernelGGL(attn_prefill_kernel<8>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
-    case 4: hipLaunchKernelGGL(attn_prefill_kernel<4>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
-    case 2: hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
-    case 1: hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 8: hipLaunchKernelGGL((attn_prefill_kernel<8, QT>), grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 4: hipLaunchKernelGGL((attn_prefill_kernel<4, QT>), grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 2: hipLaunchKernelGGL((attn_prefill_kernel<2, QT>), grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
+    case 1: hipLaunchKernelGGL((attn_prefill_kernel<1, QT>), grid, block, 0, stream, q, k, v, sinks, out, S, Hq, Hkv, scale2); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

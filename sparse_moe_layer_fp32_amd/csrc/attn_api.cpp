@@ -30,7 +30,9 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
   if (hs != MOE_OK) return hs;
   const int G = Hq / Hkv;
   if (!(G == 1 || G == 2 || G == 4 || G % 8 == 0)) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)S * Hq * D >= kMaxElems || Hq / (G >= 8 ? 8 : G) > 65535) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)S * Hq * D >= kMaxElems ||
+      (int64_t)((S + 63) / 64 + 1) * 8 * (Hq / (G >= 8 ? 8 : G)) >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   if (S == 0) return MOE_OK;
   const void* ptrs[] = {q, k, v, sinks, out};
   for (const void* p : ptrs)
