@@ -47,7 +47,7 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
                              float sm_scale, void* stream);
 
 /* Bytes of device workspace attn_sink_decode needs (the per-split partial
- * results: B * Hq * ceil(Lmax / 256) records of 68 floats). */
+ * results: at most B * Hq * ceil(Lmax / 256) records of 68 floats). */
 size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
 
 /* One query per sequence over a KV cache laid out heads major with each
@@ -60,8 +60,9 @@ size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
  *                                [0, Lmax] are clamped; 0 keys give a zero output)
  *   sinks    fp32 [Hq]
  *   out      bf16 [B, Hq, D]     written
- * Keys are split in parts of 256 (one wave each) and merged by a second
- * kernel; Hq / Hkv must be at most 16. */
+ * Keys are split in parts of 256 * 2^j (one wave each; j grows while the
+ * waves B * Hkv * splits exceed what the chip holds at once) and merged by a
+ * second kernel; Hq / Hkv must be at most 16. */
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_len, const float* sinks, void* out, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax, float sm_scale,

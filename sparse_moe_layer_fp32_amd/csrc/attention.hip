@@ -266,7 +266,7 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one wave per (sequence b, key/value head, split of kSplitKeys keys);
+// Decode: one wave per (sequence b, key/value head, split of skeys keys);
 // its G <= 16 query heads form the 16 MFMA columns (the rest are zero).  K
 // fragments come straight from the cache (a lane reads 16 bytes of one key
 // row); each 64-key block of V is staged in the wave's own LDS slice for the
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ sinks, float* __restrict__ part,
-    int B, int Hq, int Hkv, int Lmax, int nsplit, float scale2) {
+    int B, int Hq, int Hkv, int Lmax, int nsplit, int skeys, float scale2) {
   __shared__ __attribute__((aligned(16))) uint8_t vl[4][ABK * APITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   if (b >= B) return;
   const int G = Hq / Hkv;
   const int n = min(max(kv_len[b], 0), Lmax);      // lengths outside [0, Lmax] are clamped
-  const int k0 = split * kSplitKeys, k1 = min(n, k0 + kSplitKeys);
+  const int k0 = split * skeys, k1 = min(n, k0 + skeys);
   const int h = kvh * G + l16;                      // query head of column l16
   const bool hv = l16 < G;
 
@@ -305,29 +305,35 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
   const size_t cache_base = ((size_t)b * Hkv + kvh) * (size_t)Lmax * AD;
   uint8_t* vw = vl[wave];
-  for (int key0 = k0; key0 < k1; key0 += ABK) {
-    // V block -> LDS (key rows key0 .., 8 x 16 bytes per lane); rows past k1 are zero
+  // block registers: V rows 8 j + lane / 8 (16 bytes each) and the K fragments
+  // of rows 16 kt + l16; the next block is fetched while the current one is used
+  uint4 kA[8], vA[8], kB[8], vB[8];
+  auto fetch = [&](int key0, uint4 (&kr)[8], uint4 (&vr)[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int row = 8 * j + (lane >> 3), chunk = lane & 7;
-      const int key = key0 + row;
-      const uint4 val = key < k1 ? *reinterpret_cast<const uint4*>(vc + cache_base + (size_t)key * AD + 8 * chunk)
-                                 : make_uint4(0u, 0u, 0u, 0u);
-      *reinterpret_cast<uint4*>(vw + row * APITCH + 16 * chunk) = val;
+      const int key = key0 + 8 * j + (lane >> 3);
+      vr[j] = key < k1 ? *reinterpret_cast<const uint4*>(vc + cache_base + (size_t)key * AD + 8 * (lane & 7))
+                       : make_uint4(0u, 0u, 0u, 0u);
     }
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = key0 + 16 * kt + l16;
+      const uint16_t* pk = kc + cache_base + (size_t)key * AD + 8 * g;
+      kr[2 * kt] = key < k1 ? *reinterpret_cast<const uint4*>(pk) : make_uint4(0u, 0u, 0u, 0u);
+      kr[2 * kt + 1] = key < k1 ? *reinterpret_cast<const uint4*>(pk + 32) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto block = [&](int key0, const uint4 (&kr)[8], const uint4 (&vr)[8], uint4 (&kn)[8], uint4 (&vn)[8]) {
+    if (key0 + ABK < k1) fetch(key0 + ABK, kn, vn);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<uint4*>(vw + (8 * j + (lane >> 3)) * APITCH + 16 * (lane & 7)) = vr[j];
     // S^T: keys key0 + 16 kt + 4 g + i, query column l16
     v4f s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const int key = key0 + 16 * kt + l16;
-      uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
-      if (key < k1) {
-        const uint16_t* pk = kc + cache_base + (size_t)key * AD + 8 * g;
-        a0 = *reinterpret_cast<const uint4*>(pk);
-        a1 = *reinterpret_cast<const uint4*>(pk + 32);
-      }
-      s[kt] = mfma_bf16(a0, qf[0], v4f{0.f, 0.f, 0.f, 0.f});
-      s[kt] = mfma_bf16(a1, qf[1], s[kt]);
+      s[kt] = mfma_bf16(kr[2 * kt], qf[0], v4f{0.f, 0.f, 0.f, 0.f});
+      s[kt] = mfma_bf16(kr[2 * kt + 1], qf[1], s[kt]);
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -367,6 +373,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);             // the reads are done before the next block's writes
+  };
+  if (k0 < k1) fetch(k0, kA, vA);
+  for (int key0 = k0; key0 < k1; key0 += 2 * ABK) {
+    block(key0, kA, vA, kB, vB);
+    if (key0 + ABK < k1) block(key0 + ABK, kB, vB, kA, vA);
   }
   // partials: [b][h][split] = {O[64], m, l, -, -}; the four lanes of a head add their sums
   l = sum4(l);
@@ -386,10 +397,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part,
                                                           const int32_t* __restrict__ kv_len,
                                                           uint16_t* __restrict__ out, int Hq, int Lmax,
-                                                          int nsplit) {
+                                                          int nsplit, int skeys) {
   const int bh = blockIdx.x, d = threadIdx.x;
   const int b = bh / Hq;
-  const int used = (min(max(kv_len[b], 0), Lmax) + kSplitKeys - 1) / kSplitKeys;
+  const int used = (min(max(kv_len[b], 0), Lmax) + skeys - 1) / skeys;
   const int ns = used < 1 ? 1 : used;               // split 0 always holds the sink
   const float* pp = part + (size_t)bh * nsplit * kPartFloats;
   float M = -INFINITY;
@@ -405,7 +416,17 @@ __global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restric
 
 }  // namespace
 
-int attn_decode_splits(int Lmax) { return Lmax <= 0 ? 1 : (Lmax + kSplitKeys - 1) / kSplitKeys; }
+int attn_decode_split_keys(int B, int Hkv, int Lmax) {
+  int s = kMinSplitKeys;
+  while (s < Lmax && (int64_t)B * Hkv * ceil_div(Lmax, s) > kResidentWaves) s *= 2;
+  return s;
+}
+
+int attn_decode_splits(int B, int Hkv, int Lmax) {
+  return Lmax <= 0 ? 1 : ceil_div(Lmax, attn_decode_split_keys(B, Hkv, Lmax));
+}
+
+int attn_decode_max_splits(int Lmax) { return Lmax <= 0 ? 1 : ceil_div(Lmax, kMinSplitKeys); }
 
 hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const float* sinks, uint16_t* out, int S, int Hq, int Hkv,
@@ -429,14 +450,15 @@ hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint1
 hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                               const int32_t* kv_len, const float* sinks, uint16_t* out, float* part,
                               int B, int Hq, int Hkv, int Lmax, float sm_scale, hipStream_t stream) {
-  const int nsplit = attn_decode_splits(Lmax);
+  const int skeys = attn_decode_split_keys(B, Hkv, Lmax);
+  const int nsplit = ceil_div(Lmax, skeys);
   const int units = B * Hkv * nsplit;
   hipLaunchKernelGGL(attn_decode_kernel, dim3(ceil_div(units, 4)), dim3(256), 0, stream, q, kc, vc, kv_len,
-                     sinks, part, B, Hq, Hkv, Lmax, nsplit, sm_scale * kLog2e);
+                     sinks, part, B, Hq, Hkv, Lmax, nsplit, skeys, sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(AD), 0, stream, part, kv_len, out, Hq, Lmax,
-                     nsplit);
+                     nsplit, skeys);
   return hipGetLastError();
 }
 

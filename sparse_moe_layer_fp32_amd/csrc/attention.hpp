@@ -5,11 +5,17 @@
 
 namespace moe {
 
-constexpr int kSplitKeys = 256;   // keys per decode split
-constexpr int kPartFloats = 68;   // per (sequence, head, split): O[64], max, sum, 2 pad (16-byte records)
+constexpr int kMinSplitKeys = 256;    // smallest decode split
+constexpr int kResidentWaves = 2048;  // decode waves the chip holds at once (2 per SIMD)
+constexpr int kPartFloats = 68;       // per (sequence, head, split): O[64], max, sum, 2 pad (16-byte records)
 
-// splits of a decode call for caches of Lmax tokens
-int attn_decode_splits(int Lmax);
+// Keys per decode split: the smallest 256 * 2^j that keeps B * Hkv * splits
+// within one resident round of waves (longer splits hide more latency per
+// wave; more splits than resident waves only queue).
+int attn_decode_split_keys(int B, int Hkv, int Lmax);
+// splits of a decode call, and the most any (B, Hkv) can need for Lmax
+int attn_decode_splits(int B, int Hkv, int Lmax);
+int attn_decode_max_splits(int Lmax);
 
 // q [S, Hq, 64], k and v [S, Hkv, 64] bf16 (token major), sinks [Hq] fp32, out [S, Hq, 64] bf16.
 // Hq / Hkv must be 1, 2, 4 or a multiple of 8.

@@ -47,7 +47,7 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
 
 size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax) {
   if (B < 0 || Hq < 1 || Lmax < 1) return 0;
-  return (size_t)B * Hq * moe::attn_decode_splits(Lmax) * moe::kPartFloats * sizeof(float);
+  return (size_t)B * Hq * moe::attn_decode_max_splits(Lmax) * moe::kPartFloats * sizeof(float);
 }
 
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -59,7 +59,7 @@ moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_ca
   if (hs != MOE_OK) return hs;
   if (Hq / Hkv > 16) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv * Lmax * D >= kMaxElems ||
-      (int64_t)B * Hkv * moe::attn_decode_splits(Lmax) >= (int64_t(1) << 31))
+      (int64_t)B * Hkv * moe::attn_decode_max_splits(Lmax) >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (B == 0) return MOE_OK;
   const void* ptrs[] = {q, k_cache, v_cache, kv_len, sinks, out, workspace};

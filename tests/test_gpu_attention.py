@@ -62,7 +62,9 @@ def test_prefill_vs_oracle(S, Hq, Hkv):
 DECODE = [
     # (B, Hq, Hkv, Lmax, lengths or None for seeded ragged lengths)
     (4, 8, 1, 300, None), (16, 64, 8, 1024, None), (3, 16, 1, 513, None), (5, 4, 4, 64, None),
-    (6, 8, 2, 600, [1, 256, 257, 600, 511, 2]),
+    (6, 8, 2, 1100, [1, 256, 257, 1100, 1023, 513]),   # 256-key splits
+    (40, 16, 8, 2000, None),                         # 512-key splits
+    (48, 8, 8, 2100, [1, 512, 513, 2100, 1024, 1025] * 8),
 ]
 
 
