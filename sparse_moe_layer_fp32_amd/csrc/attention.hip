@@ -270,7 +270,9 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
 // its G <= 16 query heads form the 16 MFMA columns (the rest are zero).  K
 // fragments come straight from the cache (a lane reads 16 bytes of one key
 // row); each 64-key block of V is staged in the wave's own LDS slice for the
-// transposing reads.  The split's running max, partial sum and O go to the
+// transposing reads.  Both are loaded to registers one block ahead, so a
+// wave keeps 16 KB of loads in flight while it computes.  The split's
+// running max, partial sum and O go to the
 // workspace; split 0 starts from the sink (max = sink, sum = 1), the others
 // from an empty softmax (max = -inf, sum = 0).
 __global__ __launch_bounds__(256) void attn_decode_kernel(
