@@ -381,6 +381,76 @@ __device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k,
   }
 }
 
+// Top-k + softmax of up to RT_TT tokens with eight lanes per token (all 512
+// threads of the workgroup): lane j of a token's group holds the keys of
+// experts j, j + 8, ...; each of the k rounds takes the group maximum with
+// three lane exchanges and clears the winner.  The keys are those of
+// topk_thread, so the picks are identical.  Lane s < k of the group writes
+// pick s, counts it, and marks the token in the expert's mask.
+template <int EP>
+__device__ void topk_group8(const float* sl, const float* sbr, int T, int E, int k, int gate_mode,
+                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int* shist,
+                            int* spick, uint32_t* smask_lo, uint32_t* smask_hi) {
+  constexpr int KPL = EP / 8;  // keys per lane
+  const int t = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  const float* row = sl + t * (EP + 1);
+  uint64_t key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int e = 8 * j + sub;
+    key[j] = (t < T && e < E) ? ((uint64_t)ordered_key(row[e] + sbr[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
+                              : 0ull;
+  }
+  uint64_t sel[kMaxTopK];
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    sel[s] = 0ull;
+    if (s < k) {
+      uint64_t best = key[0];
+#pragma unroll
+      for (int j = 1; j < KPL; ++j) best = key[j] > best ? key[j] : best;
+#pragma unroll
+      for (int o = 4; o > 0; o >>= 1) {
+        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o);
+        const uint32_t lo = __shfl_xor((uint32_t)best, o);
+        const uint64_t other = ((uint64_t)hi << 32) | lo;
+        best = other > best ? other : best;
+      }
+      sel[s] = best;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (key[j] == best) key[j] = 0ull;
+    }
+  }
+  if (t >= T) return;
+  const float l0 = key_value((uint32_t)(sel[0] >> 32));
+  float ex[kMaxTopK];
+  float sum = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    ex[s] = s < k ? expf(key_value((uint32_t)(sel[s] >> 32)) - l0) : 0.f;
+    sum += ex[s];
+  }
+  if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits (lane sums, then an xor tree)
+    float part = 0.f;
+    for (int e = sub; e < E; e += 8) part += expf(row[e] + sbr[e] - l0);
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) part += __shfl_xor(part, o);
+    sum = part;
+  }
+#pragma unroll
+  for (int s = 0; s < kMaxTopK; ++s) {
+    if (s < k && sub == s) {
+      const int e = (int)(0xffffffffu - (uint32_t)sel[s]);
+      topk_idx[(size_t)t * k + s] = e;
+      topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
+      atomicAdd(&shist[e], 1);
+      spick[t * k + s] = e;
+      atomicOr(t < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (t & 31));
+    }
+  }
+}
+
 // Logits of the tile's RT_TT tokens into sl [RT_TT][EP + 1] (odd pitch: the
 // per-token readers of topk_thread hit distinct banks): the sum of every
 // (token, expert) partial in split order.  A thread takes 4 experts of one
@@ -465,6 +535,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     int nt0, int max0, int bm1, int nt1, int max1, int32_t* __restrict__ row_of,
     int32_t* __restrict__ row_token) {
   constexpr int EP = NBW * 16;
+  static_assert(RT_TT * 8 == 512, "the top-k takes eight lanes per token");
   __shared__ float sl[RT_TT * (EP + 1)];
   __shared__ int spick[RT_TT * kMaxTopK];
   __shared__ int scnt[kMaxExperts], soff[kMaxExperts + 1], so0[kMaxExperts + 1], so1[kMaxExperts + 1];
@@ -484,9 +555,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   }
   __syncthreads();
   if (!have_topk) {
-    if (tid < T)
-      topk_thread(sl + tid * (EP + 1), sbr, E, k, gate_mode, tid, topk_idx, topk_w, scnt, spick + tid * k, smask[0],
-                  smask[1], tid);
+    topk_group8<EP>(sl, sbr, T, E, k, gate_mode, topk_idx, topk_w, scnt, spick, smask[0], smask[1]);
   } else {
     for (int p = tid; p < R; p += 512) {
       const int t = p / k;
@@ -569,8 +638,12 @@ __global__ __launch_bounds__(512) void route_small_kernel(
         if (so[mid] <= L) lo = mid; else hi = mid;
       }
       const int cnt = scnt[lo];
-      const int mt = ceil_div(cnt, bm);
       const int local = L - so[lo];
+      if (cnt <= bm) {  // one row block: the entries are the column tiles in order
+        tiles[L] = make_int4(lo, soff[lo], cnt, local);
+        continue;
+      }
+      const int mt = ceil_div(cnt, bm);
       const int ng = local / (mt * kTileGroup);
       const int rem = local - ng * mt * kTileGroup;
       const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
