@@ -160,6 +160,8 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
 }
 
 // out[t, :] = bf16( sum_j w[t,j] * Y[row_of[t,j], :] ), fp32 in slot order.
+// Workgroup (t, y) takes columns 1024 y.. of token t (one pass per thread for
+// hidden sizes up to 1024 * gridDim.y).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ topk_w, int T,
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
     ws[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
   }
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+  for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < d; c += 1024 * gridDim.y) {
     float4 acc = *reinterpret_cast<const float4*>(Y + (size_t)rows[0] * d + c);
     acc.x *= ws[0];
     acc.y *= ws[0];
@@ -224,8 +226,8 @@ hipError_t launch_tile_table(const int32_t* tile_off, const int32_t* counts, con
 
 hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
                           int k, uint16_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, stream, Y, row_of, topk_w, T, d, k,
-                     out);
+  hipLaunchKernelGGL(combine_kernel, dim3(T, ceil_div(d, 1024)), dim3(256), 0, stream, Y, row_of, topk_w, T,
+                     d, k, out);
   return hipGetLastError();
 }
 

@@ -682,7 +682,7 @@ int router_splits(int T, int d) {
   if (T <= 0) return 1;
   const int tiles = ceil_div(T, RT_TT);
   const int ngroups = d / kBlock;
-  const int want = ceil_div(256, tiles);  // about one workgroup per CU
+  const int want = ceil_div(512, tiles);  // about two workgroups per CU
   const int ns = want < ngroups ? want : ngroups;
   if (ns <= 1) return 1;
   const int gps = ceil_div(ngroups, ns);
