@@ -148,16 +148,26 @@ __device__ __forceinline__ v4i sgpr4(v4i r) {
   }
   return r;
 }
-template <bool PIN = false>
+// NT: the non-temporal policy, for data read once (decode weights): the
+// stream then does not displace what the caches still serve.
+template <bool PIN = false, bool NT = false>
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voff) {
   rsrc = sgpr4<PIN>(rsrc);
   int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(rsrc)
-      : "memory");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
+  else
+    asm volatile(
+        "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
 }
 template <bool PIN = false>
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voff) {
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
         dma16<MX>(rA, sbase + (S::A_PER * wave + q) * 1024, aoff[q] + ka);
 #pragma unroll
     for (int q = 0; q < S::B_PER; ++q)
-      dma16<MX>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
+      dma16<MX, true>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
     dma4<MX>(rSide, sbase + DMA_SA + DMA_SB + side_dst, soff + (uint32_t)(kbl * side_step));
     ++kbl;
   };

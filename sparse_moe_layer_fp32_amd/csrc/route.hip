@@ -161,7 +161,12 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restri
 
 // out[t, :] = bf16( sum_j w[t,j] * Y[row_of[t,j], :] ), fp32 in slot order.
 // Workgroup (t, y) takes columns 1024 y.. of token t (one pass per thread for
-// hidden sizes up to 1024 * gridDim.y).
+// hidden sizes up to 1024 * gridDim.y).  Every Y row is read once: the loads
+// carry the non-temporal policy.
+typedef float v4f_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4f_nt load_once(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f_nt*>(p));
+}
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ topk_w, int T,
@@ -175,19 +180,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     ws[j] = j < k ? topk_w[(size_t)t * k + j] : 0.f;
   }
   for (int c = (blockIdx.y * 256 + threadIdx.x) * 4; c < d; c += 1024 * gridDim.y) {
-    float4 acc = *reinterpret_cast<const float4*>(Y + (size_t)rows[0] * d + c);
-    acc.x *= ws[0];
-    acc.y *= ws[0];
-    acc.z *= ws[0];
-    acc.w *= ws[0];
+    const v4f_nt y0 = load_once(Y + (size_t)rows[0] * d + c);
+    float4 acc = make_float4(y0[0] * ws[0], y0[1] * ws[0], y0[2] * ws[0], y0[3] * ws[0]);
 #pragma unroll
     for (int j = 1; j < kMaxTopK; ++j) {
       if (j < k) {
-        const float4 y = *reinterpret_cast<const float4*>(Y + (size_t)rows[j] * d + c);
-        acc.x = fmaf(ws[j], y.x, acc.x);
-        acc.y = fmaf(ws[j], y.y, acc.y);
-        acc.z = fmaf(ws[j], y.z, acc.z);
-        acc.w = fmaf(ws[j], y.w, acc.w);
+        const v4f_nt y = load_once(Y + (size_t)rows[j] * d + c);
+        acc.x = fmaf(ws[j], y[0], acc.x);
+        acc.y = fmaf(ws[j], y[1], acc.y);
+        acc.z = fmaf(ws[j], y[2], acc.z);
+        acc.w = fmaf(ws[j], y[3], acc.w);
       }
     }
     uint2 o;
