@@ -307,6 +307,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
   const size_t cache_base = ((size_t)b * Hkv + kvh) * (size_t)Lmax * AD;
   uint8_t* vw = vl[wave];
+  // every cached key and value row is read once per call: non-temporal loads
+  auto load_once = [](const uint16_t* p) -> uint4 {
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
   // block registers: V rows 8 j + lane / 8 (16 bytes each) and the K fragments
   // of rows 16 kt + l16; the next block is fetched while the current one is used
   uint4 kA[8], vA[8], kB[8], vB[8];
@@ -314,15 +319,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = key0 + 8 * j + (lane >> 3);
-      vr[j] = key < k1 ? *reinterpret_cast<const uint4*>(vc + cache_base + (size_t)key * AD + 8 * (lane & 7))
+      vr[j] = key < k1 ? load_once(vc + cache_base + (size_t)key * AD + 8 * (lane & 7))
                        : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int key = key0 + 16 * kt + l16;
       const uint16_t* pk = kc + cache_base + (size_t)key * AD + 8 * g;
-      kr[2 * kt] = key < k1 ? *reinterpret_cast<const uint4*>(pk) : make_uint4(0u, 0u, 0u, 0u);
-      kr[2 * kt + 1] = key < k1 ? *reinterpret_cast<const uint4*>(pk + 32) : make_uint4(0u, 0u, 0u, 0u);
+      kr[2 * kt] = key < k1 ? load_once(pk) : make_uint4(0u, 0u, 0u, 0u);
+      kr[2 * kt + 1] = key < k1 ? load_once(pk + 32) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
   auto block = [&](int key0, const uint4 (&kr)[8], const uint4 (&vr)[8], uint4 (&kn)[8], uint4 (&vn)[8]) {
