@@ -65,6 +65,7 @@ DECODE = [
     (6, 8, 2, 1100, [1, 256, 257, 1100, 1023, 513]),   # 256-key splits
     (40, 16, 8, 2000, None),                         # 512-key splits
     (48, 8, 8, 2100, [1, 512, 513, 2100, 1024, 1025] * 8),
+    (300, 8, 8, 600, None),                          # one split covers the cache
 ]
 
 
