@@ -333,67 +333,26 @@ __global__ __launch_bounds__(256) void router_kernel(
   for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
 
-// Top-k + softmax of one token by one thread, from its logits in LDS (the
-// same 64-bit keys, ties and softmax as topk_emit): every key passes through
-// a sorted list of k entries (compare-exchange down the list).  Writes the
-// picks, the weights, the histogram and optionally an LDS copy of the picks
-// and the token's bit in the per-expert token masks.
-__device__ void topk_thread(const float* sl_row, const float* sbr, int E, int k, int gate_mode,
-                            int t, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-                            int* shist, int* spick_row, uint32_t* smask_lo, uint32_t* smask_hi,
-                            int tl) {
-  uint64_t best[kMaxTopK];
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) best[s] = 0ull;
-  for (int e = 0; e < E; ++e) {
-    uint64_t carry = ((uint64_t)ordered_key(sl_row[e] + sbr[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-      if (s < k) {
-        const uint64_t b = best[s];
-        best[s] = carry > b ? carry : b;
-        carry = carry > b ? b : carry;
-      }
-    }
-  }
-  const float l0 = key_value((uint32_t)(best[0] >> 32));
-  float ex[kMaxTopK];
-  float sum = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    ex[s] = s < k ? expf(key_value((uint32_t)(best[s] >> 32)) - l0) : 0.f;
-    sum += ex[s];
-  }
-  if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits, in expert order
-    sum = 0.f;
-    for (int e = 0; e < E; ++e) sum += expf(sl_row[e] + sbr[e] - l0);
-  }
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    if (s < k) {
-      const int e = (int)(0xffffffffu - (uint32_t)best[s]);
-      topk_idx[(size_t)t * k + s] = e;
-      topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
-      atomicAdd(&shist[e], 1);
-      if (spick_row) spick_row[s] = e;
-      if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
-    }
-  }
-}
-
-// Top-k + softmax of up to RT_TT tokens with eight lanes per token (all 512
-// threads of the workgroup): lane j of a token's group holds the keys of
-// experts j, j + 8, ...; each of the k rounds takes the group maximum with
-// three lane exchanges and clears the winner.  The keys are those of
-// topk_thread, so the picks are identical.  Lane s < k of the group writes
-// pick s, counts it, and marks the token in the expert's mask.
+// Top-k + softmax of the RT_TT tokens tt0.. of a router tile with eight lanes
+// per token (all 512 threads of the workgroup), from their logits in LDS (sl
+// [RT_TT][EP + 8]: the eight tokens of a wave start 8 banks apart, so a
+// wave's 64 reads of one round hit 64 distinct banks).
+// Lane j of a token's group holds the 64-bit keys of experts j, j + 8, ...
+// (ordered logit bits, then the complemented expert index, so ties go to the
+// lower index and every pick is a valid, distinct expert); each of the k
+// rounds takes the group maximum with three lane exchanges and clears the
+// winner.  Lane s < k of the group writes pick s and its weight (softmax over
+// the selected logits, or over all E for kGateSoftmaxAll), counts it in the
+// tile histogram and, when given, records it in spick and the token's bit in
+// the expert's token mask.
 template <int EP>
-__device__ void topk_group8(const float* sl, const float* sbr, int T, int E, int k, int gate_mode,
-                            int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int* shist,
-                            int* spick, uint32_t* smask_lo, uint32_t* smask_hi) {
+__device__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, int E, int k,
+                            int gate_mode, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+                            int* shist, int* spick, uint32_t* smask_lo, uint32_t* smask_hi) {
   constexpr int KPL = EP / 8;  // keys per lane
-  const int t = threadIdx.x >> 3, sub = threadIdx.x & 7;
-  const float* row = sl + t * (EP + 1);
+  const int tl = threadIdx.x >> 3, sub = threadIdx.x & 7;
+  const int t = tt0 + tl;
+  const float* row = sl + tl * (EP + 8);
   uint64_t key[KPL];
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
@@ -445,14 +404,14 @@ __device__ void topk_group8(const float* sl, const float* sbr, int T, int E, int
       topk_idx[(size_t)t * k + s] = e;
       topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
       atomicAdd(&shist[e], 1);
-      spick[t * k + s] = e;
-      atomicOr(t < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (t & 31));
+      if (spick) spick[tl * k + s] = e;
+      if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
     }
   }
 }
 
-// Logits of the tile's RT_TT tokens into sl [RT_TT][EP + 1] (odd pitch: the
-// per-token readers of topk_thread hit distinct banks): the sum of every
+// Logits of the tile's RT_TT tokens into sl [RT_TT][EP + 8] (the pitch of
+// topk_group8): the sum of every
 // (token, expert) partial in split order.  A thread takes 4 experts of one
 // token (one float4 per split, up to 16 splits in flight per round).
 template <int EP>
@@ -482,7 +441,7 @@ __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int 
           }
       }
     }
-    float* dst = sl + tl * (EP + 1) + e4;
+    float* dst = sl + tl * (EP + 8) + e4;
     dst[0] = s.x;
     dst[1] = s.y;
     dst[2] = s.z;
@@ -501,7 +460,7 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
                                                              float* __restrict__ topk_w,
                                                              int32_t* __restrict__ hist) {
   constexpr int EP = NBW * 16;
-  __shared__ float sl[RT_TT * (EP + 1)];
+  __shared__ float sl[RT_TT * (EP + 8)];
   __shared__ int shist[kMaxExperts];
   __shared__ float sbr[kMaxExperts];
   const int tid = threadIdx.x;
@@ -512,10 +471,7 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
   }
   sum_partials<EP>(partial, nsplit, T, tt0, sl, 512);
   __syncthreads();  // the sums are in LDS, shist and sbr are set
-  const int t = tt0 + tid;
-  if (tid < RT_TT && t < T)
-    topk_thread(sl + tid * (EP + 1), sbr, E, k, gate_mode, t, topk_idx, topk_w, shist, nullptr,
-                nullptr, nullptr, 0);
+  topk_group8<EP>(sl, sbr, tt0, T, E, k, gate_mode, topk_idx, topk_w, shist, nullptr, nullptr, nullptr);
   __syncthreads();  // the histogram atomics are done
   for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
 }
@@ -536,7 +492,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     int32_t* __restrict__ row_token) {
   constexpr int EP = NBW * 16;
   static_assert(RT_TT * 8 == 512, "the top-k takes eight lanes per token");
-  __shared__ float sl[RT_TT * (EP + 1)];
+  __shared__ float sl[RT_TT * (EP + 8)];
   __shared__ int spick[RT_TT * kMaxTopK];
   __shared__ int scnt[kMaxExperts], soff[kMaxExperts + 1], so0[kMaxExperts + 1], so1[kMaxExperts + 1];
   __shared__ uint32_t smask[2][kMaxExperts];  // tokens (bits) that chose each expert
@@ -555,7 +511,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   }
   __syncthreads();
   if (!have_topk) {
-    topk_group8<EP>(sl, sbr, T, E, k, gate_mode, topk_idx, topk_w, scnt, spick, smask[0], smask[1]);
+    topk_group8<EP>(sl, sbr, 0, T, E, k, gate_mode, topk_idx, topk_w, scnt, spick, smask[0], smask[1]);
   } else {
     for (int p = tid; p < R; p += 512) {
       const int t = p / k;
