@@ -264,7 +264,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the MoE block here is "
-              "built for a single MI355X; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "built for a single MI355X (no sharding across GPUs is built).", file=sys.stderr)
         sys.exit(2)
 
     if args.workload.startswith("attn"):

@@ -215,7 +215,7 @@ def decision_adjusted_reference(dbg: dict, ref: dict, inp: dict):
 
 
 def check_end_to_end(g: np.ndarray, dbg: dict, ref: dict, inp: dict, d_real: int) -> dict:
-    """The spec gates against the oracle; where the literal max gate fails,
+    """The end-to-end accuracy gates against the oracle; where the literal max gate fails,
     the same gate is applied after accounting for the admissible h decisions
     (see check_h_decisions), and both results are returned."""
     o = ref["out64"][:, :d_real]

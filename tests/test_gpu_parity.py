@@ -205,5 +205,5 @@ def test_full_size_sampled(cfg, fmt):
     # changes the E8M0 scale of 32 h values at once (an admissible decision,
     # checked above), so the decision-adjusted gate is the one that applies
     if fmt == "block128":
-        assert m["gate"] == "literal", f"{cfg}: the literal north-star gates must hold on the configs: {m}"
+        assert m["gate"] == "literal", f"{cfg}: the literal end-to-end gates must hold on these workloads: {m}"
     assert np.all(g[:, dr:] == 0)
