@@ -166,8 +166,8 @@ moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_r
  * of at most 64 tokens the router stage performs the whole routing (counts,
  * offsets, tile lists, placement) and the scan and place stages have no work. */
 #define MOE_STAGE_ROUTER 0  /* router logits, top-k, softmax, x quantisation, tile histogram */
-#define MOE_STAGE_SCAN 1    /* expert counts, offsets, per-tile row bases, GEMM tile tables   */
-#define MOE_STAGE_PLACE 2   /* permuted row of every (token, slot)                             */
+#define MOE_STAGE_SCAN 1    /* expert counts, offsets, per-tile row bases, GEMM tile offsets  */
+#define MOE_STAGE_PLACE 2   /* permuted row of every (token, slot); both GEMMs' tile lists     */
 #define MOE_STAGE_GATEUP 3  /* gate/up grouped GEMM + bias + SwiGLU + h quantisation           */
 #define MOE_STAGE_DOWN 4    /* down grouped GEMM + bias                                        */
 #define MOE_STAGE_COMBINE 5 /* weighted sum of each token's k rows -> bf16 out                */

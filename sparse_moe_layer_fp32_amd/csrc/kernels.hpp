@@ -75,14 +75,15 @@ hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, in
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
                              int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream);
 
-// Tile list of one grouped GEMM from its per-expert tile offsets (row blocks
-// of bm rows, n_tiles column tiles, grouped kTileGroup column tiles at a time).
-hipError_t launch_tile_table(const int32_t* tile_off, const int32_t* counts, const int32_t* offsets,
-                             int E, int bm, int n_tiles, int max_tiles, int32_t* tiles,
-                             hipStream_t stream);
-
-hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
-                              int k, int32_t* row_of, int32_t* row_token, hipStream_t stream);
+// After the scan: the row of every (token, slot) pair (rank among the earlier
+// pairs of its router tile with the same expert), and the tile lists of both
+// grouped GEMMs from their per-expert tile offsets (row blocks of bm rows,
+// nt column tiles, grouped kTileGroup column tiles at a time), in one launch.
+hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
+                                     int k, int32_t* row_of, int32_t* row_token, const int32_t* counts,
+                                     const int32_t* offsets, const int32_t* tile_off0, int bm0,
+                                     int nt0, int max0, int32_t* tiles0, const int32_t* tile_off1,
+                                     int bm1, int nt1, int max1, int32_t* tiles1, hipStream_t stream);
 
 hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
                           int k, uint16_t* out, hipStream_t stream);

@@ -176,16 +176,12 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         if (small) break;  // done by the router stage
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
                                      tile_base, tile_off0, tile_off1, stream);
-        if (err == hipSuccess)
-          err = moe::launch_tile_table(tile_off0, counts, offsets, E, gs.bm, nt_g, max_g, tiles0,
-                                       stream);
-        if (err == hipSuccess)
-          err = moe::launch_tile_table(tile_off1, counts, offsets, E, ps.bm, nt_p, max_p, tiles1,
-                                       stream);
         break;
       case MOE_STAGE_PLACE:
         if (small) break;  // done by the router stage
-        err = moe::launch_route_place(topk_idx, tile_base, T, E, k, row_of, row_token, stream);
+        err = moe::launch_route_place_tables(topk_idx, tile_base, T, E, k, row_of, row_token, counts,
+                                             offsets, tile_off0, gs.bm, nt_g, max_g, tiles0, tile_off1,
+                                             ps.bm, nt_p, max_p, tiles1, stream);
         break;
       case MOE_STAGE_GATEUP: {
         moe::GemmArgs g{};

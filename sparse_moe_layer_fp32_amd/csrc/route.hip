@@ -108,16 +108,13 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   }
 }
 
-// One workgroup per router tile: rank of every (token, slot) pair among the
-// earlier pairs of the tile with the same expert (a token never picks an
-// expert twice, so this is the token order).
-__global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_kernel(const int32_t* __restrict__ topk_idx,
-                                                          const int32_t* __restrict__ tile_base,
-                                                          int T, int E, int k,
-                                                          int32_t* __restrict__ row_of,
-                                                          int32_t* __restrict__ row_token) {
-  __shared__ int se[RT_TT * kMaxTopK];
-  const int tl = blockIdx.x, t0 = tl * RT_TT;
+// Rank of every (token, slot) pair of router tile tl among the earlier pairs
+// of the tile with the same expert (a token never picks an expert twice, so
+// this is the token order), and its row.
+__device__ void place_tile(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ tile_base,
+                           int tl, int T, int E, int k, int32_t* __restrict__ row_of,
+                           int32_t* __restrict__ row_token, int* se) {
+  const int t0 = tl * RT_TT;
   const int n = min(RT_TT, T - t0) * k;
   const int p = threadIdx.x;
   if (p < n) se[p] = topk_idx[(size_t)t0 * k + p];
@@ -132,30 +129,56 @@ __global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_kernel(const int
   }
 }
 
-// Entry L of the tile list: the expert whose tiles hold L (binary search of
-// the tile offsets), then inside the expert the order (column group of
-// kTileGroup tiles, row block, column tile), so that consecutive tiles share
-// one slice of the expert's weights.
-__global__ __launch_bounds__(256) void tile_table_kernel(const int32_t* __restrict__ tile_off,
-                                                        const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets, int E,
-                                                        int bm, int n_tiles, int max_tiles,
-                                                        int4* __restrict__ tiles) {
+// Entries L = first, first + stride, ... of a GEMM's tile list: the expert
+// whose tiles hold L (binary search of the tile offsets), then inside the
+// expert the order (column group of kTileGroup tiles, row block, column
+// tile), so that consecutive tiles share one slice of the expert's weights.
+__device__ void tile_entries(const int32_t* __restrict__ tile_off, const int32_t* __restrict__ counts,
+                             const int32_t* __restrict__ offsets, int E, int bm, int n_tiles,
+                             int max_tiles, int4* __restrict__ tiles, int first, int stride) {
   const int total = min(tile_off[E], max_tiles);
-  for (int L = blockIdx.x * 256 + threadIdx.x; L < total; L += gridDim.x * 256) {
+  for (int L = first; L < total; L += stride) {
     int lo = 0, hi = E;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (tile_off[mid] <= L) lo = mid; else hi = mid;
     }
     const int cnt = counts[lo];
-    const int mt = ceil_div(cnt, bm);
     const int local = L - tile_off[lo];
+    if (cnt <= bm) {  // one row block: the entries are the column tiles in order
+      tiles[L] = make_int4(lo, offsets[lo], cnt, local);
+      continue;
+    }
+    const int mt = ceil_div(cnt, bm);
     const int ng = local / (mt * kTileGroup);
     const int rem = local - ng * mt * kTileGroup;
     const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
     const int m = rem / gw;
     tiles[L] = make_int4(lo, offsets[lo] + m * bm, min(bm, cnt - m * bm), ng * kTileGroup + rem % gw);
+  }
+}
+
+// After the scan, in one launch: workgroups [0, nt) place router tile
+// blockIdx.x, the next g0 build the gate/up GEMM's tile list and the last g1
+// the down GEMM's (the three only read the scan's results).
+__global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_tables_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ tile_base, int T, int E, int k,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ row_token, int nt,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ tile_off0, int bm0, int n_tiles0, int max0, int4* __restrict__ tiles0,
+    int g0, const int32_t* __restrict__ tile_off1, int bm1, int n_tiles1, int max1,
+    int4* __restrict__ tiles1, int g1) {
+  __shared__ int se[RT_TT * kMaxTopK];
+  constexpr int NTH = RT_TT * kMaxTopK;
+  const int b = blockIdx.x;
+  if (b < nt) {
+    place_tile(topk_idx, tile_base, b, T, E, k, row_of, row_token, se);
+  } else if (b < nt + g0) {
+    tile_entries(tile_off0, counts, offsets, E, bm0, n_tiles0, max0, tiles0, (b - nt) * NTH + threadIdx.x,
+                 g0 * NTH);
+  } else {
+    tile_entries(tile_off1, counts, offsets, E, bm1, n_tiles1, max1, tiles1,
+                 (b - nt - g0) * NTH + threadIdx.x, g1 * NTH);
   }
 }
 
@@ -209,20 +232,19 @@ hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, in
   return hipGetLastError();
 }
 
-hipError_t launch_route_place(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
-                              int k, int32_t* row_of, int32_t* row_token, hipStream_t stream) {
-  hipLaunchKernelGGL(route_place_kernel, dim3(ceil_div(T, RT_TT)), dim3(RT_TT * kMaxTopK), 0, stream, topk_idx,
-                     tile_base, T, E, k, row_of, row_token);
-  return hipGetLastError();
-}
-
-hipError_t launch_tile_table(const int32_t* tile_off, const int32_t* counts, const int32_t* offsets,
-                             int E, int bm, int n_tiles, int max_tiles, int32_t* tiles,
-                             hipStream_t stream) {
-  if (max_tiles <= 0) return hipSuccess;
-  const int grid = std::min(1024, ceil_div(max_tiles, 256));
-  hipLaunchKernelGGL(tile_table_kernel, dim3(grid), dim3(256), 0, stream, tile_off, counts, offsets,
-                     E, bm, n_tiles, max_tiles, reinterpret_cast<int4*>(tiles));
+hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
+                                     int k, int32_t* row_of, int32_t* row_token, const int32_t* counts,
+                                     const int32_t* offsets, const int32_t* tile_off0, int bm0,
+                                     int nt0, int max0, int32_t* tiles0, const int32_t* tile_off1,
+                                     int bm1, int nt1, int max1, int32_t* tiles1, hipStream_t stream) {
+  constexpr int NTH = RT_TT * kMaxTopK;
+  const int nt = ceil_div(T, RT_TT);
+  const int g0 = max0 > 0 ? std::min(1024, ceil_div(max0, NTH)) : 0;
+  const int g1 = max1 > 0 ? std::min(1024, ceil_div(max1, NTH)) : 0;
+  hipLaunchKernelGGL(route_place_tables_kernel, dim3(nt + g0 + g1), dim3(NTH), 0, stream, topk_idx,
+                     tile_base, T, E, k, row_of, row_token, nt, counts, offsets, tile_off0, bm0, nt0,
+                     max0, reinterpret_cast<int4*>(tiles0), g0, tile_off1, bm1, nt1, max1,
+                     reinterpret_cast<int4*>(tiles1), g1);
   return hipGetLastError();
 }
 
