@@ -61,7 +61,7 @@ size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
  *   sinks    fp32 [Hq]
  *   out      bf16 [B, Hq, D]     written
  * Keys are split in parts of 256 * 2^j (one wave each; j grows while the
- * waves B * Hkv * splits exceed what the chip holds at once) and merged by a
+ * waves B * Hkv * splits exceed one per SIMD of the chip) and merged by a
  * second kernel; Hq / Hkv must be at most 16. */
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_len, const float* sinks, void* out, int32_t B,

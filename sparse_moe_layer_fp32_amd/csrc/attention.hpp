@@ -6,12 +6,12 @@
 namespace moe {
 
 constexpr int kMinSplitKeys = 256;    // smallest decode split
-constexpr int kResidentWaves = 2048;  // decode waves the chip holds at once (2 per SIMD)
+constexpr int kResidentWaves = 1024;  // decode waves: one per SIMD
 constexpr int kPartFloats = 68;       // per (sequence, head, split): O[64], max, sum, 2 pad (16-byte records)
 
 // Keys per decode split: the smallest 256 * 2^j that keeps B * Hkv * splits
-// within one resident round of waves (longer splits hide more latency per
-// wave; more splits than resident waves only queue).
+// within one wave per SIMD (a wave streams its split with two blocks in
+// flight; more, shorter splits measured slower at every batch shape tried).
 int attn_decode_split_keys(int B, int Hkv, int Lmax);
 // splits of a decode call, and the most any (B, Hkv) can need for Lmax
 int attn_decode_splits(int B, int Hkv, int Lmax);

@@ -63,8 +63,9 @@ DECODE = [
     # (B, Hq, Hkv, Lmax, lengths or None for seeded ragged lengths)
     (4, 8, 1, 300, None), (16, 64, 8, 1024, None), (3, 16, 1, 513, None), (5, 4, 4, 64, None),
     (6, 8, 2, 1100, [1, 256, 257, 1100, 1023, 513]),   # 256-key splits
-    (40, 16, 8, 2000, None),                         # 512-key splits
-    (48, 8, 8, 2100, [1, 512, 513, 2100, 1024, 1025] * 8),
+    (24, 8, 8, 1500, [1, 512, 513, 1500, 1023, 1024] * 4),   # 512-key splits
+    (40, 16, 8, 2000, None),                         # 1024-key splits
+    (48, 8, 8, 2100, [1, 2048, 2049, 2100, 1024, 1025] * 8),   # 2048-key splits
     (300, 8, 8, 600, None),                          # one split covers the cache
 ]
 
