@@ -34,6 +34,7 @@ constexpr int ABK = 64;         // keys per block
 constexpr int APITCH = 144;     // LDS bytes per key row (128 + 16: rows on distinct banks)
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kAttnQt = 2;      // prefill query tiles (16 rows) per wave: 16 waves of 32 rows
+constexpr uint32_t kOnes2 = 0x3f803f80u;  // two bf16 ones
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -120,14 +121,19 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
       qf[qt][c] = r < S ? *reinterpret_cast<const uint4*>(q + ((size_t)r * Hq + h) * AD + 32 * c + 8 * g)
                         : make_uint4(0u, 0u, 0u, 0u);
   }
-  // running max (log2 domain) per query column, per-lane partial sums, O^T
-  float m[QT], l[QT];
+  // running max (log2 domain) per query column, the sink's term of the sum,
+  // O^T, and the sum of the probabilities: an MFMA of an all-ones A operand
+  // with P^T, whose 16 rows all hold the column sums (one MFMA instead of
+  // eight adds per lane and qt; it sums the bf16 P that the P V product uses)
+  float m[QT], sterm[QT];
+  v4f lsum[QT];
   v4f o[4][QT];  // [dt][qt]: dims 16 dt + 4 g + i, query 16 qt + l16
   const float sink2 = sinks[h] * kLog2e;
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    m[qt] = sink2;                 // the sink seeds the running maximum ...
-    l[qt] = g == 0 ? 1.0f : 0.0f;  // ... and contributes exp2(0) = 1 to the sum (once per query)
+    m[qt] = sink2;     // the sink seeds the running maximum ...
+    sterm[qt] = 1.0f;  // ... and contributes exp2(0) = 1 to the sum
+    lsum[qt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt][qt] = v4f{0.f, 0.f, 0.f, 0.f};
   }
@@ -208,23 +214,22 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
           const float alpha = ex2(m[qt] - mn);
           m[qt] = mn;
           float pr[2][4];
-          float sum = 0.f;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              pr[kt][i] = ex2(fmaf(s[kt][qt][i], scale2, -mn));
-              sum += pr[kt][i];
-            }
-          l[qt] = fmaf(l[qt], alpha, sum);
-          // O is rescaled only when some query's maximum moved (rare once it settles)
+            for (int i = 0; i < 4; ++i) pr[kt][i] = ex2(fmaf(s[kt][qt][i], scale2, -mn));
+          // O and the sum are rescaled only when some query's maximum moved
+          // (rare once it settles)
           if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
+            lsum[qt] *= alpha;
+            sterm[qt] *= alpha;
           }
           // B operand of the PV MFMA: keys kh0 + 4 g + j, then kh0 + 16 + 4 g + j
           pb[qt] = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
                               pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
+          lsum[qt] = mfma_bf16(make_uint4(kOnes2, kOnes2, kOnes2, kOnes2), pb[qt], lsum[qt]);
         }
         // O^T += V^T P^T: lanes of group g address key rows 32p + 4g + i/4 (and +16),
         // dims 16 dt + 4 (i % 4)
@@ -250,10 +255,10 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
     if (kb + 1 < nblk) block(kb + 1, lr1, lr0);
   }
 
-  // out[query][h][d] = O^T[d][query] / sum; the four lanes of a query hold partial sums
+  // out[query][h][d] = O^T[d][query] / sum
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const float inv = 1.0f / sum4(l[qt]);
+    const float inv = 1.0f / (lsum[qt][0] + sterm[qt]);
     const int r = row0 + 16 * qt + l16;
     if (r >= S) continue;
     uint16_t* po = out + ((size_t)r * Hq + h) * AD + 4 * g;
