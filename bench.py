@@ -252,7 +252,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # compute-bound kernels reach their steady clock after about 20 launches
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS) + ["attn_decode", "attn_prefill"])
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),

@@ -211,16 +211,17 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
 #pragma unroll
             for (int i = 0; i < 4; ++i) bm = fmaxf(bm, s[kt][qt][i]);
           const float mn = fmaxf(m[qt], max4(bm) * scale2);
-          const float alpha = ex2(m[qt] - mn);
+          // O and the sum are rescaled only when some query's maximum moved
+          // (rare once it settles); the factor's exp2 is skipped otherwise
+          const bool moved = __builtin_amdgcn_ballot_w64(mn != m[qt]) != 0;
+          const float alpha = moved ? ex2(m[qt] - mn) : 1.0f;
           m[qt] = mn;
           float pr[2][4];
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) pr[kt][i] = ex2(fmaf(s[kt][qt][i], scale2, -mn));
-          // O and the sum are rescaled only when some query's maximum moved
-          // (rare once it settles)
-          if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+          if (moved) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) o[dt][qt] *= alpha;
             lsum[qt] *= alpha;
