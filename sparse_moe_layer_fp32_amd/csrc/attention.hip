@@ -51,13 +51,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{a, b}, v2bf));
 }
 
+// IEEE maximum (v_maximum3_f32): unlike fmaxf it needs no quieting of its
+// operands first, which the compiler otherwise adds for values that come out
+// of lane swaps (two extra VALU operations per maximum)
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // max / sum over the four lanes l, l^16, l^32, l^48 (one query column of an
 // S^T tile) with the VALU lane swaps (no LDS round trip)
 __device__ __forceinline__ float max4(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float sum4(float x) {
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) bm = fmaxf(bm, s[kt][qt][i]);
-          const float mn = fmaxf(m[qt], max4(bm) * scale2);
+          const float mn = vmax(m[qt], max4(bm) * scale2);
           // O and the sum are rescaled only when some query's maximum moved
           // (rare once it settles); the factor's exp2 is skipped otherwise
           const bool moved = __builtin_amdgcn_ballot_w64(mn != m[qt]) != 0;
@@ -356,7 +361,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         if (key0 + 16 * kt + 4 * g + i >= k1) s[kt][i] = -INFINITY;  // past the sequence
         bm = fmaxf(bm, s[kt][i]);
       }
-    const float mn = fmaxf(m, max4(bm) * scale2);  // finite: the block has a valid key
+    const float mn = vmax(m, max4(bm) * scale2);  // finite: the block has a valid key
     const float alpha = ex2(m - mn);
     m = mn;
     float sum = 0.f;
