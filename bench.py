@@ -53,24 +53,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 271547.388, "write_kib": 759.212,
-        "copy_fetch_kib": 524313.375, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 892949.850, "write_kib": 104093.375,
-        "copy_fetch_kib": 524304.625, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 279936.237, "write_kib": 761.312,
-        "copy_fetch_kib": 524308.1875, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 943960.250, "write_kib": 103747.981,
-        "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 144505.275, "write_kib": 760.025,
-        "copy_fetch_kib": 524314.5625, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "bd42b3877f0e534f4f0f8edb3481bfe58c75b225b04115eaf107af0f6114bbd1",
-        "fetch_kib": 579798.912, "write_kib": 103726.762,
-        "copy_fetch_kib": 524306.25, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 271558.550, "write_kib": 759.206,
+        "copy_fetch_kib": 524311.75, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 878063.162, "write_kib": 104024.725,
+        "copy_fetch_kib": 524307.5, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 279949.650, "write_kib": 761.038,
+        "copy_fetch_kib": 524306.5625, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 941940.488, "write_kib": 103693.331,
+        "copy_fetch_kib": 524307.8125, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 144512.788, "write_kib": 759.400,
+        "copy_fetch_kib": 524311.3125, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
+        "fetch_kib": 580615.450, "write_kib": 103850.550,
+        "copy_fetch_kib": 524305.375, "copy_write_kib": 1048576.0},
 }
 
 

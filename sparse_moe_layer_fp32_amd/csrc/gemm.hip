@@ -265,8 +265,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // loads that must read zeros get an offset past the buffer, which stays past
   // it when the K-block stride is added
   v4i rB;
+  // weights read once (the expert's rows fit one row block) stream with the
+  // non-temporal policy; an expert with more row blocks keeps them cacheable
+  // for its other tiles, which read the same weight slices
+  bool b_once = true;
   auto setup = [&](const DmaTile& t, int buf) {
     const int n0 = t.nt * (GATED ? kBlock : BNP);
+    b_once = ((const const_i32*)g.counts)[t.e] <= BM;
     rB = dma_rsrc(g.B + (size_t)t.e * S::KR * nkb * N, (uint32_t)(S::KR * nkb) * (uint32_t)N);
 #pragma unroll
     for (int q = 0; q < S::A_PER; ++q) {  // A: 1 KB chunk c = rows 8c..8c+7; wave w: A_PER chunks
@@ -314,7 +319,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
         dma16<MX>(rA, sbase + (S::A_PER * wave + q) * 1024, aoff[q] + ka);
 #pragma unroll
     for (int q = 0; q < S::B_PER; ++q)
-      dma16<MX, true>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
+      if (b_once) dma16<MX, true>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
+      else dma16<MX, false>(rB, sbase + DMA_SA + (S::B_PER * wave + q) * 1024, boff[q] + kb);
     dma4<MX>(rSide, sbase + DMA_SA + DMA_SB + side_dst, soff + (uint32_t)(kbl * side_step));
     ++kbl;
   };
