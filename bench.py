@@ -53,24 +53,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 271558.550, "write_kib": 759.206,
-        "copy_fetch_kib": 524311.75, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 878063.162, "write_kib": 104024.725,
-        "copy_fetch_kib": 524307.5, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 279949.650, "write_kib": 761.038,
-        "copy_fetch_kib": 524306.5625, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 941940.488, "write_kib": 103693.331,
-        "copy_fetch_kib": 524307.8125, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 144512.788, "write_kib": 759.400,
-        "copy_fetch_kib": 524311.3125, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "0d120ec65ddb88c4714895ecc0e2dcefd9ab9cfcd1d141a44130826c66be9d81",
-        "fetch_kib": 580615.450, "write_kib": 103850.550,
-        "copy_fetch_kib": 524305.375, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 271558.388, "write_kib": 759.281,
+        "copy_fetch_kib": 524307.875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 893061.338, "write_kib": 103759.700,
+        "copy_fetch_kib": 524308.0625, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 279949.487, "write_kib": 760.731,
+        "copy_fetch_kib": 524308.9375, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 946794.100, "write_kib": 103701.650,
+        "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 144512.725, "write_kib": 759.725,
+        "copy_fetch_kib": 524313.875, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
+        "fetch_kib": 576616.713, "write_kib": 103708.881,
+        "copy_fetch_kib": 524305.625, "copy_write_kib": 1048576.0},
 }
 
 
