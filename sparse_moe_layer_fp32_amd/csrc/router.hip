@@ -480,7 +480,7 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
 // regime) in one workgroup: the split partials are summed in split order,
 // then top-k + softmax, the expert counts and offsets (exclusive scan), the
 // stable placement of every (token, slot) pair, and the tile lists of both
-// GEMMs (the same entries as tile_table_kernel).  With one split the router
+// GEMMs (the same entries as route_place_tables_kernel writes).  With one split the router
 // already chose the experts (have_topk) and only the rest runs here.
 template <int NBW>
 __global__ __launch_bounds__(512) void route_small_kernel(
