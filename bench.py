@@ -53,24 +53,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 271558.388, "write_kib": 759.281,
-        "copy_fetch_kib": 524307.875, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 893061.338, "write_kib": 103759.700,
-        "copy_fetch_kib": 524308.0625, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 279949.487, "write_kib": 760.731,
-        "copy_fetch_kib": 524308.9375, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 946794.100, "write_kib": 103701.650,
-        "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 144512.725, "write_kib": 759.725,
-        "copy_fetch_kib": 524313.875, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "bcec0e7c595b074390b496028becb3eb1eda4d93dfaed1375353bc5ff81c304f",
-        "fetch_kib": 576616.713, "write_kib": 103708.881,
-        "copy_fetch_kib": 524305.625, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 271558.525, "write_kib": 759.269,
+        "copy_fetch_kib": 524307.0, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 923734.450, "write_kib": 103737.319,
+        "copy_fetch_kib": 524306.5625, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 279949.575, "write_kib": 760.781,
+        "copy_fetch_kib": 524307.0625, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 953680.037, "write_kib": 103674.794,
+        "copy_fetch_kib": 524306.125, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 144512.775, "write_kib": 759.413,
+        "copy_fetch_kib": 524311.875, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
+        "fetch_kib": 580680.725, "write_kib": 103735.169,
+        "copy_fetch_kib": 524304.5625, "copy_write_kib": 1048576.0},
 }
 
 

@@ -938,11 +938,12 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
         wf[nb][2 * r] = t[0];
         wf[nb][2 * r + 1] = t[1];
       }
-    // MB * NB MFMAs j = 4 mb + nb; the FMAs of MFMA j follow MFMA j + 2
+    // MB * NB MFMAs j = 4 mb + nb; the FMAs of MFMA j follow MFMA j + 3, by
+    // when its result is ready (two behind measured 1.4 % slower)
     v4f pp[MB * NB];
     v8i xf[MB];
 #pragma unroll
-    for (int j = 0; j < MB * NB + 2; ++j) {
+    for (int j = 0; j < MB * NB + 3; ++j) {
       if (j < MB * NB) {
         const int mb = j >> 2, nb = j & 3;
         if (nb == 0) {
@@ -953,8 +954,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
         }
         pp[j] = mfma_fp8_16x16x128(wf[nb], xf[mb], v4f{0.f, 0.f, 0.f, 0.f});
       }
-      if (j >= 2) {
-        const int q = j - 2, mb = q >> 2, nb = q & 3;
+      if (j >= 3) {
+        const int q = j - 3, mb = q >> 2, nb = q & 3;
         const float sa = mb < 4 ? sl[mb] : sh[mb - 4];
         const float s = sa * ((GATED && nb >= 2) ? sb1 : sb0);
 #pragma unroll
@@ -962,7 +963,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       }
       // keep each MFMA ahead of the promotions that follow it in this order:
       // left free, the scheduler pulls them next to the MFMA whose result
-      // they read and stalls on it (c2 gate/up 659 -> 650 us)
+      // they read and stalls on it
       __builtin_amdgcn_sched_barrier(0);
     }
   };
