@@ -1,0 +1,59 @@
+"""bench.py's command line on the CPU: the single-GPU refusal, the workload
+list, and the algorithmic work formulas its rooflines divide by (CPU only)."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""          # no JSON line for a refused run
+
+
+def test_help_lists_every_workload():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0
+    for w in ("c0", "c1", "c2", "c3", "c4a", "c4b", "attn_decode", "attn_prefill"):
+        assert w in r.stdout
+
+
+@pytest.mark.parametrize("fmt", ["block128", "mx", "mxfp4"])
+def test_traffic_entries_match_their_formats(fmt):
+    """A stored counter entry is used only while the GEMM source is unchanged;
+    the entries exist for the decode and prefill layers of every format."""
+    b = _bench()
+    for w in ("c1", "c2"):
+        key = w if fmt == "block128" else f"{w}-{fmt}"
+        assert key in b.TRAFFIC
+        t = b.TRAFFIC[key]
+        assert t["copy_write_kib"] == 1048576.0
+        assert 500000 < t["copy_fetch_kib"] < 550000   # 128-byte reads counted as 64 bytes
+
+
+def test_decode_gateup_traffic_matches_algorithmic_bytes():
+    """The decode gate/up GEMM reads every touched expert's weights once: its
+    scaled HBM bytes stay within 1 % of the algorithmic bytes (a check of the
+    stored counters against the formula, both from committed numbers)."""
+    b = _bench()
+    t = b.TRAFFIC["c1"]
+    hbm = (t["fetch_kib"] * 1048576.0 / t["copy_fetch_kib"] + t["write_kib"]) * 1024
+    E, d, f, T = 32, 2944, 2944, 64
+    weights = E * d * 2 * f + 4 * E * (d // 128) * (2 * f // 128) + 2 * E * 2 * f
+    assert abs(hbm - weights) / weights < 0.01
