@@ -46,8 +46,9 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
                              void* out, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
                              float sm_scale, void* stream);
 
-/* Bytes of device workspace attn_sink_decode needs (the per-split partial
- * results: at most B * Hq * ceil(Lmax / 256) records of 68 floats). */
+/* Bytes of device workspace attn_sink_decode needs (the partial results of
+ * the sequence pieces the waves hold: min(1024 + 2 B, B (ceil(Lmax / 256) + 2))
+ * * Hq records of 68 floats, then 2 B + 2 int32 of work plan). */
 size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
 
 /* One query per sequence over a KV cache laid out heads major with each
@@ -60,9 +61,10 @@ size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
  *                                [0, Lmax] are clamped; 0 keys give a zero output)
  *   sinks    fp32 [Hq]
  *   out      bf16 [B, Hq, D]     written
- * Keys are split in parts of 256 * 2^j (one wave each; j grows while the
- * waves B * Hkv * splits exceed one per SIMD of the chip) and merged by a
- * second kernel; Hq / Hkv must be at most 16. */
+ * For each key/value head the keys of all sequences are cut into equal
+ * ranges of at least 256 keys, one wave each (one wave per SIMD of the chip
+ * in all), so a wave may hold pieces of several sequences; a second kernel
+ * merges each sequence's pieces; Hq / Hkv must be at most 16. */
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_len, const float* sinks, void* out, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax, float sm_scale,

@@ -20,6 +20,7 @@
 // sm_scale * log2(e) and exponentiated with exp2.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 
 #include "attention.hpp"
@@ -277,52 +278,75 @@ __global__ __launch_bounds__(64 * (32 / QT)) void attn_prefill_kernel(const uint
 }
 
 // ---------------------------------------------------------------------------
-// Decode: one wave per (sequence b, key/value head, split of skeys keys);
-// its G <= 16 query heads form the 16 MFMA columns (the rest are zero).  K
-// fragments come straight from the cache (a lane reads 16 bytes of one key
-// row); each 64-key block of V is staged in the wave's own LDS slice for the
-// transposing reads.  Both are loaded to registers one block ahead, so a
-// wave keeps 16 KB of loads in flight while it computes.  The split's
-// running max, partial sum and O go to the
-// workspace; split 0 starts from the sink (max = sink, sum = 1), the others
-// from an empty softmax (max = -inf, sum = 0).
-__global__ __launch_bounds__(256) void attn_decode_kernel(
+// Decode, balanced over the waves: for each key/value head the cached keys of
+// all sequences, taken one sequence after the other (offset P_b for sequence
+// b), are cut into wk ranges of Q = max(kMinSplitKeys, ceil(total / wk)) keys,
+// one per wave, so every wave streams the same amount whatever the length mix.
+// A range can hold pieces of several sequences; each piece (b, keys k0..k1 of
+// b) is a segment with its own running max, sum and O, written to record slot
+// base_b + (its index among b's segments); the segment that starts at key 0
+// of b also carries the sink (max = sink, sum = 1), the others start from an
+// empty softmax.  Every wave derives P_b, the segment counts and base_b from
+// kv_len itself (wave scans over chunks of 64 sequences); wave (0, 0) stores
+// P_b and base_b for the combine.
+//
+// A segment: the G <= 16 query heads of the key/value head are the 16 MFMA
+// columns (the rest are zero); K fragments come straight from the cache (a
+// lane reads 16 bytes of one key row); each 64-key block of V is staged in the
+// wave's own LDS slice for the transposing reads; both are loaded to
+// registers one block ahead.
+__device__ __forceinline__ int wave_excl_scan(int v, int lane) {
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  return incl - v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ kv_len, const float* __restrict__ sinks, float* __restrict__ part,
-    int B, int Hq, int Hkv, int Lmax, int nsplit, int skeys, float scale2) {
+    int32_t* __restrict__ plan, int B, int Hq, int Hkv, int Lmax, int wk, int slots, float scale2) {
   __shared__ __attribute__((aligned(16))) uint8_t vl[4][ABK * APITCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int unit = blockIdx.x * 4 + wave;           // (b, kvh, split), split fastest
-  const int split = unit % nsplit;
-  const int kvh = (unit / nsplit) % Hkv;
-  const int b = unit / (nsplit * Hkv);
-  if (b >= B) return;
+  const int wid = blockIdx.x * 4 + wave;
+  const int kvh = wid / wk, wi = wid % wk;
+  if (kvh >= Hkv) return;
+  const bool planner = wid == 0;                    // stores P_b and base_b
   const int G = Hq / Hkv;
-  const int n = min(max(kv_len[b], 0), Lmax);      // lengths outside [0, Lmax] are clamped
-  const int k0 = split * skeys, k1 = min(n, k0 + skeys);
   const int h = kvh * G + l16;                      // query head of column l16
   const bool hv = l16 < G;
-
-  uint4 qf[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-    qf[c] = hv ? *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h) * AD + 32 * c + 8 * g)
-               : make_uint4(0u, 0u, 0u, 0u);
   const float sink2 = hv ? sinks[h] * kLog2e : 0.f;
-  float m = split == 0 ? sink2 : -INFINITY;
-  float l = (split == 0 && g == 0) ? 1.0f : 0.0f;
-  v4f o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const size_t cache_base = ((size_t)b * Hkv + kvh) * (size_t)Lmax * AD;
+  // total keys per key/value head, then this wave's range [lo, hi); the
+  // lengths of the first 64 sequences are kept for the walk below
+  const int len0 = lane < B ? min(max(kv_len[lane], 0), Lmax) : 0;
+  int tot = len0;
+  for (int c = 64; c < B; c += 64) {
+    const int bb = c + lane;
+    tot += bb < B ? min(max(kv_len[bb], 0), Lmax) : 0;
+  }
+  const int total = wave_sum(tot);
+  const int Q = max(kMinSplitKeys, ceil_div(total, wk));
+  const int64_t lo = (int64_t)wi * Q, hi = lo + Q;
+  if (lo >= total && !planner) return;
+
   uint8_t* vw = vl[wave];
   // every cached key and value row is read once per call: non-temporal loads
   auto load_once = [](const uint16_t* p) -> uint4 {
     const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
     return make_uint4(v[0], v[1], v[2], v[3]);
   };
+  size_t cache_base = 0;
+  int k1 = 0;
   // block registers: V rows 8 j + lane / 8 (16 bytes each) and the K fragments
   // of rows 16 kt + l16; the next block is fetched while the current one is used
   uint4 kA[8], vA[8], kB[8], vB[8];
@@ -341,6 +365,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       kr[2 * kt + 1] = key < k1 ? load_once(pk + 32) : make_uint4(0u, 0u, 0u, 0u);
     }
   };
+  uint4 qf[2];
+  float m = 0.f, l = 0.f;
+  v4f o[4];
   auto block = [&](int key0, const uint4 (&kr)[8], const uint4 (&vr)[8], uint4 (&kn)[8], uint4 (&vn)[8]) {
     if (key0 + ABK < k1) fetch(key0 + ABK, kn, vn);
 #pragma unroll
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (key0 + 16 * kt + 4 * g + i >= k1) s[kt][i] = -INFINITY;  // past the sequence
+        if (key0 + 16 * kt + 4 * g + i >= k1) s[kt][i] = -INFINITY;  // past the segment
         bm = fmaxf(bm, s[kt][i]);
       }
     const float mn = vmax(m, max4(bm) * scale2);  // finite: the block has a valid key
@@ -385,66 +412,147 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const uint8_t* pv = vw + (32 * p + 4 * g + (l16 >> 2)) * APITCH + 2 * (16 * dt + 4 * (l16 & 3));
-        const uint2 lo = tr16(pv);
-        const uint2 hi = tr16(pv + 16 * APITCH);
-        o[dt] = mfma_bf16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb, o[dt]);
+        const uint2 lo2 = tr16(pv);
+        const uint2 hi2 = tr16(pv + 16 * APITCH);
+        o[dt] = mfma_bf16(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y), pb, o[dt]);
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);             // the reads are done before the next block's writes
   };
-  if (k0 < k1) fetch(k0, kA, vA);
-  for (int key0 = k0; key0 < k1; key0 += 2 * ABK) {
-    block(key0, kA, vA, kB, vB);
-    if (key0 + ABK < k1) block(key0 + ABK, kB, vB, kA, vA);
-  }
-  // partials: [b][h][split] = {O[64], m, l, -, -}; the four lanes of a head add their sums
-  l = sum4(l);
-  if (!hv) return;
-  float* pp = part + (((size_t)b * Hq + h) * nsplit + split) * kPartFloats;
-  if (g == 0) {
-    pp[AD] = m;
-    pp[AD + 1] = l;
-  }
+  // one segment: keys k0 .. k1 - 1 of sequence b into record slot `slot`
+  auto segment = [&](int b, int k0, int kend, int slot) {
+    k1 = kend;
+    cache_base = ((size_t)b * Hkv + kvh) * (size_t)Lmax * AD;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    *reinterpret_cast<v4f*>(pp + 16 * dt + 4 * g) = o[dt];
+    for (int c = 0; c < 2; ++c)
+      qf[c] = hv ? *reinterpret_cast<const uint4*>(q + ((size_t)b * Hq + h) * AD + 32 * c + 8 * g)
+                 : make_uint4(0u, 0u, 0u, 0u);
+    m = k0 == 0 ? sink2 : -INFINITY;
+    l = (k0 == 0 && g == 0) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (k0 < k1) fetch(k0, kA, vA);
+    for (int key0 = k0; key0 < k1; key0 += 2 * ABK) {
+      block(key0, kA, vA, kB, vB);
+      if (key0 + ABK < k1) block(key0 + ABK, kB, vB, kA, vA);
+    }
+    // record [slot][h] = {O[64], m, l, -, -}; the four lanes of a head add their sums
+    const float lt = sum4(l);
+    if (!hv || slot < 0 || slot >= slots) return;
+    float* pp = part + ((size_t)slot * Hq + h) * kPartFloats;
+    if (g == 0) {
+      pp[AD] = m;
+      pp[AD + 1] = lt;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      *reinterpret_cast<v4f*>(pp + 16 * dt + 4 * g) = o[dt];
+  };
+
+  // walk the sequences 64 at a time: P_b, segment counts, base_b; run the
+  // segments of this wave's range in sequence order
+  int prun = 0, brun = 0;
+  for (int c = 0; c < B && (prun < hi || planner); c += 64) {
+    const int bb = c + lane;
+    const int len = c == 0 ? len0 : bb < B ? min(max(kv_len[bb], 0), Lmax) : 0;
+    const int P = prun + wave_excl_scan(len, lane);
+    const int cnt = len > 0 ? (P + len - 1) / Q - P / Q + 1 : 0;
+    const int base = brun + wave_excl_scan(cnt, lane);
+    if (planner && bb < B) {
+      plan[bb] = P;
+      plan[B + 1 + bb] = base;
+    }
+    uint64_t mine = __builtin_amdgcn_ballot_w64(bb < B && len > 0 && P < hi && P + len > lo);
+    while (mine) {
+      const int j = __builtin_ctzll(mine);
+      mine &= mine - 1;
+      const int b = c + j;
+      const int Pj = __shfl(P, j), lenj = __shfl(len, j), basej = __shfl(base, j);
+      const int k0 = (int)max((int64_t)0, lo - Pj);
+      const int kend = (int)min((int64_t)lenj, hi - Pj);
+      segment(b, k0, kend, basej + wi - Pj / Q);
+    }
+    prun += wave_sum(len);
+    brun += wave_sum(cnt);
+  }
+  if (planner && lane == 0) {
+    plan[B] = total;
+    plan[2 * B + 1] = brun;
+  }
 }
 
-// out[b][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the splits
-// that hold keys (M = max_s m_s, finite: split 0 carries the sink).
-__global__ __launch_bounds__(64) void attn_combine_kernel(const float* __restrict__ part,
-                                                          const int32_t* __restrict__ kv_len,
-                                                          uint16_t* __restrict__ out, int Hq, int Lmax,
-                                                          int nsplit, int skeys) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  const int b = bh / Hq;
-  const int used = (min(max(kv_len[b], 0), Lmax) + skeys - 1) / skeys;
-  const int ns = used < 1 ? 1 : used;               // split 0 always holds the sink
-  const float* pp = part + (size_t)bh * nsplit * kPartFloats;
+// out[b][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s over the segments
+// of sequence b (M = max_s m_s, finite: the first segment carries the sink);
+// a sequence without keys has the sink alone and a zero output.  One
+// workgroup of W waves per (b, h): wave w takes records w, w + W, ... and the
+// waves add their sums through LDS (W = 4 where a sequence can have tens to
+// hundreds of records, 1 where it has at most 32).
+template <int W>
+__global__ __launch_bounds__(64 * W) void attn_combine_kernel(const float* __restrict__ part,
+                                                              const int32_t* __restrict__ kv_len,
+                                                              const int32_t* __restrict__ plan,
+                                                              uint16_t* __restrict__ out, int B, int Hq,
+                                                              int Lmax, int wk, int slots) {
+  __shared__ float red[W][AD + 1];
+  const int bh = blockIdx.x, t = threadIdx.x, d = t & 63, w = t >> 6;
+  const int b = bh / Hq, h = bh % Hq;
+  const int len = min(max(kv_len[b], 0), Lmax);
+  if (len == 0) {
+    if (w == 0) out[(size_t)bh * AD + d] = 0;
+    return;
+  }
+  const int total = plan[B], P = plan[b], base = plan[B + 1 + b];
+  const int Q = max(kMinSplitKeys, ceil_div(total, wk));
+  const int n = max(0, min((P + len - 1) / Q - P / Q + 1, slots - base));
+  const float* rec = part + ((size_t)base * Hq + h) * kPartFloats;
+  const size_t stride = (size_t)Hq * kPartFloats;  // between consecutive slots
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pp[s * kPartFloats + AD]);
+  for (int s = t; s < n; s += 64 * W) M = fmaxf(M, rec[s * stride + AD]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if constexpr (W > 1) {
+    if (d == 0) red[w][0] = M;
+    __syncthreads();
+    M = red[0][0];
+#pragma unroll
+    for (int i = 1; i < W; ++i) M = fmaxf(M, red[i][0]);
+    __syncthreads();
+  }
   float num = 0.f, den = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(pp[s * kPartFloats + AD] - M);
-    den += w * pp[s * kPartFloats + AD + 1];
-    num += w * pp[s * kPartFloats + d];
+#pragma unroll 4
+  for (int s = w; s < n; s += W) {
+    const float* pp = rec + s * stride;
+    const float wt = exp2f(pp[AD] - M);
+    den = fmaf(wt, pp[AD + 1], den);
+    num = fmaf(wt, pp[d], num);
+  }
+  if constexpr (W > 1) {
+    red[w][d] = num;
+    if (d == 0) red[w][AD] = den;
+    __syncthreads();
+    if (w != 0) return;
+    num = red[0][d];
+    den = red[0][AD];
+#pragma unroll
+    for (int i = 1; i < W; ++i) {
+      num += red[i][d];
+      den += red[i][AD];
+    }
   }
   out[(size_t)bh * AD + d] = f32_to_bf16(num / den);
 }
 
 }  // namespace
 
-int attn_decode_split_keys(int B, int Hkv, int Lmax) {
-  int s = kMinSplitKeys;
-  while (s < Lmax && (int64_t)B * Hkv * ceil_div(Lmax, s) > kResidentWaves) s *= 2;
-  return s;
-}
+int attn_decode_waves(int Hkv) { return std::max(1, kResidentWaves / std::max(1, Hkv)); }
 
-int attn_decode_splits(int B, int Hkv, int Lmax) {
-  return Lmax <= 0 ? 1 : ceil_div(Lmax, attn_decode_split_keys(B, Hkv, Lmax));
+int64_t attn_decode_slots(int B, int Lmax) {
+  // segments of all sequences: at most total / Q + 2 B with total / Q <= the
+  // waves per head (<= kResidentWaves), and at most B (Lmax / kMinSplitKeys + 2)
+  const int64_t by_waves = (int64_t)kResidentWaves + 2 * (int64_t)B;
+  const int64_t by_len = (int64_t)B * (ceil_div(std::max(Lmax, 1), kMinSplitKeys) + 2);
+  return std::min(by_waves, by_len);
 }
-
-int attn_decode_max_splits(int Lmax) { return Lmax <= 0 ? 1 : ceil_div(Lmax, kMinSplitKeys); }
 
 hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                const float* sinks, uint16_t* out, int S, int Hq, int Hkv,
@@ -467,16 +575,21 @@ hipError_t launch_attn_prefill(const uint16_t* q, const uint16_t* k, const uint1
 
 hipError_t launch_attn_decode(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
                               const int32_t* kv_len, const float* sinks, uint16_t* out, float* part,
-                              int B, int Hq, int Hkv, int Lmax, float sm_scale, hipStream_t stream) {
-  const int skeys = attn_decode_split_keys(B, Hkv, Lmax);
-  const int nsplit = ceil_div(Lmax, skeys);
-  const int units = B * Hkv * nsplit;
-  hipLaunchKernelGGL(attn_decode_kernel, dim3(ceil_div(units, 4)), dim3(256), 0, stream, q, kc, vc, kv_len,
-                     sinks, part, B, Hq, Hkv, Lmax, nsplit, skeys, sm_scale * kLog2e);
+                              int32_t* plan, int B, int Hq, int Hkv, int Lmax, float sm_scale,
+                              hipStream_t stream) {
+  const int wk = attn_decode_waves(Hkv);
+  const int slots = (int)attn_decode_slots(B, Lmax);
+  hipLaunchKernelGGL(attn_decode_kernel, dim3(ceil_div(Hkv * wk, 4)), dim3(256), 0, stream, q, kc, vc, kv_len,
+                     sinks, part, plan, B, Hq, Hkv, Lmax, wk, slots, sm_scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(B * Hq), dim3(AD), 0, stream, part, kv_len, out, Hq, Lmax,
-                     nsplit, skeys);
+  // a sequence has at most ceil(Lmax / kMinSplitKeys) + 1 records
+  if (ceil_div(std::max(Lmax, 1), kMinSplitKeys) + 1 > 32)
+    hipLaunchKernelGGL(attn_combine_kernel<4>, dim3(B * Hq), dim3(256), 0, stream, part, kv_len, plan, out, B,
+                       Hq, Lmax, wk, slots);
+  else
+    hipLaunchKernelGGL(attn_combine_kernel<1>, dim3(B * Hq), dim3(64), 0, stream, part, kv_len, plan, out, B,
+                       Hq, Lmax, wk, slots);
   return hipGetLastError();
 }
 

@@ -45,9 +45,16 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+namespace {
+// segment records, then the plan (2 B + 2 int32, rounded to 16 bytes)
+size_t decode_records_bytes(int32_t B, int32_t Hq, int32_t Lmax) {
+  return (size_t)moe::attn_decode_slots(B, Lmax) * Hq * moe::kPartFloats * sizeof(float);
+}
+}  // namespace
+
 size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax) {
   if (B < 0 || Hq < 1 || Lmax < 1) return 0;
-  return (size_t)B * Hq * moe::attn_decode_max_splits(Lmax) * moe::kPartFloats * sizeof(float);
+  return decode_records_bytes(B, Hq, Lmax) + (((size_t)2 * B + 2) * sizeof(int32_t) + 15) / 16 * 16;
 }
 
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -59,7 +66,7 @@ moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_ca
   if (hs != MOE_OK) return hs;
   if (Hq / Hkv > 16) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv * Lmax * D >= kMaxElems ||
-      (int64_t)B * Hkv * moe::attn_decode_max_splits(Lmax) >= (int64_t(1) << 31))
+      moe::attn_decode_slots(B, Lmax) * Hq * moe::kPartFloats >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
   if (B == 0) return MOE_OK;
   const void* ptrs[] = {q, k_cache, v_cache, kv_len, sinks, out, workspace};
@@ -71,7 +78,9 @@ moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_ca
   const hipError_t e = moe::launch_attn_decode(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
       static_cast<const uint16_t*>(v_cache), kv_len, sinks, static_cast<uint16_t*>(out),
-      static_cast<float*>(workspace), B, Hq, Hkv, Lmax, sm_scale, static_cast<hipStream_t>(stream));
+      static_cast<float*>(workspace),
+      reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + decode_records_bytes(B, Hq, Lmax)), B,
+      Hq, Hkv, Lmax, sm_scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

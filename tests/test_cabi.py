@@ -167,6 +167,9 @@ def test_attn_decode_argument_errors(kw, want):
 
 
 def test_attn_decode_workspace_size():
-    assert moe.attn_decode_workspace_bytes(4, 8, 256) == 4 * 8 * 1 * 68 * 4
-    assert moe.attn_decode_workspace_bytes(4, 8, 257) == 4 * 8 * 2 * 68 * 4
+    # segment records: min(1024 + 2 B, B (ceil(Lmax / 256) + 2)) slots of Hq records of
+    # 68 floats, then the plan (2 B + 2 int32, rounded to 16 bytes)
+    assert moe.attn_decode_workspace_bytes(4, 8, 256) == 4 * 3 * 8 * 68 * 4 + 48
+    assert moe.attn_decode_workspace_bytes(4, 8, 257) == 4 * 4 * 8 * 68 * 4 + 48
+    assert moe.attn_decode_workspace_bytes(600, 8, 4096) == (1024 + 1200) * 8 * 68 * 4 + 4816
     assert moe.attn_decode_workspace_bytes(4, 8, 0) == 0

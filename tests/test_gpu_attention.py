@@ -62,11 +62,19 @@ def test_prefill_vs_oracle(S, Hq, Hkv):
 DECODE = [
     # (B, Hq, Hkv, Lmax, lengths or None for seeded ragged lengths)
     (4, 8, 1, 300, None), (16, 64, 8, 1024, None), (3, 16, 1, 513, None), (5, 4, 4, 64, None),
-    (6, 8, 2, 1100, [1, 256, 257, 1100, 1023, 513]),   # 256-key splits
-    (24, 8, 8, 1500, [1, 512, 513, 1500, 1023, 1024] * 4),   # 512-key splits
-    (40, 16, 8, 2000, None),                         # 1024-key splits
-    (48, 8, 8, 2100, [1, 2048, 2049, 2100, 1024, 1025] * 8),   # 2048-key splits
-    (300, 8, 8, 600, None),                          # one split covers the cache
+    # the keys of all sequences are cut into equal ranges, one per wave (at least
+    # 256 keys): ranges that start or end inside sequences and hold several
+    # sequences, lengths 1 and 0 around them
+    (6, 8, 2, 1100, [1, 256, 257, 1100, 1023, 513]),
+    (24, 8, 8, 1500, [1, 512, 513, 1500, 1023, 1024] * 4),
+    (40, 16, 8, 2000, None),
+    (48, 8, 8, 2100, [1, 2048, 2049, 2100, 1024, 1025] * 8),
+    (300, 8, 8, 600, None),                          # ranges of about 1000 keys over 2-4 sequences
+    (9, 8, 8, 700, [0, 5, 0, 700, 1, 0, 300, 0, 2]),
+    # long caches: a sequence in up to a few hundred ranges, merged by four waves
+    (2, 8, 1, 40000, [40000, 9000]),
+    (3, 16, 2, 20000, [20000, 1, 9999]),
+    (1, 64, 8, 65536, [65536]),
 ]
 
 
