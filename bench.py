@@ -53,24 +53,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 271558.525, "write_kib": 759.269,
-        "copy_fetch_kib": 524307.0, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 923734.450, "write_kib": 103737.319,
-        "copy_fetch_kib": 524306.5625, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 279949.575, "write_kib": 760.781,
-        "copy_fetch_kib": 524307.0625, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 953680.037, "write_kib": 103674.794,
-        "copy_fetch_kib": 524306.125, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 144512.775, "write_kib": 759.413,
-        "copy_fetch_kib": 524311.875, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "6b5cdbb23ae542c8a633d7455ed1d7e30e275d26bee18199377be2dd561c6358",
-        "fetch_kib": 580680.725, "write_kib": 103735.169,
-        "copy_fetch_kib": 524304.5625, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 271558.388, "write_kib": 759.200,
+        "copy_fetch_kib": 524306.75, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 920632.137, "write_kib": 103961.769,
+        "copy_fetch_kib": 524307.9375, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 279949.625, "write_kib": 760.819,
+        "copy_fetch_kib": 524307.125, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 946080.863, "write_kib": 103826.913,
+        "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 144511.850, "write_kib": 759.181,
+        "copy_fetch_kib": 524312.75, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
+        "fetch_kib": 580981.262, "write_kib": 103756.781,
+        "copy_fetch_kib": 524304.875, "copy_write_kib": 1048576.0},
 }
 
 

@@ -1180,17 +1180,36 @@ int grid_persistent(int max_tiles) {
   return std::min(cus[dev], grid_for(max_tiles));
 }
 
+// Persistent decode grid: as many workgroups per CU as the kernel's registers
+// and LDS allow, at most two (a second workgroup keeps a second ring of weight
+// loads in flight on the CU), fewer when the tile list cannot fill them.
+template <bool GATED, int DBM, int DBN, bool MX, bool FP4>
+dim3 grid_decode(int max_tiles) {
+  static int per = 0;  // one value per kernel
+  if (per == 0) {
+    int n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4>,
+                                                     DMA_WAVES * 64, 0) != hipSuccess || n < 1)
+      n = 1;
+    per = std::min(n, 2);
+  }
+  return dim3(std::min(per * grid_persistent(1 << 30), grid_for(max_tiles)));
+}
+
 template <bool GATED, int DBM, int DBN>
 hipError_t launch_gemm(const GemmArgs& a, bool decode, int fmt, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   if (decode) {
     if (fmt == kFmtMxFp4)
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, true>),
+                         (grid_decode<GATED, DBM, DBN, true, true>(max_tiles)), block, 0, stream, a);
     else if (fmt == kFmtMx)
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, false>),
+                         (grid_decode<GATED, DBM, DBN, true, false>(max_tiles)), block, 0, stream, a);
     else
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, false, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, false, false>),
+                         (grid_decode<GATED, DBM, DBN, false, false>(max_tiles)), block, 0, stream, a);
   } else {
     if (fmt == kFmtMxFp4)
       hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, true>), grid, block, 0, stream, a);
