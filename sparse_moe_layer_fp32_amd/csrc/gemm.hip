@@ -608,6 +608,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     __syncthreads();
   }
   setup(tl, 0);
+  if constexpr (GATED) {
+    // every wave has read rtok[0] before a tile move inside the prologue (K of
+    // one or two blocks) loads the tile after next into it
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
 
   // One K block; returns false after the workgroup's last tile.
   int pend = 0;
