@@ -53,24 +53,24 @@ GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 271558.388, "write_kib": 759.200,
-        "copy_fetch_kib": 524306.75, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 920632.137, "write_kib": 103961.769,
-        "copy_fetch_kib": 524307.9375, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 279949.625, "write_kib": 760.819,
-        "copy_fetch_kib": 524307.125, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 946080.863, "write_kib": 103826.913,
-        "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 144511.850, "write_kib": 759.181,
-        "copy_fetch_kib": 524312.75, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "49d490dd0ecb83a501255ee4c0c26466d97be6824d4f06a9dfecec075d066be0",
-        "fetch_kib": 580981.262, "write_kib": 103756.781,
-        "copy_fetch_kib": 524304.875, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 271558.412, "write_kib": 759.256,
+        "copy_fetch_kib": 524311.125, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 920012.425, "write_kib": 103914.719,
+        "copy_fetch_kib": 524305.6875, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 279949.713, "write_kib": 761.312,
+        "copy_fetch_kib": 524308.125, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 942775.488, "write_kib": 103719.781,
+        "copy_fetch_kib": 524307.75, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 144512.350, "write_kib": 759.256,
+        "copy_fetch_kib": 524314.25, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
+        "fetch_kib": 579350.738, "write_kib": 103737.000,
+        "copy_fetch_kib": 524305.875, "copy_write_kib": 1048576.0},
 }
 
 
