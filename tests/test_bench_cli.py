@@ -57,3 +57,13 @@ def test_decode_gateup_traffic_matches_algorithmic_bytes():
     E, d, f, T = 32, 2944, 2944, 64
     weights = E * d * 2 * f + 4 * E * (d // 128) * (2 * f // 128) + 2 * E * 2 * f
     assert abs(hbm - weights) / weights < 0.01
+
+
+def test_event_steps_are_sampled_inside_the_timed_steps():
+    """Per-kernel events go on every N-th timed step (at least one), all of
+    them inside the timed range."""
+    b = _bench()
+    assert b.sampled_steps(50, 5) == [4, 9, 14, 19, 24, 29, 34, 39, 44, 49]
+    assert b.sampled_steps(3, 5) == [2]
+    assert b.sampled_steps(4, 1) == [0, 1, 2, 3]
+    assert b.sampled_steps(7, 0) == list(range(7))
