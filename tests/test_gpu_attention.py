@@ -75,6 +75,7 @@ DECODE = [
     (2, 8, 1, 40000, [40000, 9000]),
     (3, 16, 2, 20000, [20000, 1, 9999]),
     (1, 64, 8, 65536, [65536]),
+    (70, 8, 1, 9000, None),                          # two chunks of sequences, four-wave merge
 ]
 
 
