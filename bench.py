@@ -42,6 +42,7 @@ FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 ATTN_METRIC = "attention tokens/s + % of bf16 MFMA peak (prefill) / % HBM BW (decode)"
 GEMM_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "gemm.hip")
+ATTN_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "attention.hip")
 
 # HBM traffic of one gate/up GEMM launch from rocprofv3 --pmc runs (one run for
 # FETCH_SIZE, one for WRITE_SIZE, KiB per dispatch) of
@@ -74,19 +75,58 @@ TRAFFIC = {
 }
 
 
-def gemm_src_sha():
+# The same for one decode-attention call (the decode and combine kernels of a
+# call added), keyed by the SHA-256 of the attention source.
+ATTN_TRAFFIC = {
+    "attn_decode": {"attn_sha256": "6d6c0ca7148f64c1d2ebc260ac251caef4f263eb474b80f45f15010cd2236884",
+        "fetch_kib": 197909.969, "write_kib": 3759.625,
+        "copy_fetch_kib": 524316.4375, "copy_write_kib": 1048576.0},
+}
+
+
+def src_sha(path):
     import hashlib
-    with open(GEMM_SRC, "rb") as fh:
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()
+
+
+def gemm_src_sha():
+    return src_sha(GEMM_SRC)
+
+
+def _scaled_bytes(t):
+    fetch = t["fetch_kib"] * (1 << 20) / t["copy_fetch_kib"]
+    write = t["write_kib"] * (1 << 20) / t["copy_write_kib"]
+    return int(round((fetch + write) * 1024))
 
 
 def measured_traffic(workload):
     t = TRAFFIC.get(workload)
     if t is None or t["gemm_sha256"] != gemm_src_sha():
         return None
-    fetch = t["fetch_kib"] * (1 << 20) / t["copy_fetch_kib"]
-    write = t["write_kib"] * (1 << 20) / t["copy_write_kib"]
-    return int(round((fetch + write) * 1024))
+    return _scaled_bytes(t)
+
+
+def measured_attn_traffic(workload):
+    t = ATTN_TRAFFIC.get(workload)
+    if t is None or t["attn_sha256"] != src_sha(ATTN_SRC):
+        return None
+    return _scaled_bytes(t)
+
+
+def calibration_copy(mib, dev):
+    """A device copy of known size in the profiled process: the counter runs
+    scale FETCH_SIZE and WRITE_SIZE by what they read for it."""
+    if mib <= 0:
+        return
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy of {n} bytes")
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def sampled_steps(steps, every):
@@ -194,6 +234,7 @@ def attn_bench(args):
         tokens = B
         kv_bytes = int(inp["kv_len"].astype(np.int64).sum()) * shape.Hkv * shape.D * 2 * 2
         work = dict(bytes=kv_bytes + 2 * B * shape.Hq * shape.D * 2)  # K, V of the visible keys + q + out
+    calibration_copy(args.copy_calibration_mib, dev)
     log(f"[bench] {args.workload}: warmup {args.warmup}")
     for _ in range(args.warmup):
         run()
@@ -222,7 +263,7 @@ def attn_bench(args):
     else:
         ach = work["bytes"] / (call_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_attn_traffic(args.workload),
                 "kernel": "attn_decode_kernel + attn_combine_kernel (the whole call)",
                 "avg_ms": round(call_ms, 5), "algorithmic_bytes": work["bytes"]}
     roof["timed_launches"] = len(sampled)
@@ -304,15 +345,7 @@ def main():
     out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     x = p["x"]
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        log(f"[bench] calibration copy of {n} bytes")
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args.copy_calibration_mib, dev)
 
     dbg = moe.forward_debug(x, *w_args, path=args.path, fmt=fmt)
     torch.cuda.synchronize()

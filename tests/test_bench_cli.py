@@ -67,3 +67,16 @@ def test_event_steps_are_sampled_inside_the_timed_steps():
     assert b.sampled_steps(3, 5) == [2]
     assert b.sampled_steps(4, 1) == [0, 1, 2, 3]
     assert b.sampled_steps(7, 0) == list(range(7))
+
+
+def test_decode_attention_traffic_matches_algorithmic_bytes():
+    """One decode-attention call of the bench batch (64 seeded ragged sequences,
+    sum of kv_len 195045: K and V rows of 8 heads x 64 dims in bf16, plus q and
+    out = 400500736 bytes) reads every cached row once: the stored counters,
+    scaled, stay within 3 % of that (the rest is the partial-result records)."""
+    b = _bench()
+    t = b.ATTN_TRAFFIC["attn_decode"]
+    alg = 195045 * 8 * 64 * 2 * 2 + 2 * 64 * 64 * 64 * 2
+    assert alg == 400500736
+    hbm = b._scaled_bytes(t)
+    assert alg <= hbm < 1.03 * alg
