@@ -75,12 +75,16 @@ TRAFFIC = {
 }
 
 
-# The same for one decode-attention call (the decode and combine kernels of a
-# call added), keyed by the SHA-256 of the attention source.
+# The same for one attention call (decode: the decode and combine kernels of a
+# call added; prefill: its one kernel), keyed by the SHA-256 of the attention
+# source.
 ATTN_TRAFFIC = {
     "attn_decode": {"attn_sha256": "6d6c0ca7148f64c1d2ebc260ac251caef4f263eb474b80f45f15010cd2236884",
         "fetch_kib": 197909.969, "write_kib": 3759.625,
         "copy_fetch_kib": 524316.4375, "copy_write_kib": 1048576.0},
+    "attn_prefill": {"attn_sha256": "6d6c0ca7148f64c1d2ebc260ac251caef4f263eb474b80f45f15010cd2236884",
+        "fetch_kib": 51132.094, "write_kib": 65536.000,
+        "copy_fetch_kib": 524313.6875, "copy_write_kib": 1048576.0},
 }
 
 
@@ -258,7 +262,7 @@ def attn_bench(args):
     if prefill:
         ach = work["flops"] / (call_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": measured_attn_traffic(args.workload),
                 "kernel": "attn_prefill_kernel<8, 2>", "avg_ms": round(call_ms, 5), "algorithmic_flops": work["flops"]}
     else:
         ach = work["bytes"] / (call_ms * 1e-3) / 1e9

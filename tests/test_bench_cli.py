@@ -80,3 +80,14 @@ def test_decode_attention_traffic_matches_algorithmic_bytes():
     assert alg == 400500736
     hbm = b._scaled_bytes(t)
     assert alg <= hbm < 1.03 * alg
+
+
+def test_prefill_attention_writes_each_output_once():
+    """The stored prefill counters: WRITE_SIZE is exactly the bf16 output
+    (8192 x 64 x 64), and the scaled reads are at least q, k and v once."""
+    b = _bench()
+    t = b.ATTN_TRAFFIC["attn_prefill"]
+    out = 8192 * 64 * 64 * 2
+    assert t["write_kib"] * 1024 == out
+    read = t["fetch_kib"] * (1 << 20) / t["copy_fetch_kib"] * 1024
+    assert read >= out + 2 * 8192 * 8 * 64 * 2
