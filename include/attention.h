@@ -44,7 +44,7 @@ extern "C" {
  * Hq not a multiple of Hkv is MOE_ERR_SHAPE. */
 moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
                              void* out, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
-                             float sm_scale, void* stream);
+                             float sm_scale, hipStream_t stream);
 
 /* Bytes of device workspace attn_sink_decode needs (the partial results of
  * the sequence pieces the waves hold: min(1024 + 2 B, B (ceil(Lmax / 256) + 2))
@@ -68,7 +68,7 @@ size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax);
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_len, const float* sinks, void* out, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax, float sm_scale,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

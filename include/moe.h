@@ -25,29 +25,52 @@
  * deq(W,S) multiplies every e4m3 weight by the fp32 scale of its 128x128
  * block.  FP8 is OCP E4M3 ("fn": max 448, NaN 0x7F/0xFF, no infinities).
  *
- * Conventions for every entry point below:
- *  - Tensor pointers are DEVICE pointers, row-major, owned by the caller;
- *    the library allocates no device memory and keeps no pointer after the
- *    call returns.  Every pointer must be 16-byte aligned.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *    and the call returns without waiting for it; results are valid once
- *    the stream has reached that point.  There is no host-device sync and
- *    no device-to-host copy, so the sequence can be captured in a graph.
- *  - Argument errors are found on the host before anything is enqueued and
- *    return a negative status; nothing is written then.  A launch failure
- *    returns MOE_ERR_HIP.  Device faults surface at the caller's next sync.
+ * Conventions for every entry point below.  The pages describe serving
+ * engines rather than this interface; each convention names the passage it
+ * serves.
+ *  - Memory: tensor pointers are DEVICE pointers, row-major, owned by the
+ *    caller; the library allocates no device memory and keeps no pointer
+ *    after the call returns ("Fast embeddings on GPUs", section "CUDA graph
+ *    management": buffers are set up once, in the eager warm-up before a
+ *    graph is captured, and reused by every replay).  Every pointer must be
+ *    16-byte aligned.
+ *  - Ordering: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and the call returns without waiting for it; results are valid
+ *    once the stream has reached that point.  There is no host-device sync
+ *    and no device-to-host copy, so the launch sequence can be captured in a
+ *    HIP graph and replayed ("GPT-OSS on day 0", the opening of section
+ *    "Kernels for GPT-OSS": the decoders and their CUDA-graph framework were
+ *    reused unchanged for the new model; "Fast
+ *    embeddings on GPUs", sections "CUDA graph management" and "Lazy
+ *    Tensors": the forward is launched asynchronously and its result is
+ *    tracked through an event; the page "The GPU sat idle, and the CPU was to
+ *    blame" on Moondream's Photon engine, section "Two slots and copying
+ *    behind the GPU's back": reading a result back to the host forces a
+ *    synchronisation, so none happens inside the step).
+ *  - Errors: argument errors are found on the host before anything is
+ *    enqueued and return a negative status; nothing is written then.  A
+ *    launch failure returns MOE_ERR_HIP.  Device faults surface at the
+ *    caller's next sync.  No C++ exception crosses the boundary.
  *  - T == 0 is a no-op returning MOE_OK (x and out may then be NULL).
  *  - Deterministic: the same inputs give the same output bits (no atomics
- *    on data paths; every reduction has a fixed order).
+ *    on data paths; every reduction has a fixed order), so a replayed graph
+ *    reproduces the eager call bit for bit.
  *  - `out` must not alias any input or the workspace.
- *  - NaN inputs propagate to outputs; expert indices are always valid and
- *    distinct whatever the logits hold.
+ *  - NaN: a NaN in x makes every output of its token NaN; a NaN weight code,
+ *    weight scale or bias of an expert makes the outputs of the tokens routed
+ *    to it NaN.  The expert indices are always valid and distinct: the logit
+ *    bits order the selection, so a positive NaN logit ranks above every
+ *    number and a negative NaN logit below every number.
  *  - Calls that share a workspace must be ordered (same stream); calls on
  *    different workspaces may overlap.
+ *  - Thread safety: entry points may be called from several host threads;
+ *    the only process-wide state is a per-device cache of the compute-unit
+ *    count and kernel occupancy, filled once under a lock.
  */
 #ifndef SPARSE_MOE_MI355_H
 #define SPARSE_MOE_MI355_H
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -60,8 +83,10 @@ typedef enum {
   MOE_ERR_NULL = -1,        /* a required pointer is NULL                         */
   MOE_ERR_SHAPE = -2,       /* T < 0, d or f not a positive multiple of 128, E < 1 */
   MOE_ERR_UNSUPPORTED = -3, /* k < 1, k > E, k > MOE_MAX_TOPK, E > MOE_MAX_EXPERTS,
-                               d or f > MOE_MAX_HIDDEN, or tensors of 2^31 bytes
-                               or more (T*d, T*k*f, d*2f, scales)                 */
+                               d or f > MOE_MAX_HIDDEN, or buffers of 2^31 bytes
+                               or more: x codes (T*d), h codes (T*k*f), one
+                               expert's gate/up weights (2*d*f), the activation
+                               scales, or the fp32 expert outputs (4*T*k*d)   */
   MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_bytes */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
   MOE_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError)           */
@@ -89,7 +114,7 @@ typedef enum {
  * they stay fp32). */
 #define MOE_ROUTE_SOFTMAX_ALL 4u
 #define MOE_GATE_BF16 8u
-/* MOE_FORMAT_MX: the MXFP8 variant ("GPT-OSS on day 0", section
+/* MOE_FORMAT_MX: the MXFP8 variant ("Hosting Qwen on Blackwell", section
  * "Quantization": microscaling, the Blackwell format, with the weights
  * converted statically).  Every 32 consecutive elements along the
  * contraction share one E8M0 scale (a uint8 e; value 2^(e-127), 0xFF NaN):
@@ -115,12 +140,19 @@ typedef enum {
 #define MOE_FORMAT_MXFP4 (MOE_FORMAT_MX | MOE_WEIGHTS_FP4)
 
 /* Bytes of device workspace moe_forward needs for these sizes (0 if the sizes
- * are invalid).  The workspace holds the routing tables, the quantised
- * activations, h and the per-row expert outputs; its content between calls
- * is meaningless.  Size for C-ABI users: about T*(d + k*(f + 4*d + 8)) bytes. */
+ * are invalid).  The workspace holds the routing tables ("GPT-OSS on day 0",
+ * section "MoE": the dispatcher selects the tokens of each expert; "Hosting
+ * Qwen on Blackwell", section "Expert Parallel": dispatch aggregates the
+ * routing information and stages the tokens in the MoE GEMM's input buffer),
+ * the quantised activations, h and the per-row expert outputs; nothing in it
+ * has to be initialised and its content between calls is meaningless.  The
+ * caller allocates it once per batch shape, as "Fast embeddings on GPUs",
+ * section "CUDA graph management", sets up buffers before capture.  Size for
+ * C-ABI users: about T*(d + k*(f + 4*d + 8)) bytes. */
 size_t moe_workspace_bytes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k);
 
-/* The block forward for T tokens.
+/* The block forward for T tokens: the formula above ("GPT-OSS on day 0",
+ * sections "GPT-OSS on Hopper" and "MoE").
  *   x          bf16  [T, d]
  *   W_router   fp32  [d, E]
  *   b_router   fp32  [E]
@@ -139,19 +171,25 @@ moe_status moe_forward(const void* x, const float* W_router, const float* b_rout
                        const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                        const uint8_t* W_down, const float* S_down, const void* b_down, void* out,
                        int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       size_t workspace_bytes, hipStream_t stream);
 
 /* moe_forward with `flags`: a GEMM path (MOE_PATH_*; the paths give the same
- * results to rounding of the fp32 accumulation order), the gate-weight
- * options MOE_ROUTE_SOFTMAX_ALL and MOE_GATE_BF16, and the weight format
- * MOE_FORMAT_MX. */
+ * results to rounding of the fp32 accumulation order; "Hosting Qwen on
+ * Blackwell", sections "Prefiller" and "Decoder": prefill batches make the
+ * MoE GEMM dense and compute-bound, decode batches are bound by loading the
+ * weights; "Disaggregated prefill and decode", section "Prefill vs decode
+ * performance"), the gate-weight options MOE_ROUTE_SOFTMAX_ALL and
+ * MOE_GATE_BF16 ("GPT-OSS on day 0", section "MoE"), and the weight formats
+ * MOE_FORMAT_MX / MOE_FORMAT_MXFP4 ("Hosting Qwen on Blackwell", section
+ * "Quantization"; "GPT-OSS on day 0", section "GPT-OSS on Hopper"). */
 moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_router, int32_t k,
                           const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                           const uint8_t* W_down, const float* S_down, const void* b_down,
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream);
+                          size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
-/* moe_forward_ex with MXFP8 weights (flags | MOE_FORMAT_MX):
+/* moe_forward_ex with MXFP8 weights (flags | MOE_FORMAT_MX; "Hosting Qwen on
+ * Blackwell", section "Quantization"):
  *   X_gateup   E8M0 [E, d/32, 2f]
  *   X_down     E8M0 [E, f/32, d]
  * the other arguments and `flags` bits as for moe_forward_ex (MOE_WEIGHTS_FP4
@@ -160,9 +198,12 @@ moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_r
                           const uint8_t* W_gateup, const uint8_t* X_gateup, const void* b_gateup,
                           const uint8_t* W_down, const uint8_t* X_down, const void* b_down,
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream);
+                          size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
-/* The forward runs in six stages, in this order on the stream.  For a batch
+/* The forward runs in six stages, in this order on the stream: routing,
+ * dispatch, the two expert GEMMs and the weighted combine ("GPT-OSS on day
+ * 0", section "MoE"; "Hosting Qwen on Blackwell", section "Expert
+ * Parallel").  For a batch
  * of at most 64 tokens the router stage performs the whole routing (counts,
  * offsets, tile lists, placement) and the scan and place stages have no work. */
 #define MOE_STAGE_ROUTER 0  /* router logits, top-k, softmax, x quantisation, tile histogram */
@@ -179,16 +220,20 @@ moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_r
  * the tables the earlier stages wrote into the workspace: running a stage
  * whose predecessors have not run on that workspace with the same arguments
  * is undefined behaviour (out-of-bounds device accesses).  Meant for timing
- * single kernels between events.  MOE_ERR_FLAGS for a bad stage range. */
+ * single kernels between events, the way "Hosting Qwen on Blackwell",
+ * section "MoE GEMM", benchmarks the grouped GEMM on its own.  MOE_ERR_FLAGS
+ * for a bad stage range. */
 moe_status moe_forward_stages(const void* x, const float* W_router, const float* b_router,
                               int32_t k, const uint8_t* W_gateup, const float* S_gateup,
                               const void* b_gateup, const uint8_t* W_down, const float* S_down,
                               const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
                               int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
-                              int32_t first_stage, int32_t last_stage, void* stream);
+                              int32_t first_stage, int32_t last_stage, hipStream_t stream);
 
 /* moe_forward_ex, then copies of intermediates into the optional (nullable)
- * device buffers, for parity tests and debugging:
+ * device buffers, for parity tests and debugging (each array is one step of
+ * the formula above; the copies are device-to-device and stream-ordered, so
+ * no synchronisation happens here either):
  *   topk_idx   int32 [T, k]   selected experts, descending logit
  *   topk_w     fp32  [T, k]   gate weights in the same order
  *   offsets    int32 [E+1]    first permuted row of every expert (exclusive scan)
@@ -203,11 +248,12 @@ moe_status moe_forward_debug(const void* x, const float* W_router, const float* 
                              const void* b_gateup, const uint8_t* W_down, const float* S_down,
                              const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
                              int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
-                             void* stream, int32_t* topk_idx, float* topk_w, int32_t* offsets,
+                             hipStream_t stream, int32_t* topk_idx, float* topk_w, int32_t* offsets,
                              int32_t* row_token, int32_t* row_of, uint8_t* xq, float* xs,
                              uint8_t* hq, float* hs, float* y);
 
-/* Static text for a status code. */
+/* Static text for a status code (never NULL; "unknown status" for other
+ * values), so callers can report an error without a device call. */
 const char* moe_status_string(int32_t status);
 
 #ifdef __cplusplus

@@ -7,8 +7,8 @@ The FP8 format is the one the "GPT-OSS on day 0" post serves the experts in
 (section "GPT-OSS on Hopper": FP8 with 128x128 block scaling).  Its element
 type is OCP E4M3 ("fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
 bits, no infinities, NaN = S.1111.111, largest finite 448, smallest
-subnormal 2^-9.  The MXFP8 variant (the post's section "Quantization" on
-Blackwell: microscaling) adds the OCP E8M0 scale: 8 exponent bits with bias
+subnormal 2^-9.  The MXFP8 variant (the "Hosting Qwen on Blackwell"
+post, section "Quantization": microscaling on Blackwell) adds the OCP E8M0 scale: 8 exponent bits with bias
 127, no sign and no mantissa, code 0xFF = NaN.  The FP4 weights (the post's
 section "GPT-OSS on Hopper": the checkpoints ship in MXFP4) use the OCP E2M1
 element: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, no

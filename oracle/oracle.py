@@ -27,11 +27,11 @@ weighted accumulation):
 9. ``Y = deq(hq) @ deq(W_down) + b_down`` (fp64);
 10. ``out[t] = sum_j w[t,j] * Y[row(t,j)]`` in fp64, not rounded.
 
-MXFP8 variant (``inp["format"] == "mx"``; the post's section
-"Quantization" names microscaling as the Blackwell format, with the weights
-converted statically): steps 6 and 8 quantise per row per 32 columns with a
-power-of-two E8M0 scale, and the weights carry one E8M0 scale per 32 rows
-of K per column; everything else is unchanged.  MXFP4 weights
+MXFP8 variant (``inp["format"] == "mx"``; the "Hosting Qwen on Blackwell"
+post, section "Quantization", names microscaling as the Blackwell format,
+with the weights converted statically): steps 6 and 8 quantise per row per
+32 columns with a power-of-two E8M0 scale, and the weights carry one E8M0
+scale per 32 rows of K per column; everything else is unchanged.  MXFP4 weights
 (``"mxfp4"``; the post's section "GPT-OSS on Hopper" says the checkpoints ship
 in MXFP4): the weights are E2M1 with the same E8M0 scale blocks, two codes per
 byte along K; the activations are MXFP8 as above.

@@ -24,7 +24,7 @@ extern "C" {
 
 moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const float* sinks,
                              void* out, int32_t S, int32_t Hq, int32_t Hkv, int32_t D,
-                             float sm_scale, void* stream) {
+                             float sm_scale, hipStream_t stream) {
   if (S < 0) return MOE_ERR_SHAPE;
   const moe_status hs = check_heads(Hq, Hkv, D);
   if (hs != MOE_OK) return hs;
@@ -41,7 +41,7 @@ moe_status attn_sink_prefill(const void* q, const void* k, const void* v, const 
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   const hipError_t e = moe::launch_attn_prefill(
       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      sinks, static_cast<uint16_t*>(out), S, Hq, Hkv, sm_scale, static_cast<hipStream_t>(stream));
+      sinks, static_cast<uint16_t*>(out), S, Hq, Hkv, sm_scale, stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -60,7 +60,7 @@ size_t attn_sink_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Lmax) {
 moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* kv_len, const float* sinks, void* out, int32_t B,
                             int32_t Hq, int32_t Hkv, int32_t D, int32_t Lmax, float sm_scale,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (B < 0 || Lmax < 1) return MOE_ERR_SHAPE;
   const moe_status hs = check_heads(Hq, Hkv, D);
   if (hs != MOE_OK) return hs;
@@ -80,7 +80,7 @@ moe_status attn_sink_decode(const void* q, const void* k_cache, const void* v_ca
       static_cast<const uint16_t*>(v_cache), kv_len, sinks, static_cast<uint16_t*>(out),
       static_cast<float*>(workspace),
       reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + decode_records_bytes(B, Hq, Lmax)), B,
-      Hq, Hkv, Lmax, sm_scale, static_cast<hipStream_t>(stream));
+      Hq, Hkv, Lmax, sm_scale, stream);
   return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

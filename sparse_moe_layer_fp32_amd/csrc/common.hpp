@@ -41,21 +41,39 @@ __device__ __forceinline__ uint32_t f32x4_to_e4m3(float a, float b, float c, flo
   return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true));
 }
 
+// ----------------------------------------------------------------------------- NaN-keeping quantisation
+// IEEE 754-2019 maximum / minimum (v_maximum_f32 / v_minimum_f32 on gfx950):
+// a NaN operand gives NaN, where fmaxf / fminf would drop it.  The quantisers
+// take their group maxima and clamps with these, so a NaN value turns its
+// group's scale and its own code into NaN and reaches the outputs.
+__device__ __forceinline__ float nan_max(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float nan_min(float a, float b) { return __builtin_elementwise_minimum(a, b); }
+
+// v clamped to the e4m3 range [-448, 448]; NaN stays NaN (and encodes as NaN).
+__device__ __forceinline__ float clamp_fp8(float v) { return nan_min(nan_max(v, -kFp8Max), kFp8Max); }
+
+// fp32 scale of a 1x128 group with largest magnitude amax: amax / 448 (IEEE
+// division), 1 for an all-zero group, NaN when amax is NaN.
+__device__ __forceinline__ float group_scale(float amax) { return amax == 0.f ? 1.0f : amax / kFp8Max; }
+
 // ----------------------------------------------------------------------------- MX scales
 // E8M0 code (e + 127, at least 0) of the MX scale 2^e of a block whose largest
 // magnitude is amax >= 0: the smallest e with amax <= 448 * 2^e.  With
 // amax = m 2^p (1 <= m < 2) and 448 = 1.75 * 2^8, e = p - 8 when m <= 1.75
 // and p - 7 otherwise: integer work on the fp32 bits, exact for every input
-// (zero and subnormals give code 0, the smallest scale 2^-127).
+// (zero and subnormals give code 0, the smallest scale 2^-127).  A NaN amax
+// gives 0xFF, the E8M0 NaN.
 __device__ __forceinline__ uint32_t mx_code(float amax) {
   const uint32_t b = __float_as_uint(amax);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return 0xffu;
   const int c = static_cast<int>(b >> 23) - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
   return c > 0 ? static_cast<uint32_t>(c) : 0u;
 }
 
-// 1 / 2^e = 2^(127 - code) for an MX code from mx_code (code <= 248).
+// 1 / 2^e = 2^(127 - code) for an MX code from mx_code (code <= 248), and
+// NaN for the NaN code 0xFF.
 __device__ __forceinline__ float mx_inv_scale(uint32_t code) {
-  return __uint_as_float((254u - code) << 23);
+  return code == 0xffu ? __uint_as_float(0x7fc00000u) : __uint_as_float((254u - code) << 23);
 }
 
 // ----------------------------------------------------------------------------- wave reductions

@@ -20,6 +20,7 @@
 // Tiles are taken from a device-side table (expert, row block, column block),
 // grouped so that tiles sharing weights run together on one XCD (L2).
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -499,10 +500,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
             // far below the e4m3 spacing h is rounded to)
             const float ex = __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f);
             h[mb][j][i] = gv * __builtin_amdgcn_rcpf(1.0f + ex) * uv;
-            mx = fmaxf(mx, fabsf(h[mb][j][i]));
+            mx = nan_max(mx, fabsf(h[mb][j][i]));
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = nan_max(mx, __shfl_xor(mx, 16));
+        pmax[mb] = nan_max(mx, __shfl_xor(mx, 32));
       }
       if constexpr (MX) {
         // the wave's 32 h columns of a row are one MX block: no exchange
@@ -545,8 +546,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
         for (int mb = 0; mb < MB; ++mb) {
           const int r = wm * WR + 16 * mb + l16;
           const float amax =
-              fmaxf(fmaxf(smax[r], smax[BM + r]), fmaxf(smax[2 * BM + r], smax[3 * BM + r]));
-          const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+              nan_max(nan_max(smax[r], smax[BM + r]), nan_max(smax[2 * BM + r], smax[3 * BM + r]));
+          const float s = group_scale(amax);
           const float inv = 1.0f / s;
           const bool ok = r < t.valid;
           const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
@@ -554,7 +555,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
           for (int j = 0; j < 2; ++j) {
             float q[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(h[mb][j][i] * inv, -kFp8Max), kFp8Max);
+            for (int i = 0; i < 4; ++i) q[i] = clamp_fp8(h[mb][j][i] * inv);
             __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
                                                   ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
           }
@@ -1013,10 +1014,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
             const float ex = __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f);
             const float hv = gv * __builtin_amdgcn_rcpf(1.0f + ex) * uv;
             acc[mb][j][i] = hv;
-            mx = fmaxf(mx, fabsf(hv));
+            mx = nan_max(mx, fabsf(hv));
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        pmax[mb] = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = nan_max(mx, __shfl_xor(mx, 16));
+        pmax[mb] = nan_max(mx, __shfl_xor(mx, 32));
       }
       if constexpr (MX) {
         // the wave's 32 h columns of a row are one MX block: no exchange, no barrier
@@ -1059,9 +1060,9 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           const int r = wm * W_HALF + 16 * mb + l16;
-          const float amax = fmaxf(fmaxf(smax[r], smax[WM_ROWS + r]),
-                                   fmaxf(smax[2 * WM_ROWS + r], smax[3 * WM_ROWS + r]));
-          const float s = amax > 0.f ? amax / kFp8Max : 1.0f;
+          const float amax = nan_max(nan_max(smax[r], smax[WM_ROWS + r]),
+                                     nan_max(smax[2 * WM_ROWS + r], smax[3 * WM_ROWS + r]));
+          const float s = group_scale(amax);
           const float inv = 1.0f / s;
           const bool ok = r < t.valid;
           const uint32_t hrow = (uint32_t)(t.row0 + r) * (uint32_t)g.f + n0 + 32 * wn + 4 * gq;
@@ -1069,7 +1070,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
           for (int j = 0; j < 2; ++j) {
             float q[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(acc[mb][j][i] * inv, -kFp8Max), kFp8Max);
+            for (int i = 0; i < 4; ++i) q[i] = clamp_fp8(acc[mb][j][i] * inv);
             __builtin_amdgcn_raw_buffer_store_b32(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), rH,
                                                   ok ? (int)(hrow + 16 * j) : (int)kOob, 0, 0);
           }
@@ -1173,35 +1174,62 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 
 int grid_for(int max_tiles) { return 8 * ceil_div(max_tiles, 8); }
 
-// Persistent prefill grid: one workgroup per CU (a multiple of 8, one slice
-// per XCD), fewer when the tile list cannot fill them.
-int grid_persistent(int max_tiles) {
-  static int cus[64] = {0};
+// Launch facts of a device, looked up once per device and then read without
+// a lock: std::call_once orders the first lookup before every later read, so
+// concurrent callers on several host threads see a complete value.
+constexpr int kMaxDevices = 64;
+
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] == 0) {
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  return dev;
+}
+
+// Compute units of the current device, rounded up to a multiple of 8 (one
+// slice per XCD).
+int device_cus() {
+  auto lookup = [](int dev) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cus[dev] = 8 * ceil_div(n, 8);
-  }
-  return std::min(cus[dev], grid_for(max_tiles));
+    return 8 * ceil_div(n, 8);
+  };
+  const int dev = current_device();
+  if (dev >= kMaxDevices) return lookup(dev);
+  static std::once_flag once[kMaxDevices];
+  static int cus[kMaxDevices];
+  std::call_once(once[dev], [&] { cus[dev] = lookup(dev); });
+  return cus[dev];
 }
+
+// Persistent prefill grid: one workgroup per CU (a multiple of 8, one slice
+// per XCD), fewer when the tile list cannot fill them.
+int grid_persistent(int max_tiles) { return std::min(device_cus(), grid_for(max_tiles)); }
 
 // Persistent decode grid: as many workgroups per CU as the kernel's registers
 // and LDS allow, at most two (a second workgroup keeps a second ring of weight
-// loads in flight on the CU), fewer when the tile list cannot fill them.
+// loads in flight on the CU), fewer when the tile list cannot fill them.  The
+// occupancy is looked up once per kernel instance and device.
 template <bool GATED, int DBM, int DBN, bool MX, bool FP4>
 dim3 grid_decode(int max_tiles) {
-  static int per = 0;  // one value per kernel
-  if (per == 0) {
+  auto lookup = [] {
     int n = 1;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4>,
                                                      DMA_WAVES * 64, 0) != hipSuccess || n < 1)
       n = 1;
-    per = std::min(n, 2);
+    return std::min(n, 2);
+  };
+  const int dev = current_device();
+  int per;
+  if (dev >= kMaxDevices) {
+    per = lookup();
+  } else {
+    static std::once_flag once[kMaxDevices];
+    static int per_dev[kMaxDevices];
+    std::call_once(once[dev], [&] { per_dev[dev] = lookup(); });
+    per = per_dev[dev];
   }
-  return dim3(std::min(per * grid_persistent(1 << 30), grid_for(max_tiles)));
+  return dim3(std::min(per * device_cus(), grid_for(max_tiles)));
 }
 
 template <bool GATED, int DBM, int DBN>

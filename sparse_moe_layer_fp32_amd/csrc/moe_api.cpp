@@ -62,10 +62,14 @@ moe_status check_sizes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k) {
   // the GEMMs keep one weight scale per K block in one lane: at most 64 blocks
   if ((int64_t)T * k > kMaxRows || d > 64 * MOE_BLOCK || f > 64 * MOE_BLOCK)
     return MOE_ERR_UNSUPPORTED;
-  // buffer offsets of the GEMM loads are 32-bit and must stay below 2^31
+  // The GEMMs address their loads and stores through 32-bit buffer offsets,
+  // and a masked lane stores at offset 2^31, which the buffer's size must
+  // exclude: every buffer they touch stays below 2^31 bytes (x codes, h
+  // codes, one expert's weights, the activation scales and the fp32 expert
+  // outputs Y, 4*R*d bytes).
   const int64_t R = (int64_t)T * k;
   if ((int64_t)T * d >= kMaxBuffer || R * f >= kMaxBuffer || 2 * (int64_t)d * f >= kMaxBuffer ||
-      4 * R * (d / MOE_BLOCK + f / MOE_BLOCK) >= kMaxBuffer)
+      4 * R * (d / MOE_BLOCK + f / MOE_BLOCK) >= kMaxBuffer || 4 * R * d >= kMaxBuffer)
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -86,7 +90,7 @@ const char* moe_status_string(int32_t s) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "invalid shape (T < 0, or d/f not a positive multiple of 128, or E < 1)";
-    case MOE_ERR_UNSUPPORTED: return "unsupported sizes (k outside [1, min(E, 8)], E > 256, or too many rows)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported sizes (k outside [1, min(E, 8)], E > 256, d or f > 8192, or a buffer of 2^31 bytes or more)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MOE_ERR_HIP: return "a HIP kernel launch failed";
@@ -100,7 +104,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                               const void* b_gateup, const uint8_t* W_down, const float* S_down,
                               const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
                               int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
-                              int32_t first_stage, int32_t last_stage, void* stream_) {
+                              int32_t first_stage, int32_t last_stage, hipStream_t stream) {
   const moe_status sz = check_sizes(T, d, f, E, k);
   if (sz != MOE_OK) return sz;
   if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX |
@@ -125,7 +129,6 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   const Layout l = make_layout(T, d, f, E, k);
   if (workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
 
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   auto at = [&](size_t off) { return ws + off; };
   float* partial = reinterpret_cast<float*>(at(l.partial));
@@ -247,7 +250,7 @@ moe_status moe_forward_ex(const void* x, const float* W_router, const float* b_r
                           const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                           const uint8_t* W_down, const float* S_down, const void* b_down,
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream) {
+                          size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
   return moe_forward_stages(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
                             b_down, out, T, d, f, E, workspace, workspace_bytes, flags, 0,
                             MOE_NUM_STAGES - 1, stream);
@@ -257,7 +260,7 @@ moe_status moe_forward(const void* x, const float* W_router, const float* b_rout
                        const uint8_t* W_gateup, const float* S_gateup, const void* b_gateup,
                        const uint8_t* W_down, const float* S_down, const void* b_down, void* out,
                        int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, hipStream_t stream) {
   return moe_forward_ex(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
                         b_down, out, T, d, f, E, workspace, workspace_bytes, MOE_PATH_AUTO, stream);
 }
@@ -266,7 +269,7 @@ moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_r
                           const uint8_t* W_gateup, const uint8_t* X_gateup, const void* b_gateup,
                           const uint8_t* W_down, const uint8_t* X_down, const void* b_down,
                           void* out, int32_t T, int32_t d, int32_t f, int32_t E, void* workspace,
-                          size_t workspace_bytes, uint32_t flags, void* stream) {
+                          size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
   return moe_forward_stages(x, W_router, b_router, k, W_gateup,
                             reinterpret_cast<const float*>(X_gateup), b_gateup, W_down,
                             reinterpret_cast<const float*>(X_down), b_down, out, T, d, f, E,
@@ -279,14 +282,13 @@ moe_status moe_forward_debug(const void* x, const float* W_router, const float* 
                              const void* b_gateup, const uint8_t* W_down, const float* S_down,
                              const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
                              int32_t E, void* workspace, size_t workspace_bytes, uint32_t flags,
-                             void* stream_, int32_t* topk_idx, float* topk_w, int32_t* offsets,
+                             hipStream_t stream, int32_t* topk_idx, float* topk_w, int32_t* offsets,
                              int32_t* row_token, int32_t* row_of, uint8_t* xq, float* xs,
                              uint8_t* hq, float* hs, float* y) {
   const moe_status st =
       moe_forward_ex(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
-                     b_down, out, T, d, f, E, workspace, workspace_bytes, flags, stream_);
+                     b_down, out, T, d, f, E, workspace, workspace_bytes, flags, stream);
   if (st != MOE_OK || T == 0) return st;
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
   const Layout l = make_layout(T, d, f, E, k);
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
   const size_t R = (size_t)T * k;

@@ -6,8 +6,9 @@
 // max-subtracted form of section "Sink attention").  Section "GPT-OSS on
 // Hopper" fixes FP8 with 128x128 block scaling; activations are quantised per
 // token per 128 columns so that every 128-deep K block of the expert GEMMs has
-// one activation scale per row.  Its section "Quantization" names MXFP8
-// microscaling for Blackwell: there every 32 columns get an E8M0 scale.
+// one activation scale per row.  "Hosting Qwen on Blackwell", section
+// "Quantization", serves the experts in MXFP8 microscaling on Blackwell:
+// there every 32 columns get an E8M0 scale.
 //
 // Design: every wave owns 16 tokens.  The logits run on the bf16 matrix
 // cores with each fp32 router weight split into three exact bf16 parts, so
@@ -244,10 +245,10 @@ __global__ __launch_bounds__(256) void router_kernel(
         }
       }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
-      am = fmaxf(am, __shfl_xor(am, 16));
-      am = fmaxf(am, __shfl_xor(am, 32));
-      const float s = am > 0.f ? am / kFp8Max : 1.0f;
+      for (int i = 0; i < 32; ++i) am = nan_max(am, fabsf(v[i]));
+      am = nan_max(am, __shfl_xor(am, 16));
+      am = nan_max(am, __shfl_xor(am, 32));
+      const float s = group_scale(am);
       if (mx) {
         // MXFP8: columns 32c..32c+31 of the group are one block, held 8 per
         // lane by the four lanes l16 + 16 gq; E8M0 codes of the 4 blocks -> one dword
@@ -256,9 +257,9 @@ __global__ __launch_bounds__(256) void router_kernel(
         for (int c = 0; c < 4; ++c) {
           float bm = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(v[8 * c + i]));
-          bm = fmaxf(bm, __shfl_xor(bm, 16));
-          bm = fmaxf(bm, __shfl_xor(bm, 32));
+          for (int i = 0; i < 8; ++i) bm = nan_max(bm, fabsf(v[8 * c + i]));
+          bm = nan_max(bm, __shfl_xor(bm, 16));
+          bm = nan_max(bm, __shfl_xor(bm, 32));
           const uint32_t code = mx_code(bm);
           const float inv = mx_inv_scale(code);
           if (xt < T)
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(256) void router_kernel(
         for (int c = 0; c < 4; ++c) {
           float q[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[8 * c + i] / s, -kFp8Max), kFp8Max);
+          for (int i = 0; i < 8; ++i) q[i] = clamp_fp8(v[8 * c + i] / s);
           *reinterpret_cast<uint2*>(xq + (size_t)xt * d + g * kBlock + 32 * c + 8 * gq) =
               make_uint2(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), f32x4_to_e4m3(q[4], q[5], q[6], q[7]));
         }

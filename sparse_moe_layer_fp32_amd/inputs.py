@@ -10,8 +10,8 @@ three input-preparation jobs:
 * converts expert weights statically, as the "GPT-OSS on day 0" post's
   serving formats need: FP8 e4m3 with one fp32 scale per 128x128 block
   (section "GPT-OSS on Hopper"), or MXFP8 with one E8M0 power-of-two scale
-  per 32 rows of K per column (section "Quantization": microscaling, weights
-  converted statically), both rounded by PyTorch's ``float8_e4m3fn`` cast (a
+  per 32 rows of K per column (the "Hosting Qwen on Blackwell" post, section
+  "Quantization": microscaling, weights converted statically), both rounded by PyTorch's ``float8_e4m3fn`` cast (a
   library routine), or MXFP4 (section "GPT-OSS on Hopper": the checkpoints
   ship in MXFP4): E2M1 codes with the same scale blocks, rounded here by a
   nearest-value search, packed two per byte along K;

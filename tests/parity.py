@@ -8,12 +8,23 @@ Gates (written here, used by every GPU parity test):
 * activation quantisation: x codes and scales (fp32 per 128 columns, or E8M0
   per 32 columns for the MXFP8 format) are bit-identical;
 * output: with o the oracle's unrounded fp64 output and g the GPU's bf16,
-  over the real (unpadded) columns,
-      max|g - o| <= 2e-2 * RMS(o)   and   sum|g - o| / sum|o| <= 5e-3.
-  bf16 rounding of o alone can exceed the max gate for rare large outputs
-  (2e-2 is 5.12 bf16 half-spacings of RMS); when the literal max gate fails,
-  the gate is applied to max(|g - o| - |bf16(o) - o|), the error beyond the
-  output format's own rounding, and both numbers are reported.
+  over the real (unpadded) columns, the mean gate
+      sum|g - o| / sum|o| <= 5e-3
+  always holds, and the max gate holds in one of three forms, reported by
+  name (``check_end_to_end``):
+  - "literal":  max|g - o| <= 2e-2 * RMS(o);
+  - "bf16-floor": only where the bf16 rounding of o ALONE exceeds the bound
+    (max|bf16(o) - o| > 2e-2 * RMS(o): 2e-2 is 5.12 bf16 half-spacings of RMS,
+    so rare large outputs near a rounding midpoint cannot meet it in bf16),
+    the bound applies to max(|g - o| - |bf16(o) - o|), the error beyond the
+    output format's own rounding;
+  - "decision-adjusted": the max gate (literal, or bf16-floor under the same
+    precondition) against the oracle with its h decisions replaced by the
+    GPU's validated ones (``decision_adjusted_reference``): an h code or
+    scale is a floating-point-decided integer, taken here in the kernel's
+    precision.
+  A result that passes only in the third form is a miss of the literal gate,
+  and is reported as one.
 """
 from __future__ import annotations
 
@@ -43,14 +54,6 @@ def output_metrics(g: np.ndarray, o: np.ndarray) -> dict:
                 floor_rel_rms=float(floor.max(initial=0.0) / rms) if rms else 0.0,
                 mean_rel=float(err.sum() / np.abs(o).sum()) if o.size and np.abs(o).sum() else 0.0,
                 mean_elem_rel=float(np.mean(err / np.maximum(np.abs(o), 1e-30))) if o.size else 0.0)
-
-
-def check_output(g: np.ndarray, o: np.ndarray, what="out") -> dict:
-    m = output_metrics(g, o)
-    ok_max = m["max_rel_rms"] <= MAX_REL_RMS or m["max_excess_rel_rms"] <= MAX_REL_RMS
-    assert ok_max, f"{what}: max error {m}"
-    assert m["mean_rel"] <= MEAN_REL, f"{what}: mean relative error {m}"
-    return m
 
 
 def check_routing(dbg: dict, ref: dict, T: int, k: int, gate_bf16: bool = False):
@@ -214,28 +217,68 @@ def decision_adjusted_reference(dbg: dict, ref: dict, inp: dict):
     return adj
 
 
+def _max_gate(g: np.ndarray, o: np.ndarray, rms: float):
+    """(form, max_rel_rms, floor_rel_rms, excess_rel_rms) of the max gate of g
+    against o: "literal", "bf16-floor" (only when the floor alone exceeds the
+    bound) or None when neither holds."""
+    err = np.abs(g - o)
+    floor = np.abs(codecs.bf16_round(o) - o)
+    mx = float(err.max(initial=0.0) / rms) if rms else 0.0
+    fl = float(floor.max(initial=0.0) / rms) if rms else 0.0
+    ex = float(np.max(err - floor, initial=0.0) / rms) if rms else 0.0
+    if mx <= MAX_REL_RMS:
+        return "literal", mx, fl, ex
+    if fl > MAX_REL_RMS and ex <= MAX_REL_RMS:
+        return "bf16-floor", mx, fl, ex
+    return None, mx, fl, ex
+
+
 def check_end_to_end(g: np.ndarray, dbg: dict, ref: dict, inp: dict, d_real: int) -> dict:
-    """The end-to-end accuracy gates against the oracle; where the literal max gate fails,
-    the same gate is applied after accounting for the admissible h decisions
-    (see check_h_decisions), and both results are returned."""
+    """The end-to-end accuracy gates against the oracle (module docstring).
+    Returns the metrics with ``gate`` = the form of the max gate that holds
+    ("literal", "bf16-floor" or "decision-adjusted"); with the last one the
+    adjusted metrics are under ``adjusted``."""
     o = ref["out64"][:, :d_real]
-    m = output_metrics(g[:, :d_real], o)
+    g = g[:, :d_real]
+    m = output_metrics(g, o)
     assert m["mean_rel"] <= MEAN_REL, f"out: mean relative error {m}"
-    if m["max_rel_rms"] <= MAX_REL_RMS or m["max_excess_rel_rms"] <= MAX_REL_RMS:
-        m["gate"] = "literal"
+    form, *_ = _max_gate(g, o, m["rms"])
+    if form is not None:
+        m["gate"] = form
         return m
     adj = decision_adjusted_reference(dbg, ref, inp)[:, :d_real]
-    ma = output_metrics(g[:, :d_real], adj)
-    ma["rms"] = m["rms"]
-    rms = m["rms"]
-    ma["max_rel_rms"] = float(np.abs(g[:, :d_real] - adj).max() / rms)
-    floor = np.abs(codecs.bf16_round(adj) - adj)
-    ma["max_excess_rel_rms"] = float(np.max(np.abs(g[:, :d_real] - adj) - floor) / rms)
-    assert ma["max_rel_rms"] <= MAX_REL_RMS or ma["max_excess_rel_rms"] <= MAX_REL_RMS, \
-        f"out: max error {m}; with the GPU's h decisions {ma}"
-    m["gate"] = "h-decision adjusted"
+    aform, amx, afl, aex = _max_gate(g, adj, m["rms"])
+    ma = dict(max_rel_rms=amx, floor_rel_rms=afl, max_excess_rel_rms=aex, form=aform,
+              mean_rel=float(np.abs(g - adj).sum() / np.abs(o).sum()))
+    assert aform is not None, f"out: max error {m}; against the GPU's h decisions {ma}"
+    m["gate"] = "decision-adjusted"
     m["adjusted"] = ma
     return m
+
+
+def record(row: dict):
+    """Append one result row (JSON) to the file named by $MOE_PARITY_LOG, if set:
+    the full-size parity table is assembled from these rows."""
+    import json
+    import os
+    path = os.environ.get("MOE_PARITY_LOG")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(row) + "\n")
+
+
+def tile_edge_tokens(offsets: np.ndarray, row_token: np.ndarray, tile_rows=(32, 192)) -> np.ndarray:
+    """Tokens of the first and last row of every expert's last row tile, for
+    the GEMMs' row-tile heights: the ragged tails of the tile lists."""
+    toks = []
+    for e in range(len(offsets) - 1):
+        c = int(offsets[e + 1] - offsets[e])
+        if c == 0:
+            continue
+        for bm in tile_rows:
+            first = int(offsets[e]) + ((c - 1) // bm) * bm
+            toks += [int(row_token[first]), int(row_token[int(offsets[e + 1]) - 1])]
+    return np.unique(np.asarray(toks, np.int64))
 
 
 def oracle_ref(inp: dict, tokens=None, keep=True):

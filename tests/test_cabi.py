@@ -85,6 +85,20 @@ def test_argument_errors(kw, want):
     assert call(**kw) == want
 
 
+def test_expert_output_buffer_bound():
+    # Y (fp32 [T*k, d]) is addressed with 32-bit offsets: 4*T*k*d must stay below
+    # 2^31.  d=4096, k=8: T=16383 fits (4*16383*8*4096 < 2^31), T=16384 does not,
+    # while every other buffer of these sizes is far below the bound.
+    assert moe.workspace_bytes(16383, 4096, 1536, 128, 8) > 0
+    assert moe.workspace_bytes(16384, 4096, 1536, 128, 8) == 0
+    assert moe.workspace_bytes(16448, 4096, 1536, 128, 8) == 0
+    assert call(T=16384, d=4096, f=1536, E=128, k=8, ws=1 << 40) == ERR_UNSUP
+    assert call(T=16448, d=4096, f=1536, E=128, k=8, ws=1 << 40, entry="mx") == ERR_UNSUP
+    # the skewed gpt-oss-120b-like layer (d=2944, k=4) reaches the bound at T=45591
+    assert moe.workspace_bytes(45590, 2944, 2944, 128, 4) > 0
+    assert moe.workspace_bytes(45591, 2944, 2944, 128, 4) == 0
+
+
 def test_gate_options_are_accepted_flags():
     # the routing options are valid bits: with an empty batch the call returns OK
     for fl in (4, 8, 12, 1 | 4, 2 | 8, 1 | 4 | 8):
