@@ -1,18 +1,30 @@
 """Benchmark of the sparse MoE block forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c1] [--format block128|mx|mxfp4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4b] [--format block128|mx|mxfp4]
+                    [--flush-mib 512]
     python bench.py --workload attn_prefill | attn_decode
 
 A step is one whole forward (router + top-k + softmax + x quantisation,
 routing scan and placement, gate/up grouped FP8 GEMM with SwiGLU and h
 quantisation, down grouped FP8 GEMM, weighted combine) over one batch of
 seeded synthetic input already resident in HBM.  The default workload is the
-decode-shaped gpt-oss-20b-like layer (T=64 tokens, d=2944, f=2944, E=32,
-k=4) with 128x128 block-scaled FP8 weights (``--format mx``: the MXFP8
-variant, E8M0 scales per 32; ``--format mxfp4``: E2M1 weights with those scales).  Prints one JSON line: whole-job tokens/s, the roofline of the gate/up
-GEMM (its duration measured with HIP events inside the timed region, on the
-stream it runs on) and the CPU oracle timed on a bounded sample of the same
-workload.
+largest configuration that fits one GPU: the skewed gpt-oss-120b-like layer
+at prefill size (T=16384 tokens, d=2944, f=2944, E=128, k=4, Zipf(1.1)
+expert popularity) with 128x128 block-scaled FP8 weights (``--format mx``:
+the MXFP8 variant, E8M0 scales per 32; ``--format mxfp4``: E2M1 weights with
+those scales).  ``--workload c1`` is the decode-shaped layer (T=64).
+
+Prints one JSON line: whole-job tokens/s; the roofline of the gate/up GEMM
+(its duration measured with HIP events inside the timed region, on the
+stream it runs on); ``layer_frac``, the whole step's algorithmic work over
+the step time against the binding peak (FP8 MFMA flops for prefill shapes,
+HBM bytes for decode shapes); and the CPU oracle timed on a bounded sample
+of the same workload.
+
+``--flush-mib N`` writes N MiB (more than the 4 MB L2 of each XCD and the
+256 MB memory-side cache) between timed calls, outside the calls' own
+events, so every call reads its weights from HBM; the step time is then the
+mean of the per-call event times.
 
 ``--workload attn_prefill`` / ``attn_decode`` time the attention with per-head
 sinks instead (gpt-oss shape: 64 query heads, 8 key/value heads, head dim
@@ -189,6 +201,36 @@ def down_algorithmic(inp, counts):
     return dict(bytes=w + R * f + _act_scale_bytes(R, f) + 4 * R * d, flops=2.0 * R * f * d)
 
 
+def host_facts():
+    """CPU model and the BLAS library NumPy runs the oracle's matmuls on."""
+    from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', 'n/a')} threads)"
+            for i in threadpool_info() if i.get("user_api") == "blas"]
+    return model, "; ".join(blas) or "unknown", f"numpy {np.__version__}"
+
+
+def layer_algorithmic(inp, counts):
+    """Algorithmic work of one whole forward: FP8 flops 2*T*k*(d*2f + f*d),
+    and HBM bytes = every touched expert's weights, scales and biases once +
+    the router weights and bias + x in + out (bf16)."""
+    T, d, f, E, k = inp["T"], inp["d"], inp["f"], inp["E"], inp["k"]
+    fmt = inp.get("format", "block128")
+    touched = int(np.count_nonzero(counts))
+    per_expert = (_weight_bytes(d, 2 * f, fmt) + _scale_bytes(d, 2 * f, fmt) + 2 * 2 * f +
+                  _weight_bytes(f, d, fmt) + _scale_bytes(f, d, fmt) + 2 * d)
+    byts = touched * per_expert + 4 * d * E + 4 * E + 2 * T * d + 2 * T * d
+    return dict(bytes=byts, flops=2.0 * T * k * (d * 2 * f + f * d), touched=touched)
+
+
 def cpu_baseline(inp, budget_s=12.0):
     """The CPU oracle (as it stands) on a bounded sample of the workload's tokens."""
     from threadpoolctl import threadpool_info
@@ -206,8 +248,9 @@ def cpu_baseline(inp, budget_s=12.0):
             break
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model, blas, npv = host_facts()
     return {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": model, "blas": blas, "numpy": npv,
             "sample": f"{reps} x oracle.forward on the first {n} of {T} tokens (routing of all "
                       f"{T} tokens, expert math of the sample, fp64 NumPy; {dt:.1f} s)"}
 
@@ -307,13 +350,91 @@ def attn_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def peaks_bench(args):
+    """Measured ceilings of this GPU (libmoe_peaks.so): FP8 MFMA issue rate and
+    the shader clock it settles at, HBM streaming read and device copy rates,
+    and the LDS read rates (bytes per clock per CU) of ds_read_b128 and the
+    transposing ds_read_b64_tr_b8 the GEMMs read their fragments with."""
+    import ctypes
+    from sparse_moe_layer_fp32_amd import build as b
+    if not os.path.exists(b.PEAKS_LIB):
+        raise ImportError(f"{b.PEAKS_LIB} is missing: build the package first")
+    L = ctypes.CDLL(b.PEAKS_LIB)
+    P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    L.peak_mfma_fp8.argtypes = [I, I, P, P, P]
+    L.peak_hbm_read.argtypes = [P, LL, I, P, P]
+    L.peak_lds_read.argtypes = [I, I, I, I, P, P, P]
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            z.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(z))
+        return ms
+
+    res = {"metric": "peaks", "cus": cus, "device": torch.cuda.get_device_name(dev)}
+    # FP8 MFMA: two waves per SIMD, 8 independent 16x16x128 chains each
+    blocks, iters = 2 * cus, 20000
+    sink = torch.empty(blocks * 4, dtype=torch.float32, device=dev)
+    timing = torch.empty(blocks * 8, dtype=torch.int64, device=dev)
+    log("[peaks] FP8 MFMA loop")
+    for _ in range(20):                        # the clock settles under sustained load
+        assert L.peak_mfma_fp8(blocks, iters, P(sink.data_ptr()), P(timing.data_ptr()), stream) == 0
+    ms = timed(lambda: L.peak_mfma_fp8(blocks, iters, P(sink.data_ptr()), P(timing.data_ptr()), stream), 10)
+    flops = blocks * 4 * iters * 8 * 2.0 * 16 * 16 * 128
+    cyc = timing.view(-1, 2)[:, 0].double().mean().item()
+    best = min(ms)
+    res["fp8_mfma_tflops"] = round(flops / (best * 1e-3) / 1e12, 1)
+    res["fp8_mfma_frac_of_spec"] = round(res["fp8_mfma_tflops"] / FP8_PEAK_TFLOPS, 4)
+    res["clock_ghz_under_mfma_load"] = round(cyc / (best * 1e-3) / 1e9, 3)
+    res["mfma_cycles_per_16x16x128"] = round(cyc / (iters * 8 * 2), 2)   # two waves share a SIMD
+    # HBM streaming read of 4 GiB and a 2 GiB device copy
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    hsink = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+    log("[peaks] HBM read")
+    ms = timed(lambda: L.peak_hbm_read(P(buf.data_ptr()), n, cus * 8, P(hsink.data_ptr()), stream), 10)
+    res["hbm_read_GBs"] = round(n / (min(ms) * 1e-3) / 1e9, 1)
+    res["hbm_read_frac_of_spec"] = round(res["hbm_read_GBs"] / HBM_PEAK_GBS, 4)
+    del buf
+    src = torch.ones(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    log("[peaks] device copy")
+    ms = timed(lambda: dst.copy_(src), 10)
+    res["copy_read_plus_write_GBs"] = round(2 * (1 << 31) / (min(ms) * 1e-3) / 1e9, 1)
+    del src, dst
+    # LDS read rates, one workgroup of 8 waves per CU
+    iters = 4096
+    lsink = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+    ltim = torch.empty(cus * 16, dtype=torch.int64, device=dev)
+    for tr, name, lane_bytes in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b8", 8)):
+        log(f"[peaks] LDS {name}")
+        ms = timed(lambda: L.peak_lds_read(cus, 8, iters, tr, P(lsink.data_ptr()), P(ltim.data_ptr()), stream), 5)
+        cyc = ltim.view(-1, 2)[:, 0].double().max().item()
+        per_cu = 8 * iters * 8 * 64 * lane_bytes
+        res[f"lds_{name}_bytes_per_clk_per_cu"] = round(per_cu / cyc, 1)
+    torch.cuda.synchronize()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     # compute-bound kernels reach their steady clock after about 20 launches
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="c1", choices=sorted(gen.CONFIGS) + ["attn_decode", "attn_prefill"])
+    ap.add_argument("--workload", default="c4b",
+                    choices=sorted(gen.CONFIGS) + ["attn_decode", "attn_prefill", "peaks"])
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),
                     help="weight format: 128x128 block-scaled FP8, MXFP8 (E8M0 per 32) or MXFP4")
@@ -322,6 +443,9 @@ def main():
                     help="record the per-kernel timing events on every N-th timed step only (each "
                          "event costs a few microseconds of device time; the other steps run the "
                          "plain call)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB between timed calls (outside the calls' events) so "
+                         "that every call reads its weights from HBM; 0: back-to-back steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, one device-to-device copy of this many MiB "
                          "(a kernel of known traffic for scaling HBM byte counters)")
@@ -333,6 +457,9 @@ def main():
 
     if args.workload.startswith("attn"):
         attn_bench(args)
+        return
+    if args.workload == "peaks":
+        peaks_bench(args)
         return
 
     cfg = gen.CONFIGS[args.workload]
@@ -373,24 +500,40 @@ def main():
             ev[2].record()
         moe.forward_stages("combine", "combine", x, *w_args, out, ws, path=args.path, fmt=fmt)
 
+    flush = None
+    if args.flush_mib > 0:
+        flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     sampled = sampled_steps(args.steps, args.event_every)
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)] if flush is not None else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps (stage events on {len(sampled)} of them)")
+    log(f"[bench] timing {args.steps} steps (stage events on {len(sampled)} of them"
+        + (f", {args.flush_mib} MiB flush before each)" if flush is not None else ")"))
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        step(evs.get(i))
+        if flush is not None:
+            flush.fill_(float(i))            # untimed: evicts L2 and the memory-side cache
+            calls[i][0].record()
+            step(evs.get(i))
+            calls[i][1].record()
+        else:
+            step(evs.get(i))
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     gate_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs.values()]))
     down_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs.values()]))
-    ms = total_ms / args.steps
+    if flush is not None:
+        ms = float(np.mean([a.elapsed_time(b) for a, b in calls]))
+    else:
+        ms = total_ms / args.steps
     tok_s = T / (ms * 1e-3)
 
     decode = (args.path == "decode") or (args.path == "auto" and T * k <= 32 * E)
@@ -413,6 +556,15 @@ def main():
     roof["algorithmic_bytes"] = ga["bytes"]
     roof["algorithmic_flops"] = ga["flops"]
 
+    la = layer_algorithmic(inp, counts)
+    if decode:
+        layer = {"bound": "hbm", "achieved": round(la["bytes"] / (ms * 1e-3) / 1e9, 1),
+                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": la["bytes"]}
+    else:
+        layer = {"bound": "mfma", "achieved": round(la["flops"] / (ms * 1e-3) / 1e12, 1),
+                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "algorithmic_flops": la["flops"]}
+    layer["frac"] = round(layer["achieved"] / layer["peak"], 4)
+
     res = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -423,6 +575,10 @@ def main():
                    "T": T, "d": d, "f": f, "E": E, "k": k, "path": args.path, "format": fmt,
                    "experts_touched": ga["touched"]},
         "roofline": roof,
+        "layer_frac": layer["frac"],
+        "layer_roofline": layer,
+        "flush_mib": args.flush_mib,
+        "timed_region_ms": round(total_ms, 3),
         "stages_ms": {"gateup": round(gate_ms, 5), "down": round(down_ms, 5),
                       "rest": round(ms - gate_ms - down_ms, 5)},
         "down_gemm": {"achieved_GBs": round(da["bytes"] / (down_ms * 1e-3) / 1e9, 1),

@@ -17,6 +17,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_moe.so")
+# measurement kernels (peak rates of the chip), a library of their own
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_LIB = os.path.join(PKG, "libmoe_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 ARCH = "gfx950"
@@ -59,6 +62,11 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp"
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", PEAKS_SRC, "-o", tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PEAKS_SRC}:\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
     return LIB
 
 
