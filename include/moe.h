@@ -90,8 +90,10 @@ typedef enum {
   MOE_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than moe_workspace_bytes */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                   */
   MOE_ERR_HIP = -6,         /* a kernel launch failed (hipGetLastError)           */
-  MOE_ERR_FLAGS = -7        /* unknown bits in `flags`, path 3, MOE_WEIGHTS_FP4 without
+  MOE_ERR_FLAGS = -7,       /* unknown bits in `flags`, path 3, MOE_WEIGHTS_FP4 without
                                MOE_FORMAT_MX, or a bad stage range */
+  MOE_ERR_SCRATCH = -8      /* moe_forward_noalloc: the sizes need more workspace
+                               than MOE_SCRATCH_BYTES                             */
 } moe_status;
 
 #define MOE_MAX_EXPERTS 256
@@ -251,6 +253,27 @@ moe_status moe_forward_debug(const void* x, const float* W_router, const float* 
                              hipStream_t stream, int32_t* topk_idx, float* topk_w, int32_t* offsets,
                              int32_t* row_token, int32_t* row_of, uint8_t* xq, float* xs,
                              uint8_t* hq, float* hs, float* y);
+
+/* moe_forward_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the library's own static device array of
+ * MOE_SCRATCH_BYTES per GPU serves as the workspace.  It is set up on the
+ * first call on each device (its address is looked up with that device
+ * current) and each GPU holds it until the process ends.  The call allocates
+ * nothing.  Sizes whose moe_workspace_bytes exceeds MOE_SCRATCH_BYTES return
+ * MOE_ERR_SCRATCH before anything is enqueued (64 MiB holds decode-sized
+ * batches: a 2944-wide layer with k = 4 and 32 experts up to 1025 tokens,
+ * with 128 experts up to 902).  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or host threads without ordering) race and give
+ * undefined results; order them on one stream.  Nothing in the array has to
+ * start at zero, so its leftover content from an earlier call is harmless. */
+#define MOE_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const void* x, const float* W_router, const float* b_router,
+                               int32_t k, const uint8_t* W_gateup, const float* S_gateup,
+                               const void* b_gateup, const uint8_t* W_down, const float* S_down,
+                               const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
+                               int32_t E, uint32_t flags, hipStream_t stream);
 
 /* Static text for a status code (never NULL; "unknown status" for other
  * values), so callers can report an error without a device call. */

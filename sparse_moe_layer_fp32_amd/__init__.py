@@ -36,7 +36,7 @@ MAX_EXPERTS = 256
 MAX_TOPK = 8
 
 SYMBOLS = ("moe_workspace_bytes", "moe_forward", "moe_forward_ex", "moe_forward_mx",
-           "moe_forward_stages", "moe_forward_debug", "moe_status_string",
+           "moe_forward_stages", "moe_forward_debug", "moe_forward_noalloc", "moe_status_string",
            "attn_sink_prefill", "attn_sink_decode_workspace_bytes", "attn_sink_decode")
 STAGES = {"router": 0, "scan": 1, "place": 2, "gateup": 3, "down": 4, "combine": 5}
 
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
     L.moe_forward_stages.argtypes = fwd + [U, I, I, P]
     L.moe_forward_debug.restype = I
     L.moe_forward_debug.argtypes = fwd + [U, P] + [P] * 10
+    L.moe_forward_noalloc.restype = I
+    L.moe_forward_noalloc.argtypes = fwd[:15] + [U, P]
     L.moe_status_string.restype = ctypes.c_char_p
     L.moe_status_string.argtypes = [I]
     F = ctypes.c_float
@@ -140,7 +142,7 @@ def scale_shapes(d, f, E, fmt="block128"):
 
 
 def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
-          out, workspace, fmt="block128"):
+          out, workspace, fmt="block128", need_workspace=True):
     T, d = x.shape
     E = W_router.shape[1]
     f = W_down.shape[1] * (2 if fmt == "mxfp4" else 1)
@@ -161,12 +163,11 @@ def _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down
     if out is None:
         out = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
     _expect(out, "out", (T, d), 2, dev)
-    need = workspace_bytes(T, d, f, E, k)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if need_workspace and workspace is None:
+        workspace = torch.empty(max(workspace_bytes(T, d, f, E, k), 1), dtype=torch.uint8, device=dev)
     args = [_ptr(x), _ptr(W_router), _ptr(b_router), int(k), _ptr(W_gateup), _ptr(S_gateup),
             _ptr(b_gateup), _ptr(W_down), _ptr(S_down), _ptr(b_down), _ptr(out), T, d, f, E,
-            _ptr(workspace), workspace.numel() * workspace.element_size()]
+            _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size()]
     return args, out, workspace, (T, d, f, E)
 
 
@@ -182,6 +183,25 @@ def forward(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_do
                              S_down, b_down, out, workspace, fmt)
     entry = lib().moe_forward_mx if fmt in MX_FORMATS else lib().moe_forward_ex
     _check(entry(*args, flags_of(path, routing, gate_bf16, fmt), _stream(x.device, stream, ws, out)))
+    return out
+
+
+SCRATCH_BYTES = 64 << 20   # MOE_SCRATCH_BYTES
+
+
+def forward_noalloc(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down,
+                    out, path="auto", stream=None, routing="topk_softmax", gate_bf16=False,
+                    fmt="block128"):
+    """``forward`` through ``moe_forward_noalloc``: the library's static device
+    scratch is the workspace, and the caller passes ``out`` (nothing is
+    allocated here or in the library).  Raises MoeError (status -8) when the
+    sizes need more than ``SCRATCH_BYTES`` of workspace."""
+    if out is None:
+        raise ValueError("forward_noalloc writes into a caller-provided `out`")
+    args, out, _, _ = _args(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down,
+                            S_down, b_down, out, None, fmt, need_workspace=False)
+    _check(lib().moe_forward_noalloc(*args[:15], flags_of(path, routing, gate_bf16, fmt),
+                                     _stream(x.device, stream, out)))
     return out
 
 

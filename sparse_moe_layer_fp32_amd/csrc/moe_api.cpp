@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.hpp"
 #include "moe.h"
@@ -76,6 +77,36 @@ moe_status check_sizes(int32_t T, int32_t d, int32_t f, int32_t E, int32_t k) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The workspace of moe_forward_noalloc: a device array of the library, one
+// copy per GPU, alive until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the address
+// that hipGetSymbolAddress returns for the current device instead.
+constexpr size_t kScratchBytes = MOE_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup failed.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  static std::once_flag once[kMaxScratchDevices];
+  static void* ptr[kMaxScratchDevices];
+  std::call_once(once[dev], [&] {
+    void* p = nullptr;
+    ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return ptr[dev];
+}
+
+bool valid_flags(uint32_t flags) {
+  return (flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX |
+                    MOE_WEIGHTS_FP4)) == 0u &&
+         (flags & MOE_PATH_MASK) != MOE_PATH_MASK &&
+         !((flags & MOE_WEIGHTS_FP4) != 0u && (flags & MOE_FORMAT_MX) == 0u);
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +126,7 @@ const char* moe_status_string(int32_t s) {
     case MOE_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MOE_ERR_HIP: return "a HIP kernel launch failed";
     case MOE_ERR_FLAGS: return "unknown flags";
+    case MOE_ERR_SCRATCH: return "these sizes need more workspace than the library's static scratch (MOE_SCRATCH_BYTES); pass a workspace to moe_forward_ex instead";
     default: return "unknown status";
   }
 }
@@ -107,11 +139,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
                               int32_t first_stage, int32_t last_stage, hipStream_t stream) {
   const moe_status sz = check_sizes(T, d, f, E, k);
   if (sz != MOE_OK) return sz;
-  if ((flags & ~(MOE_PATH_MASK | MOE_ROUTE_SOFTMAX_ALL | MOE_GATE_BF16 | MOE_FORMAT_MX |
-                 MOE_WEIGHTS_FP4)) != 0u ||
-      (flags & MOE_PATH_MASK) == MOE_PATH_MASK ||
-      ((flags & MOE_WEIGHTS_FP4) != 0u && (flags & MOE_FORMAT_MX) == 0u))
-    return MOE_ERR_FLAGS;
+  if (!valid_flags(flags)) return MOE_ERR_FLAGS;
   const uint32_t path = flags & MOE_PATH_MASK;
   const bool mx = (flags & MOE_FORMAT_MX) != 0u;
   const int fmt = (flags & MOE_WEIGHTS_FP4) ? moe::kFmtMxFp4 : mx ? moe::kFmtMx : moe::kFmtBlock;
@@ -274,6 +302,30 @@ moe_status moe_forward_mx(const void* x, const float* W_router, const float* b_r
                             reinterpret_cast<const float*>(X_gateup), b_gateup, W_down,
                             reinterpret_cast<const float*>(X_down), b_down, out, T, d, f, E,
                             workspace, workspace_bytes, flags | MOE_FORMAT_MX, 0,
+                            MOE_NUM_STAGES - 1, stream);
+}
+
+moe_status moe_forward_noalloc(const void* x, const float* W_router, const float* b_router,
+                               int32_t k, const uint8_t* W_gateup, const float* S_gateup,
+                               const void* b_gateup, const uint8_t* W_down, const float* S_down,
+                               const void* b_down, void* out, int32_t T, int32_t d, int32_t f,
+                               int32_t E, uint32_t flags, hipStream_t stream) {
+  const moe_status sz = check_sizes(T, d, f, E, k);
+  if (sz != MOE_OK) return sz;
+  if (make_layout(T, d, f, E, k).total > kScratchBytes) return MOE_ERR_SCRATCH;
+  if (!valid_flags(flags)) return MOE_ERR_FLAGS;
+  if (T == 0) return MOE_OK;
+  const void* ptrs[] = {x, W_router, b_router, W_gateup, S_gateup, b_gateup, W_down, S_down, b_down, out};
+  for (const void* p : ptrs)
+    if (p == nullptr) return MOE_ERR_NULL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  void* ws = scratch_address();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  // Nothing in the workspace has to start at zero: every stage writes what
+  // the later stages read before they read it.
+  return moe_forward_stages(x, W_router, b_router, k, W_gateup, S_gateup, b_gateup, W_down, S_down,
+                            b_down, out, T, d, f, E, ws, kScratchBytes, flags, 0,
                             MOE_NUM_STAGES - 1, stream);
 }
 

@@ -11,7 +11,8 @@ import sparse_moe_layer_fp32_amd as moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "attention.h")]
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS = 0, -1, -2, -3, -4, -5, -6, -7
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS, ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
 
 
 def declared_functions():
@@ -31,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS):
+    for s in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_WS, ERR_ALIGN, ERR_HIP, ERR_FLAGS, ERR_SCRATCH):
         assert moe.status_string(s) and moe.status_string(s) != "unknown status"
     assert moe.status_string(-99) == "unknown status"
 
@@ -97,6 +98,35 @@ def test_expert_output_buffer_bound():
     # the skewed gpt-oss-120b-like layer (d=2944, k=4) reaches the bound at T=45591
     assert moe.workspace_bytes(45590, 2944, 2944, 128, 4) > 0
     assert moe.workspace_bytes(45591, 2944, 2944, 128, 4) == 0
+
+
+def noalloc_call(T=64, d=256, f=256, E=8, k=2, flags=0, null=None, misalign=None):
+    ptrs = [FAKE + 4096 * i for i in range(10)]
+    if null is not None:
+        ptrs[null] = None
+    if misalign is not None:
+        ptrs[misalign] += 4
+    x, Wr, br, Wgu, Sgu, bgu, Wdn, Sdn, bdn, out = [ctypes.c_void_p(p) if p else None for p in ptrs]
+    return moe.lib().moe_forward_noalloc(x, Wr, br, k, Wgu, Sgu, bgu, Wdn, Sdn, bdn, out, T, d, f, E,
+                                         flags, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(d=200), ERR_SHAPE), (dict(k=9, E=16), ERR_UNSUP), (dict(flags=3), ERR_FLAGS),
+    (dict(flags=32), ERR_FLAGS), (dict(null=0), ERR_NULL), (dict(null=9), ERR_NULL),
+    (dict(misalign=4), ERR_ALIGN), (dict(T=0, null=0), OK), (dict(T=0, flags=16 | 2), OK),
+    # the prefill-shaped layer needs far more than the 64 MiB scratch
+    (dict(T=8192, d=2944, f=2944, E=32, k=4), ERR_SCRATCH),
+    (dict(T=1026, d=2944, f=2944, E=32, k=4), ERR_SCRATCH),
+])
+def test_noalloc_argument_errors(kw, want):
+    # every case is decided on the host before the scratch is looked up
+    assert noalloc_call(**kw) == want
+
+
+def test_noalloc_scratch_limit_matches_the_workspace_size():
+    assert moe.workspace_bytes(1025, 2944, 2944, 32, 4) <= moe.SCRATCH_BYTES
+    assert moe.workspace_bytes(1026, 2944, 2944, 32, 4) > moe.SCRATCH_BYTES
 
 
 def test_gate_options_are_accepted_flags():
