@@ -41,7 +41,7 @@ over the real columns of the sampled tokens:
 
 def main(path, cmd):
     rows = [json.loads(line) for line in open(path) if line.strip()]
-    out = [HEAD.format(cmd=cmd)]
+    out = [HEAD.format(cmd=cmd).rstrip("\n")]
     for r in rows:
         a = r.get("adjusted") or {}
         adj = f"{a['max_rel_rms']:.4f}" if "max_rel_rms" in a else "-"
