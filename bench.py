@@ -21,10 +21,12 @@ the step time against the binding peak (FP8 MFMA flops for prefill shapes,
 HBM bytes for decode shapes); and the CPU oracle timed on a bounded sample
 of the same workload.
 
-``--flush-mib N`` writes N MiB (more than the 4 MB L2 of each XCD and the
+``--flush-mib N`` reads N MiB (more than the 4 MB L2 of each XCD and the
 256 MB memory-side cache) between timed calls, outside the calls' own
 events, so every call reads its weights from HBM; the step time is then the
-mean of the per-call event times.
+mean of the per-call event times.  The flush reads rather than writes: a
+written buffer would leave dirty lines whose write-back lands inside the
+next timed call.
 
 ``--workload attn_prefill`` / ``attn_decode`` time the attention with per-head
 sinks instead (gpt-oss shape: 64 query heads, 8 key/value heads, head dim
@@ -435,6 +437,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c4b",
                     choices=sorted(gen.CONFIGS) + ["attn_decode", "attn_prefill", "peaks"])
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (same layer), e.g. 1 or 8 for small "
+                         "decode batches of the c1 layer")
     ap.add_argument("--path", default="auto", choices=sorted(moe.PATHS))
     ap.add_argument("--format", default="block128", choices=sorted(moe.FORMATS),
                     help="weight format: 128x128 block-scaled FP8, MXFP8 (E8M0 per 32) or MXFP4")
@@ -444,7 +449,7 @@ def main():
                          "event costs a few microseconds of device time; the other steps run the "
                          "plain call)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="write this many MiB between timed calls (outside the calls' events) so "
+                    help="read this many MiB between timed calls (outside the calls' events) so "
                          "that every call reads its weights from HBM; 0: back-to-back steps")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the steps, one device-to-device copy of this many MiB "
@@ -466,7 +471,7 @@ def main():
     log(f"[bench] generating {cfg.name} (T={cfg.T}, d={cfg.layer.d}, f={cfg.layer.f}, "
         f"E={cfg.layer.E}, k={cfg.layer.k})")
     fmt = args.format
-    inp = gen.make_inputs(cfg.name, fmt=fmt)
+    inp = gen.make_inputs(cfg.name, fmt=fmt, T=args.tokens or None)
     dev = torch.device("cuda:0")
     p = moe.device_inputs(inp, dev)
     T, d, f, E, k = inp["T"], inp["d"], inp["f"], inp["E"], inp["k"]
@@ -502,7 +507,8 @@ def main():
 
     flush = None
     if args.flush_mib > 0:
-        flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        flush = torch.ones(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        flush_sink = torch.empty((), dtype=torch.float32, device=dev)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -519,7 +525,7 @@ def main():
     start.record()
     for i in range(args.steps):
         if flush is not None:
-            flush.fill_(float(i))            # untimed: evicts L2 and the memory-side cache
+            flush_sink.copy_(flush.sum())   # untimed read: evicts L2 and the memory-side cache
             calls[i][0].record()
             step(evs.get(i))
             calls[i][1].record()
@@ -571,7 +577,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.layer.name} {cfg.role} T={T} d={d} "
-                               f"(real {inp['d_real']}) f={f} E={E} k={k}",
+                               f"(real {inp['d_real']}) f={f} E={E} k={k}"
+                               + (f" (T overridden from {cfg.T})" if args.tokens else ""),
                    "T": T, "d": d, "f": f, "E": E, "k": k, "path": args.path, "format": fmt,
                    "experts_touched": ga["touched"]},
         "roofline": roof,

@@ -186,18 +186,42 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
       static_cast<int>(reinterpret_cast<uintptr_t>(p))));
 }
 
-// One output tile: {expert, first row, rows, column tile} from the tile list.
+// One output tile: {expert, first row, rows, column tile} from the tile list,
+// and the K blocks [kb0, kb1) it covers: all of them, or with split K the
+// range of split sp.
 struct DmaTile {
-  int e, row0, valid, nt;
+  int e, row0, valid, nt, kb0, kb1, sp;
 };
 
 __device__ __forceinline__ DmaTile dma_tile(const GemmArgs& g, int L) {
   const const_i32* v = (const const_i32*)g.tiles + 4 * L;  // uniform: scalar loads
-  return DmaTile{v[0], v[1], v[2], v[3]};
+  return DmaTile{v[0], v[1], v[2], v[3], 0, 0, 0};
+}
+
+// Split K: work item V is split V % ksplit of tile V / ksplit, K blocks
+// [sp * kper, min(nkb, (sp + 1) * kper)); the splits of one tile are
+// consecutive items, so they run on one XCD and share its L2.
+template <bool SPLIT>
+__device__ __forceinline__ DmaTile dma_vtile(const GemmArgs& g, int V, int nkb) {
+  if constexpr (SPLIT) {
+    const int S = g.ksplit;
+    DmaTile t = dma_tile(g, V / S);
+    t.sp = V - (V / S) * S;
+    t.kb0 = t.sp * g.kper;
+    t.kb1 = min(nkb, t.kb0 + g.kper);
+    return t;
+  } else {
+    DmaTile t = dma_tile(g, V);
+    t.kb1 = nkb;
+    return t;
+  }
 }
 
 // FP4 (with MX): E2M1 weights packed two per byte along K, K/2 stored rows.
-template <bool GATED, int BM, int BNP, bool MX, bool FP4>
+// SPLIT: every tile is cut into g.ksplit K ranges, and a work item stores
+// its promoted fp32 sums (no bias, no epilogue) into its split's slice of
+// g.part [ksplit][R][N]; a finish kernel adds the slices in split order.
+template <bool GATED, int BM, int BNP, bool MX, bool FP4, bool SPLIT>
 __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(GemmArgs g) {
   using S = DmaShape<BM, BNP, MX, FP4>;
   static_assert(MX || !FP4, "FP4 weights come with E8M0 scales");
@@ -207,7 +231,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   constexpr int MB = S::MB, NB = S::NB;             // 16x16 blocks per wave
   constexpr int WR = 16 * MB;                       // rows per wave
   constexpr int RT = GATED ? 1 : 0;                 // row-token loads per cursor move
-  constexpr int ST = GATED ? MB * 3 : MB * NB;      // epilogue stores per wave
+  constexpr int ST = (GATED && !SPLIT) ? MB * 3 : MB * NB;  // epilogue stores per wave
   __shared__ __attribute__((aligned(1024))) uint8_t st0[DMA_STAGE];  // the three ring stages
   __shared__ __attribute__((aligned(1024))) uint8_t st1[DMA_STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[DMA_STAGE];
@@ -220,8 +244,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   const int gq = lane >> 4, l16 = lane & 15;
   const int K = g.K, N = g.N, nkb = K / kBlock, nsb = N / kBlock;
 
-  // ---- this workgroup's tiles: L = lo + slot + i * nslots < hi
-  const int total = ((const const_i32*)g.tile_off)[g.E];
+  // ---- this workgroup's work items: L = lo + slot + i * nslots < hi
+  const int total = ((const const_i32*)g.tile_off)[g.E] * (SPLIT ? g.ksplit : 1);
   const int nslots = gridDim.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int lo = (blockIdx.x & 7) * chunk;
@@ -242,10 +266,11 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   const uint32_t side_dst = (MX && wave >= 4) ? SIDE_BS + MX_PITCH * (wave - 4) : 256 * wave;
 
   // ---- load cursor: tile tl (index Ll), K block kbl; the next tile prefetched
-  int Ll = L0, kbl = 0, rb = 0;
+  int Ll = L0, rb = 0;
   int Lln = Ll + nslots;
-  DmaTile tl = dma_tile(g, Ll), tln = tl;
-  if (Lln < hi) tln = dma_tile(g, Lln);
+  DmaTile tl = dma_vtile<SPLIT>(g, Ll, nkb), tln = tl;
+  int kbl = tl.kb0;
+  if (Lln < hi) tln = dma_vtile<SPLIT>(g, Lln, nkb);
   uint32_t aoff[S::A_PER], boff[S::B_PER], soff;
   auto no_loads = [&]() {
     aoff[0] = aoff[S::A_PER - 1] = soff = kOob;
@@ -329,13 +354,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   // tile, whose row tokens were loaded one move earlier; returns the number
   // of loads it issued.
   auto advance = [&]() -> int {
-    if (kbl < nkb) return 0;
-    kbl = 0;
+    if (kbl < tl.kb1) return 0;
     Ll = Lln;
     tl = tln;
+    kbl = tl.kb0;
     rb ^= 1;
     Lln += nslots;
-    if (Lln < hi) tln = dma_tile(g, Lln);
+    if (Lln < hi) tln = dma_vtile<SPLIT>(g, Lln, nkb);
     if (nkb == 1) {  // the row tokens were loaded one K block ago: wait for them
       wait_vmcnt<0>();
       asm volatile("" ::: "memory");
@@ -384,12 +409,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
   auto compute_mx = [&](const uint8_t* base) {
     const uint8_t* sA = base;
     const uint8_t* sB = base + DMA_SA;
-    if (kbc == 0) {  // accumulators start from the bias
+    if (kbc == 0) {  // accumulators start from the bias (split K: from zero)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint2 w = *reinterpret_cast<const uint2*>(base + bias_pos(nb));
-        const v4f bv = v4f{bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
-                           bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+        const v4f bv = SPLIT ? v4f{0.f, 0.f, 0.f, 0.f}
+                             : v4f{bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
+                                   bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) macc[mb][nb] = bv;
       }
@@ -425,12 +451,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     const float* sbs = reinterpret_cast<const float*>(base + DMA_SA + DMA_SB + SIDE_BS);
     const float sb0 = sbs[(GATED || BNP == 128) ? 0 : (wn >> 1)];
     const float sb1 = GATED ? sbs[1] : sb0;
-    if (kbc == 0) {  // accumulators start from the bias
+    if (kbc == 0) {  // accumulators start from the bias (split K: from zero)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const uint2 w = *reinterpret_cast<const uint2*>(base + bias_pos(nb));
-        const float bv[4] = {bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
-                             bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+        float bv[4] = {bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
+                       bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16)};
+        if constexpr (SPLIT) bv[0] = bv[1] = bv[2] = bv[3] = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -484,7 +511,29 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mb][nb][i] = macc[mb][nb][i];
     }
-    if constexpr (GATED) {
+    if constexpr (SPLIT) {
+      // promoted sums of K blocks [kb0, kb1) -> part[sp][row][column]: gated
+      // block nb < 2 is gate column n0 + 32wn + 16nb + 4gq.., nb >= 2 the up
+      // column f + n0 + 32wn + 16(nb - 2) + 4gq..; plain n0 + 16 NB wn + 16nb + 4gq..
+      const __amdgpu_buffer_rsrc_t rP =
+          __builtin_amdgcn_make_buffer_rsrc(g.part, (short)0, g.part_bytes, kRsrcWord3);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int gc = GATED ? (nb < 2 ? n0 + 32 * wn + 16 * nb + 4 * gq : g.f + n0 + 32 * wn + 16 * (nb - 2) + 4 * gq)
+                             : n0 + 16 * NB * wn + 16 * nb + 4 * gq;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int r = wm * WR + 16 * mb + l16;
+          const uint32_t o = 4u * (((uint32_t)t.sp * (uint32_t)g.R + (uint32_t)(t.row0 + r)) * (uint32_t)N +
+                                   (uint32_t)gc);
+          const v4u d = v4u{__builtin_bit_cast(uint32_t, acc[mb][nb][0]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][1]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][2]),
+                            __builtin_bit_cast(uint32_t, acc[mb][nb][3])};
+          __builtin_amdgcn_raw_buffer_store_b128(d, rP, (r < t.valid && gc < N) ? (int)o : (int)kOob, 0, 0);
+        }
+      }
+    } else if constexpr (GATED) {
       // h = silu(gate) * up on registers: h column 32wn + 16j + 4gq + i
       float h[MB][2][4];
       float pmax[MB];
@@ -626,14 +675,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
     if constexpr (MX) compute_mx(cur);
     else compute(cur);
     pend = advance();
-    if (++kbc < nkb) return true;
+    if (++kbc < tc.kb1 - tc.kb0) return true;
     epilogue(tc);
     pend += ST;
     if (Lcn >= hi) return false;
     kbc = 0;
     tc = tcn;
     Lcn += nslots;
-    if (Lcn < hi) tcn = dma_tile(g, Lcn);
+    if (Lcn < hi) tcn = dma_vtile<SPLIT>(g, Lcn, nkb);
     return true;
   };
 
@@ -1172,6 +1221,87 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   wait_vmcnt<0>();  // the loads past the last tile land before the workgroup ends
 }
 
+// ---------------------------------------------------------------------------
+// Split-K finish kernels (decode path): the K splits' fp32 partial sums
+// [ksplit][R][N] are added in split order, then the fused epilogue of the
+// unsplit GEMM follows: bias, SwiGLU and h quantisation (gated), or bias (plain).
+
+// Expert of permuted row r: the last e with offsets[e] <= r (offsets[E] = R > r).
+__device__ __forceinline__ int row_expert(const int32_t* __restrict__ offsets, int E, int r) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// One wave per (row, 128 h columns); lane l holds h columns 2l, 2l + 1 of the
+// group.  h = silu(gate) * up with the same arithmetic as the fused epilogue,
+// quantised per 128 columns (fp32 scale) or, with MX, per 32 (E8M0).
+template <bool MX>
+__global__ __launch_bounds__(256) void splitk_gated_finish(GemmArgs g) {
+  const int lane = threadIdx.x & 63;
+  const int groups = g.f / kBlock;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= g.R * groups) return;
+  const int r = item / groups, gi = item - (item / groups) * groups;
+  const int e = row_expert(g.offsets, g.E, r);
+  const int N = 2 * g.f;
+  const int c = gi * kBlock + 2 * lane;
+  float h[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float gs = 0.f, us = 0.f;
+    for (int s = 0; s < g.ksplit; ++s) {
+      const float* p = g.part + ((size_t)s * g.R + r) * N;
+      gs += p[c + i];
+      us += p[g.f + c + i];
+    }
+    const float gv = gs + bf16_to_f32(g.bias[(size_t)e * N + c + i]);
+    const float uv = us + bf16_to_f32(g.bias[(size_t)e * N + g.f + c + i]);
+    const float ex = __builtin_amdgcn_exp2f(-gv * 1.44269504088896341f);
+    h[i] = gv * __builtin_amdgcn_rcpf(1.0f + ex) * uv;
+  }
+  float mx = nan_max(fabsf(h[0]), fabsf(h[1]));
+  uint8_t* hq = g.Hq + (size_t)r * g.f + c;
+  if constexpr (MX) {
+    // a 32-column block is 16 lanes
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) mx = nan_max(mx, __shfl_xor(mx, o));
+    const uint32_t code = mx_code(mx);
+    const float inv = mx_inv_scale(code);
+    *reinterpret_cast<uint16_t*>(hq) = static_cast<uint16_t>(f32x2_to_e4m3(h[0] * inv, h[1] * inv));
+    if ((lane & 15) == 0)
+      static_cast<uint8_t*>(g.Hs)[(size_t)r * (g.f / 32) + 4 * gi + (lane >> 4)] = static_cast<uint8_t>(code);
+  } else {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = nan_max(mx, __shfl_xor(mx, o));
+    const float sc = group_scale(mx);
+    const float inv = 1.0f / sc;
+    *reinterpret_cast<uint16_t*>(hq) =
+        static_cast<uint16_t>(f32x2_to_e4m3(clamp_fp8(h[0] * inv), clamp_fp8(h[1] * inv)));
+    if (lane == 0) static_cast<float*>(g.Hs)[(size_t)r * groups + gi] = sc;
+  }
+}
+
+// Y[r][n..n+3] = sum over splits + bias, one thread per 4 columns.
+__global__ __launch_bounds__(256) void splitk_plain_finish(GemmArgs g) {
+  const int q = g.N / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= g.R * q) return;
+  const int r = idx / q, c = 4 * (idx - (idx / q) * q);
+  const int e = row_expert(g.offsets, g.E, r);
+  v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < g.ksplit; ++s)
+    sum += *reinterpret_cast<const v4f*>(g.part + ((size_t)s * g.R + r) * g.N + c);
+  const uint16_t* b = g.bias + (size_t)e * g.N + c;
+  *reinterpret_cast<v4f*>(g.Y + (size_t)r * g.N + c) =
+      v4f{sum[0] + bf16_to_f32(b[0]), sum[1] + bf16_to_f32(b[1]), sum[2] + bf16_to_f32(b[2]),
+          sum[3] + bf16_to_f32(b[3])};
+}
+
 int grid_for(int max_tiles) { return 8 * ceil_div(max_tiles, 8); }
 
 // Launch facts of a device, looked up once per device and then read without
@@ -1210,12 +1340,13 @@ int grid_persistent(int max_tiles) { return std::min(device_cus(), grid_for(max_
 // and LDS allow, at most two (a second workgroup keeps a second ring of weight
 // loads in flight on the CU), fewer when the tile list cannot fill them.  The
 // occupancy is looked up once per kernel instance and device.
-template <bool GATED, int DBM, int DBN, bool MX, bool FP4>
+template <bool GATED, int DBM, int DBN, bool MX, bool FP4, bool SPLIT>
 dim3 grid_decode(int max_tiles) {
   auto lookup = [] {
     int n = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4>,
-                                                     DMA_WAVES * 64, 0) != hipSuccess || n < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4, SPLIT>, DMA_WAVES * 64, 0) != hipSuccess ||
+        n < 1)
       n = 1;
     return std::min(n, 2);
   };
@@ -1232,28 +1363,40 @@ dim3 grid_decode(int max_tiles) {
   return dim3(std::min(per * device_cus(), grid_for(max_tiles)));
 }
 
+template <bool GATED, int DBM, int DBN, bool MX, bool FP4>
+hipError_t launch_decode(const GemmArgs& a, int max_tiles, hipStream_t stream) {
+  const dim3 block(DMA_WAVES * 64);
+  if (a.ksplit <= 1) {
+    hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4, false>),
+                       (grid_decode<GATED, DBM, DBN, MX, FP4, false>(max_tiles)), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const int items = max_tiles * a.ksplit;
+  hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, MX, FP4, true>),
+                     (grid_decode<GATED, DBM, DBN, MX, FP4, true>(items)), block, 0, stream, a);
+  if (GATED)
+    hipLaunchKernelGGL((splitk_gated_finish<MX>), dim3(ceil_div(a.R * (a.f / kBlock), 4)), dim3(256), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL(splitk_plain_finish, dim3(ceil_div(a.R * (a.N / 4), 256)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <bool GATED, int DBM, int DBN>
 hipError_t launch_gemm(const GemmArgs& a, bool decode, int fmt, int max_tiles, hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   const dim3 grid(grid_persistent(max_tiles)), block(DMA_WAVES * 64);
   if (decode) {
-    if (fmt == kFmtMxFp4)
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, true>),
-                         (grid_decode<GATED, DBM, DBN, true, true>(max_tiles)), block, 0, stream, a);
-    else if (fmt == kFmtMx)
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, true, false>),
-                         (grid_decode<GATED, DBM, DBN, true, false>(max_tiles)), block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((grouped_gemm_dma_kernel<GATED, DBM, DBN, false, false>),
-                         (grid_decode<GATED, DBM, DBN, false, false>(max_tiles)), block, 0, stream, a);
-  } else {
-    if (fmt == kFmtMxFp4)
-      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, true>), grid, block, 0, stream, a);
-    else if (fmt == kFmtMx)
-      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, false>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, false, false>), grid, block, 0, stream, a);
+    if (fmt == kFmtMxFp4) return launch_decode<GATED, DBM, DBN, true, true>(a, max_tiles, stream);
+    if (fmt == kFmtMx) return launch_decode<GATED, DBM, DBN, true, false>(a, max_tiles, stream);
+    return launch_decode<GATED, DBM, DBN, false, false>(a, max_tiles, stream);
   }
+  if (fmt == kFmtMxFp4)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, true>), grid, block, 0, stream, a);
+  else if (fmt == kFmtMx)
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, true, false>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_wide_kernel<GATED, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

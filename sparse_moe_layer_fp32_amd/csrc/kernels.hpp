@@ -44,7 +44,32 @@ struct GemmArgs {
   uint8_t* Hq;                 // gated outputs: h codes [R, f] and their scales
   void* Hs;
   float* Y;                    // plain output [R, N]
+  // split K (decode path only; ksplit = 1 otherwise): K blocks per split,
+  // the routed rows R, and the fp32 partial sums [ksplit][R][N] in the workspace
+  int ksplit, kper, R;
+  float* part;
+  int part_bytes;
 };
+
+// K splits of a decode-path GEMM with at most max_tiles tiles of nkb K
+// blocks: with fewer tiles than the chip has workgroup slots (two per CU of
+// the 256-CU part), each tile is cut into K ranges of at least 4 blocks so
+// that about 512 (tile, split) items run, and every range keeps at least two
+// blocks.  Host-only arithmetic on the sizes, so the workspace can be sized
+// without a device query.
+inline int decode_ksplits(int max_tiles, int nkb) {
+  if (max_tiles <= 0 || max_tiles >= 256) return 1;
+  int s = 512 / max_tiles;
+  if (s > nkb / 4) s = nkb / 4;
+  if (s > 8) s = 8;
+  while (s > 1) {
+    const int kper = (nkb + s - 1) / s;
+    if (nkb - (s - 1) * kper >= 2) break;
+    --s;
+  }
+  return s < 1 ? 1 : s;
+}
+inline int decode_kper(int nkb, int ksplit) { return (nkb + ksplit - 1) / ksplit; }
 
 // K splits of the router for T tokens (1: top-k fused into the router kernel;
 // >1: partial logits [splits][T][E] fp32 in `partial`, then a top-k kernel).

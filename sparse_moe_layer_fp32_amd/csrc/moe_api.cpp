@@ -2,6 +2,7 @@
 // launch sequence on the caller's stream.  No allocation, no host sync.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -18,8 +19,23 @@ constexpr int64_t kMaxBuffer = int64_t(1) << 31;
 
 struct Layout {
   size_t partial, topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, tiles0,
-      tiles1, row_of, row_token, xq, xs, hq, hs, y, total;
+      tiles1, row_of, row_token, xq, xs, hq, hs, y, kpart, total;
 };
+
+// Decode-path GEMM shapes for T*k = R rows: tile-count bounds and K splits
+// (the same numbers the launch uses, so the workspace holds the partials).
+struct DecodeSplit {
+  int max_g, max_p, sg, sp;
+};
+DecodeSplit decode_split(int64_t R, int64_t d, int64_t f, int64_t E) {
+  const int nz = (int)(E < R ? E : R);
+  DecodeSplit s{};
+  s.max_g = (ceil_div((int)R, moe::kGatedDecode.bm) + nz) * (int)(f / moe::kBlock);
+  s.max_p = (ceil_div((int)R, moe::kPlainDecode.bm) + nz) * ceil_div((int)d, moe::kPlainDecode.bnp);
+  s.sg = moe::decode_ksplits(s.max_g, (int)(d / moe::kBlock));
+  s.sp = moe::decode_ksplits(s.max_p, (int)(f / moe::kBlock));
+  return s;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -53,6 +69,10 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
   l.hq = put(R * f);
   l.hs = put(4 * R * (f / moe::kBlock));
   l.y = put(4 * R * d);
+  // split-K partial sums of the decode-path GEMMs [splits][R][N], fp32
+  const DecodeSplit ds = decode_split(R, d, f, E);
+  const int64_t kp = ds.sg > 1 || ds.sp > 1 ? std::max<int64_t>(ds.sg * 2 * f, ds.sp * d) : 0;
+  l.kpart = put(4 * R * kp);
   l.total = o;
   return l;
 }
@@ -177,6 +197,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   uint8_t* hq = at(l.hq);
   void* hs = at(l.hs);
   float* y = reinterpret_cast<float*>(at(l.y));
+  float* kpart = reinterpret_cast<float*>(at(l.kpart));
 
   const int R = T * k;
   const int NT = ceil_div(T, moe::RT_TT);
@@ -190,6 +211,9 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   const int nz = E < R ? E : R;  // experts that can hold rows
   const int max_g = (ceil_div(R, gs.bm) + nz) * nt_g;
   const int max_p = (ceil_div(R, ps.bm) + nz) * nt_p;
+  // split K for decode batches with few tiles (prefill tiles are never split)
+  const DecodeSplit dsp = decode_split(R, d, f, E);
+  const int ks_g = decode ? dsp.sg : 1, ks_p = decode ? dsp.sp : 1;
   const bool small = NT == 1;  // the whole routing runs in the router stage
 
   for (int stage = first_stage; stage <= last_stage; ++stage) {
@@ -238,6 +262,11 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.Hs = hs;
         g.A_bytes = (int)((int64_t)T * d);
         g.As_bytes = (int)(4 * (int64_t)T * (d / moe::kBlock));
+        g.ksplit = ks_g;
+        g.kper = moe::decode_kper(d / moe::kBlock, ks_g);
+        g.R = R;
+        g.part = kpart;
+        g.part_bytes = (int)(4 * (int64_t)ks_g * R * 2 * f);
         err = moe::launch_gemm_gated(g, decode, fmt, max_g, stream);
         break;
       }
@@ -262,6 +291,11 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.Y = y;
         p.A_bytes = (int)((int64_t)R * f);
         p.As_bytes = (int)(4 * (int64_t)R * (f / moe::kBlock));
+        p.ksplit = ks_p;
+        p.kper = moe::decode_kper(f / moe::kBlock, ks_p);
+        p.R = R;
+        p.part = kpart;
+        p.part_bytes = (int)(4 * (int64_t)ks_p * R * d);
         err = moe::launch_gemm_plain(p, decode, fmt, max_p, stream);
         break;
       }

@@ -94,6 +94,63 @@ def test_small_shapes_vs_oracle(shape, path, fmt):
          f"down-stage err/bound {worst:.3f}")
 
 
+# Decode batches with fewer GEMM tiles than the chip's workgroup slots: both
+# decode GEMMs cut every tile into K ranges (split K), write fp32 partial sums
+# and a finish kernel adds them in split order before the epilogue.
+# (T, d, d_real, f, E, k) and the (gate/up, down) split counts they get.
+SPLITK = [
+    (1, 1024, 1024, 1024, 8, 2),        # splits 2, 2
+    (3, 2048, 2000, 1024, 16, 4),       # splits 4, 2; padded hidden size
+    (5, 1536, 1536, 1536, 64, 4),       # splits 2, 2
+]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", SPLITK, ids=[f"T{s[0]}-d{s[1]}-f{s[3]}-E{s[4]}-k{s[5]}" for s in SPLITK])
+def test_split_k_decode_vs_oracle(shape, fmt):
+    T, d, dr, f, E, k = shape
+    layer = gen.custom_layer(d, f, E, k, d_real=dr, layer_id=6000 + d + f + E + k)
+    inp = gen.make_inputs(layer, T=T, fmt=fmt)
+    _say(f"[splitk] shape={shape} fmt={fmt}")
+    dbg = run_debug(inp, "decode")
+    ref = parity.oracle_ref(inp)
+    parity.check_routing(dbg, ref, T, k)
+    parity.check_xquant(dbg, ref["xq"], ref["xs"])
+    nflip, ncodes = parity.check_h_decisions(dbg, ref, fmt)
+    worst = parity.check_down_stage(dbg, ref, inp, dr)
+    parity.check_combine_stage(dbg)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, dr)
+    assert np.all(g[:, dr:] == 0)
+    _say(f"   out {m}\n   h flips {nflip}/{ncodes}; down-stage err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("cfg,T", [("c1", 1), ("c1", 2), ("c4a", 1)])
+def test_split_k_full_layers(cfg, T, fmt):
+    """The gpt-oss-20b-like and the 128-expert layers at one and two tokens
+    (split K on both GEMMs), every token against the oracle, and repeat calls
+    bit-identical."""
+    inp = gen.make_inputs(cfg, T=T, fmt=fmt)
+    _say(f"[splitk] {cfg} T={T} fmt={fmt}")
+    dbg = run_debug(inp, "auto")
+    ref = parity.oracle_ref(inp)
+    dr = inp["d_real"]
+    parity.check_routing(dbg, ref, T, inp["k"])
+    parity.check_xquant(dbg, ref["xq"], ref["xs"])
+    parity.check_h_decisions(dbg, ref, fmt)
+    parity.check_down_stage(dbg, ref, inp, dr)
+    parity.check_combine_stage(dbg)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, dr)
+    assert np.all(g[:, dr:] == 0)
+    again = parity.bf16_to_f64(run_debug(inp, "auto")["out"])
+    np.testing.assert_array_equal(again, g)
+    _say(f"   out {m}")
+    parity.record(dict(cfg=f"{cfg} T={T}", fmt=fmt, tokens=int(T),
+                       **{k: v for k, v in m.items() if k != "adjusted"}, adjusted=m.get("adjusted")))
+
+
 GATE_SHAPES = [
     # (T, d, d_real, f, E, k): one-workgroup routing with split partials, with the
     # router's in-place top-k (one 128-column group), the per-token finisher,
