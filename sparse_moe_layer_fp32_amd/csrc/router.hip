@@ -326,12 +326,45 @@ __global__ __launch_bounds__(256) void router_kernel(
         if (t < T) partial[((size_t)blockIdx.y * T + t) * EP + e] = tot[nb][i];
       }
     }
+    // the finish kernel adds its token blocks' picks into the tile histogram
+    if (blockIdx.y == 0)
+      for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = 0;
     return;
   }
   __syncthreads();  // shist cleared
   topk_emit<NBW>(tot, br, t0, T, E, k, gate_mode, topk_idx, topk_w, shist);
   __syncthreads();
   for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
+}
+
+// Lane exchanges inside the aligned group of eight lanes (half a DPP row):
+// swap neighbours, swap pairs, then mirror the half row, so after the three
+// steps every lane of the group has combined all eight values.  DPP moves
+// read the other lane's register directly (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of a half row reads lane 7 - i
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t max_step(uint64_t v) {
+  const uint64_t o = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint64_t max8(uint64_t v) {
+  return max_step<kDppHalfMirror>(max_step<kDppSwap2>(max_step<kDppSwap1>(v)));
+}
+// Sum over the group; the same value in all eight lanes (each step adds a
+// pair of values that the partner lane adds in the other order).
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float v) {
+  return v + __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+__device__ __forceinline__ float sum8(float v) {
+  return sum_step<kDppHalfMirror>(sum_step<kDppSwap2>(sum_step<kDppSwap1>(v)));
 }
 
 // Top-k + softmax of the RT_TT tokens tt0.. of a router tile with eight lanes
@@ -341,13 +374,13 @@ __global__ __launch_bounds__(256) void router_kernel(
 // Lane j of a token's group holds the 64-bit keys of experts j, j + 8, ...
 // (ordered logit bits, then the complemented expert index, so ties go to the
 // lower index and every pick is a valid, distinct expert); each of the k
-// rounds takes the group maximum with three lane exchanges and clears the
-// winner.  Lane s < k of the group writes pick s and its weight (softmax over
+// rounds takes the group maximum with three register exchanges (max8) and
+// clears the winner.  Lane s < k of the group writes pick s and its weight (softmax over
 // the selected logits, or over all E for kGateSoftmaxAll), counts it in the
 // tile histogram and, when given, records it in spick and the token's bit in
 // the expert's token mask.
 template <int EP>
-__device__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, int E, int k,
+__device__ __forceinline__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, int E, int k,
                             int gate_mode, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                             int* shist, int* spick, uint32_t* smask_lo, uint32_t* smask_hi) {
   constexpr int KPL = EP / 8;  // keys per lane
@@ -369,13 +402,7 @@ __device__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, i
       uint64_t best = key[0];
 #pragma unroll
       for (int j = 1; j < KPL; ++j) best = key[j] > best ? key[j] : best;
-#pragma unroll
-      for (int o = 4; o > 0; o >>= 1) {
-        const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), o);
-        const uint32_t lo = __shfl_xor((uint32_t)best, o);
-        const uint64_t other = ((uint64_t)hi << 32) | lo;
-        best = other > best ? other : best;
-      }
+      best = max8(best);
       sel[s] = best;
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
@@ -394,9 +421,7 @@ __device__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, i
   if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits (lane sums, then an xor tree)
     float part = 0.f;
     for (int e = sub; e < E; e += 8) part += expf(row[e] + sbr[e] - l0);
-#pragma unroll
-    for (int o = 4; o > 0; o >>= 1) part += __shfl_xor(part, o);
-    sum = part;
+    sum = sum8(part);
   }
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) {
@@ -411,29 +436,32 @@ __device__ void topk_group8(const float* sl, const float* sbr, int tt0, int T, i
   }
 }
 
-// Logits of the tile's RT_TT tokens into sl [RT_TT][EP + 8] (the pitch of
-// topk_group8): the sum of every
-// (token, expert) partial in split order.  A thread takes 4 experts of one
-// token (one float4 per split, up to 16 splits in flight per round).
+// Logits of ntok (<= RT_TT) tokens from tt0 into sl [RT_TT][EP + 8] (the
+// pitch of topk_group8): the sum of every (token, expert) partial in split
+// order.  A
+// thread takes 4 experts of one token (one float4 per split); up to 24 splits
+// are in flight at once, so a K range of up to 24 splits costs one memory
+// round trip.
 template <int EP>
 __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int T, int tt0,
-                             float* sl, int nthreads) {
+                             float* sl, int nthreads, int ntok = RT_TT) {
   constexpr int Q = EP / 4;
+  constexpr int kInFlight = 24;
   const size_t stride = (size_t)T * EP;
-  for (int q = threadIdx.x; q < RT_TT * Q; q += nthreads) {
+  for (int q = threadIdx.x; q < ntok * Q; q += nthreads) {
     const int tl = q / Q, e4 = 4 * (q % Q);
     const int t = tt0 + tl;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (t < T) {
       const float* p = partial + (size_t)t * EP + e4;
-      for (int s0 = 0; s0 < nsplit; s0 += 16) {
-        float4 v[16];
+      for (int s0 = 0; s0 < nsplit; s0 += kInFlight) {
+        float4 v[kInFlight];
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < kInFlight; ++j)
           v[j] = s0 + j < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + j) * stride)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
+        for (int j = 0; j < kInFlight; ++j)
           if (s0 + j < nsplit) {
             s.x += v[j].x;
             s.y += v[j].y;
@@ -450,9 +478,13 @@ __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int 
   }
 }
 
-// Split-K finish: the logit of every (token, expert) of the tile is the sum of
-// its partials in split order; every thread loads all splits of its pairs at
-// once.  Then top-k + softmax + tile histogram with the router's layout.
+// Split-K finish for a block of kFinishTok tokens (a quarter of a router
+// tile, so that the partial reads of a tile spread over four CUs): the logit
+// of every (token, expert) is the sum of its partials in split order; then
+// top-k + softmax, and the block's picks are added to its router tile's
+// histogram (integer atomics: the counts do not depend on the order; the
+// router kernel zeroed the row).
+constexpr int kFinishTok = RT_TT / 4;
 template <int NBW>
 __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restrict__ partial,
                                                              int nsplit, const float* __restrict__ br,
@@ -465,16 +497,31 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
   __shared__ int shist[kMaxExperts];
   __shared__ float sbr[kMaxExperts];
   const int tid = threadIdx.x;
-  const int tt0 = blockIdx.x * RT_TT;
-  for (int i = tid; i < E; i += 512) {
-    shist[i] = 0;
-    sbr[i] = br[i];
-  }
-  sum_partials<EP>(partial, nsplit, T, tt0, sl, 512);
+  const int tt0 = blockIdx.x * kFinishTok;
+  const int tend = min(T, tt0 + kFinishTok);
+  const float brv = tid < E ? br[tid] : 0.f;
+  if (tid < E) shist[tid] = 0;
+  sum_partials<EP>(partial, nsplit, T, tt0, sl, 512, kFinishTok);
+  if (tid < E) sbr[tid] = brv;
   __syncthreads();  // the sums are in LDS, shist and sbr are set
-  topk_group8<EP>(sl, sbr, tt0, T, E, k, gate_mode, topk_idx, topk_w, shist, nullptr, nullptr, nullptr);
+  topk_group8<EP>(sl, sbr, tt0, tend, E, k, gate_mode, topk_idx, topk_w, shist, nullptr, nullptr,
+                  nullptr);
   __syncthreads();  // the histogram atomics are done
-  for (int e = tid; e < E; e += 512) hist[(size_t)blockIdx.x * E + e] = shist[e];
+  if (tid < E && shist[tid] != 0) atomicAdd(&hist[(size_t)(tt0 / RT_TT) * E + tid], shist[tid]);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: DPP row shifts scan each
+// 16-lane row, then the row totals (lanes 15, 31, 47) are added to the rows
+// above them.  Integer adds, so the order does not matter.
+__device__ __forceinline__ int scan64(int v) {
+  v += (int)__builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr 1
+  v += (int)__builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr 2
+  v += (int)__builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr 4
+  v += (int)__builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr 8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // All routing of a batch that fits one router tile (T <= RT_TT, the decode
@@ -500,16 +547,20 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   const int tid = threadIdx.x;
   const int R = T * k;
   __shared__ float sbr[kMaxExperts];
-  for (int i = tid; i < E; i += 512) {
-    scnt[i] = 0;
-    smask[0][i] = smask[1][i] = 0u;
-    sbr[i] = br[i];
+  static_assert(kMaxExperts <= 512, "one bias per thread");
+  // the bias load is issued before the partial loads, so both share one
+  // round trip to memory
+  const float brv = tid < E ? br[tid] : 0.f;
+  if (tid < E) {
+    scnt[tid] = 0;
+    smask[0][tid] = smask[1][tid] = 0u;
   }
   if (!have_topk) {
     sum_partials<EP>(partial, nsplit, T, 0, sl, 512);
   } else {
     for (int p = tid; p < R; p += 512) spick[p] = topk_idx[p];
   }
+  if (tid < E) sbr[tid] = brv;
   __syncthreads();
   if (!have_topk) {
     topk_group8<EP>(sl, sbr, 0, T, E, k, gate_mode, topk_idx, topk_w, scnt, spick, smask[0], smask[1]);
@@ -534,16 +585,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
       r0 += t0v[q];
       r1 += t1v[q];
     }
-    int ic = rc, i0 = r0, i1 = r1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int yc = __shfl_up(ic, o), y0 = __shfl_up(i0, o), y1 = __shfl_up(i1, o);
-      if (tid >= o) {
-        ic += yc;
-        i0 += y0;
-        i1 += y1;
-      }
-    }
+    const int ic = scan64(rc), i0 = scan64(r0), i1 = scan64(r1);
     int pc = ic - rc, p0 = i0 - r0, p1 = i1 - r1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -581,31 +623,31 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     row_of[p] = row;
     row_token[row] = t;
   }
-  // tile lists (expert by binary search of the tile offsets; inside the expert:
-  // column group of kTileGroup tiles, row block, column tile)
+  // tile lists: wave w writes the tiles of experts w, w + 8, ...; lane j takes
+  // the expert's tiles j, j + 64, ... (inside the expert: column group of
+  // kTileGroup tiles, row block, column tile)
+  const int wave = tid >> 6, lane = tid & 63;
   for (int pass = 0; pass < 2; ++pass) {
     const int* so = pass == 0 ? so0 : so1;
     const int bm = pass == 0 ? bm0 : bm1, n_tiles = pass == 0 ? nt0 : nt1;
+    const int max_tiles = pass == 0 ? max0 : max1;
     int4* tiles = pass == 0 ? tiles0 : tiles1;
-    const int total = min(so[E], pass == 0 ? max0 : max1);
-    for (int L = tid; L < total; L += 512) {
-      int lo = 0, hi = E;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (so[mid] <= L) lo = mid; else hi = mid;
-      }
-      const int cnt = scnt[lo];
-      const int local = L - so[lo];
-      if (cnt <= bm) {  // one row block: the entries are the column tiles in order
-        tiles[L] = make_int4(lo, soff[lo], cnt, local);
-        continue;
-      }
+    for (int e = wave; e < E; e += 8) {
+      const int cnt = scnt[e], first = so[e], row0 = soff[e];
+      const int n = min(so[e + 1], max_tiles) - first;
       const int mt = ceil_div(cnt, bm);
-      const int ng = local / (mt * kTileGroup);
-      const int rem = local - ng * mt * kTileGroup;
-      const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
-      const int m = rem / gw;
-      tiles[L] = make_int4(lo, soff[lo] + m * bm, min(bm, cnt - m * bm), ng * kTileGroup + rem % gw);
+      for (int local = lane; local < n; local += 64) {
+        if (cnt <= bm) {  // one row block: the entries are the column tiles in order
+          tiles[first + local] = make_int4(e, row0, cnt, local);
+          continue;
+        }
+        const int ng = local / (mt * kTileGroup);
+        const int rem = local - ng * mt * kTileGroup;
+        const int gw = min(kTileGroup, n_tiles - ng * kTileGroup);
+        const int m = rem / gw;
+        tiles[first + local] =
+            make_int4(e, row0 + m * bm, min(bm, cnt - m * bm), ng * kTileGroup + rem % gw);
+      }
     }
   }
 }
@@ -628,7 +670,7 @@ hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br
                        reinterpret_cast<int4*>(sr->tiles1), sr->bm0, sr->nt0, sr->max0, sr->bm1,
                        sr->nt1, sr->max1, sr->row_of, sr->row_token);
   else if (ns > 1)
-    hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(tiles), dim3(512), 0, stream, partial, ns,
+    hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(ceil_div(T, kFinishTok)), dim3(512), 0, stream, partial, ns,
                        br, T, E, k, gate_mode, topk_idx, topk_w, hist);
   return hipGetLastError();
 }
