@@ -425,6 +425,36 @@ def peaks_bench(args):
         cyc = ltim.view(-1, 2)[:, 0].double().max().item()
         per_cu = 8 * iters * 8 * 64 * lane_bytes
         res[f"lds_{name}_bytes_per_clk_per_cu"] = round(per_cu / cyc, 1)
+    # global -> LDS fill rate per CU: the GEMMs' DMA stage loads vs loads to
+    # registers + LDS writes, from an L2-resident region and from HBM-sized ones
+    L.peak_lds_fill.argtypes = [P, I, I, I, I, I, P, P, P]
+    for region, name in ((256 << 10, "l2"), (8 << 20, "hbm")):
+        fsrc = torch.ones(cus * region, dtype=torch.uint8, device=dev)
+        fsink = torch.empty(cus * 8, dtype=torch.int32, device=dev)
+        ftim = torch.empty(cus * 16, dtype=torch.int64, device=dev)
+        iters = 256 if name == "l2" else 128
+        for dma in (1, 0):
+            log(f"[peaks] LDS fill {name} dma={dma}")
+            fn = lambda: L.peak_lds_fill(P(fsrc.data_ptr()), cus, 8, region, iters, dma, P(fsink.data_ptr()),
+                                         P(ftim.data_ptr()), stream)
+            ms = timed(fn, 5)
+            cyc = ftim.view(-1, 2)[:, 0].double().max().item()
+            per_cu = 8 * iters * 8 * 1024
+            res[f"lds_fill_{name}_{'dma' if dma else 'regs'}_bytes_per_clk_per_cu"] = round(per_cu / cyc, 1)
+            res[f"lds_fill_{name}_{'dma' if dma else 'regs'}_GBs"] = round(cus * per_cu / (min(ms) * 1e-3) / 1e9, 1)
+        del fsrc
+    # the grouped GEMMs' MFMA sequence alone (fragments in registers)
+    L.peak_mfma_sequence.argtypes = [I, I, I, I, P, P, P]
+    for waves, mode, name in ((8, 0, "promote3_schedbarrier"), (8, 1, "promote3"), (8, 2, "accumulate"),
+                              (4, 0, "promote3_schedbarrier_1wave"), (4, 2, "accumulate_1wave")):
+        steps = 2000
+        seq_sink = torch.empty(cus * waves, dtype=torch.float32, device=dev)
+        seq_tim = torch.empty(cus * waves * 2, dtype=torch.int64, device=dev)
+        log(f"[peaks] MFMA sequence {name}")
+        fn = lambda: L.peak_mfma_sequence(cus, waves, steps, mode, P(seq_sink.data_ptr()), P(seq_tim.data_ptr()), stream)
+        ms = timed(fn, 5)
+        flops = cus * waves * steps * 24 * 2.0 * 16 * 16 * 128
+        res[f"mfma_seq_{name}_tflops"] = round(flops / (min(ms) * 1e-3) / 1e12, 1)
     torch.cuda.synchronize()
     print(json.dumps(res), flush=True)
 
@@ -448,6 +478,10 @@ def main():
                     help="record the per-kernel timing events on every N-th timed step only (each "
                          "event costs a few microseconds of device time; the other steps run the "
                          "plain call)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph holding one forward (captured after the warm-up, "
+                         "as a serving loop replays it) instead of eager calls; the per-kernel times "
+                         "then come from an eager pass before the timed region")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="read this many MiB between timed calls (outside the calls' events) so "
                          "that every call reads its weights from HBM; 0: back-to-back steps")
@@ -516,6 +550,24 @@ def main():
     torch.cuda.synchronize()
     sampled = sampled_steps(args.steps, args.event_every)
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    graph = None
+    if args.graph:
+        # per-kernel times from eager steps, then one forward captured for the timed replays
+        for i in sampled:
+            step(evs[i])
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
     calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)] if flush is not None else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -524,13 +576,14 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
+        run = graph.replay if graph is not None else (lambda: step(evs.get(i)))
         if flush is not None:
             flush_sink.copy_(flush.sum())   # untimed read: evicts L2 and the memory-side cache
             calls[i][0].record()
-            step(evs.get(i))
+            run()
             calls[i][1].record()
         else:
-            step(evs.get(i))
+            run()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
@@ -585,6 +638,7 @@ def main():
         "layer_frac": layer["frac"],
         "layer_roofline": layer,
         "flush_mib": args.flush_mib,
+        "graph": bool(args.graph),
         "timed_region_ms": round(total_ms, 3),
         "stages_ms": {"gateup": round(gate_ms, 5), "down": round(down_ms, 5),
                       "rest": round(ms - gate_ms - down_ms, 5)},
