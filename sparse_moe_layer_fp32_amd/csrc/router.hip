@@ -389,50 +389,45 @@ __device__ __forceinline__ void topk_group8(const float* sl, const float* sbr, i
   const float* row = sl + tl * (EP + 8);
   uint64_t key[KPL];
 #pragma unroll
-  for (int j = 0; j < KPL; ++j) {
+  for (int j = 0; j < KPL; ++j) {  // reads stay inside sl and sbr for every lane: no branch
     const int e = 8 * j + sub;
-    key[j] = (t < T && e < E) ? ((uint64_t)ordered_key(row[e] + sbr[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)
-                              : 0ull;
+    const uint64_t kv = ((uint64_t)ordered_key(row[e] + sbr[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+    key[j] = (t < T && e < E) ? kv : 0ull;
   }
-  uint64_t sel[kMaxTopK];
+  // round s: the group maximum (the same in all eight lanes) is pick s; lane
+  // s of the group keeps it, so each lane < k then finishes one pick
+  uint64_t first = 0ull, mine = 0ull;
 #pragma unroll
   for (int s = 0; s < kMaxTopK; ++s) {
-    sel[s] = 0ull;
     if (s < k) {
       uint64_t best = key[0];
 #pragma unroll
       for (int j = 1; j < KPL; ++j) best = key[j] > best ? key[j] : best;
       best = max8(best);
-      sel[s] = best;
+      if (s == 0) first = best;
+      if (sub == s) mine = best;
 #pragma unroll
       for (int j = 0; j < KPL; ++j)
         if (key[j] == best) key[j] = 0ull;
     }
   }
   if (t >= T) return;
-  const float l0 = key_value((uint32_t)(sel[0] >> 32));
-  float ex[kMaxTopK];
-  float sum = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    ex[s] = s < k ? expf(key_value((uint32_t)(sel[s] >> 32)) - l0) : 0.f;
-    sum += ex[s];
-  }
-  if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits (lane sums, then an xor tree)
+  const float l0 = key_value((uint32_t)(first >> 32));
+  const bool owner = sub < k;
+  const float ex = owner ? expf(key_value((uint32_t)(mine >> 32)) - l0) : 0.f;
+  float sum = sum8(ex);  // sum of the k selected exponentials (0 from lanes >= k)
+  if (gate_mode & kGateSoftmaxAll) {  // normaliser over all E logits (lane sums, then the group sum)
     float part = 0.f;
     for (int e = sub; e < E; e += 8) part += expf(row[e] + sbr[e] - l0);
     sum = sum8(part);
   }
-#pragma unroll
-  for (int s = 0; s < kMaxTopK; ++s) {
-    if (s < k && sub == s) {
-      const int e = (int)(0xffffffffu - (uint32_t)sel[s]);
-      topk_idx[(size_t)t * k + s] = e;
-      topk_w[(size_t)t * k + s] = gate_weight(ex[s], sum, gate_mode);
-      atomicAdd(&shist[e], 1);
-      if (spick) spick[tl * k + s] = e;
-      if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
-    }
+  if (owner) {
+    const int e = (int)(0xffffffffu - (uint32_t)mine);
+    topk_idx[(size_t)t * k + sub] = e;
+    topk_w[(size_t)t * k + sub] = gate_weight(ex, sum, gate_mode);
+    atomicAdd(&shist[e], 1);
+    if (spick) spick[tl * k + sub] = e;
+    if (smask_lo) atomicOr(tl < 32 ? &smask_lo[e] : &smask_hi[e], 1u << (tl & 31));
   }
 }
 
@@ -460,14 +455,17 @@ __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int 
         for (int j = 0; j < kInFlight; ++j)
           v[j] = s0 + j < nsplit ? *reinterpret_cast<const float4*>(p + (s0 + j) * stride)
                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+        // selects rather than a skipped add: every loaded register is consumed
+        // on every path, so no load stays in flight past this loop (on this
+        // chip a wait for loads also waits for the stores issued before it)
 #pragma unroll
-        for (int j = 0; j < kInFlight; ++j)
-          if (s0 + j < nsplit) {
-            s.x += v[j].x;
-            s.y += v[j].y;
-            s.z += v[j].z;
-            s.w += v[j].w;
-          }
+        for (int j = 0; j < kInFlight; ++j) {
+          const bool in = s0 + j < nsplit;
+          s.x = in ? s.x + v[j].x : s.x;
+          s.y = in ? s.y + v[j].y : s.y;
+          s.z = in ? s.z + v[j].z : s.z;
+          s.w = in ? s.w + v[j].w : s.w;
+        }
       }
     }
     float* dst = sl + tl * (EP + 8) + e4;
@@ -495,14 +493,14 @@ __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restr
   constexpr int EP = NBW * 16;
   __shared__ float sl[RT_TT * (EP + 8)];
   __shared__ int shist[kMaxExperts];
-  __shared__ float sbr[kMaxExperts];
+  __shared__ float sbr[512];  // entries >= E are written but never read
   const int tid = threadIdx.x;
   const int tt0 = blockIdx.x * kFinishTok;
   const int tend = min(T, tt0 + kFinishTok);
   const float brv = tid < E ? br[tid] : 0.f;
   if (tid < E) shist[tid] = 0;
   sum_partials<EP>(partial, nsplit, T, tt0, sl, 512, kFinishTok);
-  if (tid < E) sbr[tid] = brv;
+  sbr[tid] = brv;
   __syncthreads();  // the sums are in LDS, shist and sbr are set
   topk_group8<EP>(sl, sbr, tt0, tend, E, k, gate_mode, topk_idx, topk_w, shist, nullptr, nullptr,
                   nullptr);
@@ -546,10 +544,11 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   __shared__ uint32_t smask[2][kMaxExperts];  // tokens (bits) that chose each expert
   const int tid = threadIdx.x;
   const int R = T * k;
-  __shared__ float sbr[kMaxExperts];
+  __shared__ float sbr[512];  // entries >= E are written but never read
   static_assert(kMaxExperts <= 512, "one bias per thread");
   // the bias load is issued before the partial loads, so both share one
-  // round trip to memory
+  // round trip to memory; every thread stores its value (0 past E), so the
+  // load is consumed on every path and no later wait has to cover it
   const float brv = tid < E ? br[tid] : 0.f;
   if (tid < E) {
     scnt[tid] = 0;
@@ -560,7 +559,7 @@ __global__ __launch_bounds__(512) void route_small_kernel(
   } else {
     for (int p = tid; p < R; p += 512) spick[p] = topk_idx[p];
   }
-  if (tid < E) sbr[tid] = brv;
+  sbr[tid] = brv;
   __syncthreads();
   if (!have_topk) {
     topk_group8<EP>(sl, sbr, 0, T, E, k, gate_mode, topk_idx, topk_w, scnt, spick, smask[0], smask[1]);
@@ -623,20 +622,24 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     row_of[p] = row;
     row_token[row] = t;
   }
-  // tile lists: wave w writes the tiles of experts w, w + 8, ...; lane j takes
-  // the expert's tiles j, j + 64, ... (inside the expert: column group of
-  // kTileGroup tiles, row block, column tile)
-  const int wave = tid >> 6, lane = tid & 63;
-  for (int pass = 0; pass < 2; ++pass) {
-    const int* so = pass == 0 ? so0 : so1;
-    const int bm = pass == 0 ? bm0 : bm1, n_tiles = pass == 0 ? nt0 : nt1;
-    const int max_tiles = pass == 0 ? max0 : max1;
-    int4* tiles = pass == 0 ? tiles0 : tiles1;
-    for (int e = wave; e < E; e += 8) {
-      const int cnt = scnt[e], first = so[e], row0 = soff[e];
+  // tile lists: tpe threads per expert, thread j of an expert's team writes
+  // the expert's tiles j, j + tpe, ... (inside the expert: column group of
+  // kTileGroup tiles, row block, column tile); all experts at once, so the
+  // LDS reads of every expert share one round trip
+  const int tpe = E < 512 ? 512 / E : 1;
+  const int e = tid / tpe, j0 = tid - e * tpe;
+  if (e < E) {
+    const int cnt = scnt[e], row0 = soff[e];
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int* so = pass == 0 ? so0 : so1;
+      const int bm = pass == 0 ? bm0 : bm1, n_tiles = pass == 0 ? nt0 : nt1;
+      const int max_tiles = pass == 0 ? max0 : max1;
+      int4* tiles = pass == 0 ? tiles0 : tiles1;
+      const int first = so[e];
       const int n = min(so[e + 1], max_tiles) - first;
       const int mt = ceil_div(cnt, bm);
-      for (int local = lane; local < n; local += 64) {
+      for (int local = j0; local < n; local += tpe) {
         if (cnt <= bm) {  // one row block: the entries are the column tiles in order
           tiles[first + local] = make_int4(e, row0, cnt, local);
           continue;
