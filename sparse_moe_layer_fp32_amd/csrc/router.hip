@@ -571,38 +571,30 @@ __global__ __launch_bounds__(512) void route_small_kernel(
     }
   }
   __syncthreads();
-  // exclusive scans of the counts and of both GEMMs' tiles per expert (wave 0)
-  if (tid < 64) {
-    int c[4], t0v[4], t1v[4], rc = 0, r0 = 0, r1 = 0;
+  // exclusive scans, one per wave: wave 0 the counts (row offsets), waves 1
+  // and 2 the two GEMMs' tiles per expert (tile offsets); lane l takes
+  // experts 4l .. 4l + 3
+  if (tid < 192) {
+    const int w = tid >> 6, l = tid & 63;
+    const int bm = w == 1 ? bm0 : bm1, ntl = w == 1 ? nt0 : nt1;
+    int v[4], r = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
-      c[q] = e < E ? scnt[e] : 0;
-      t0v[q] = ceil_div(c[q], bm0) * nt0;
-      t1v[q] = ceil_div(c[q], bm1) * nt1;
-      rc += c[q];
-      r0 += t0v[q];
-      r1 += t1v[q];
+      const int e = 4 * l + q;
+      const int c = e < E ? scnt[e] : 0;
+      v[q] = w == 0 ? c : ceil_div(c, bm) * ntl;
+      r += v[q];
     }
-    const int ic = scan64(rc), i0 = scan64(r0), i1 = scan64(r1);
-    int pc = ic - rc, p0 = i0 - r0, p1 = i1 - r1;
+    const int inc = scan64(r);
+    int pre = inc - r;
+    int* dst = w == 0 ? soff : w == 1 ? so0 : so1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
-      if (e < E) {
-        soff[e] = pc;
-        so0[e] = p0;
-        so1[e] = p1;
-      }
-      pc += c[q];
-      p0 += t0v[q];
-      p1 += t1v[q];
+      const int e = 4 * l + q;
+      if (e < E) dst[e] = pre;
+      pre += v[q];
     }
-    if (tid == 63) {
-      soff[E] = ic;
-      so0[E] = i0;
-      so1[E] = i1;
-    }
+    if (l == 63) dst[E] = inc;
   }
   __syncthreads();
   for (int e = tid; e <= E; e += 512) {
