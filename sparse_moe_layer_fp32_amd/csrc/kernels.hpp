@@ -71,9 +71,12 @@ inline int decode_ksplits(int max_tiles, int nkb) {
 }
 inline int decode_kper(int nkb, int ksplit) { return (nkb + ksplit - 1) / ksplit; }
 
-// K splits of the router for T tokens (1: top-k fused into the router kernel;
-// >1: partial logits [splits][T][E] fp32 in `partial`, then a top-k kernel).
-int router_splits(int T, int d);
+// Waves per router workgroup (4: 64 tokens; 8: 128 tokens, for large batches
+// with at most 128 experts) and K splits of the router for T tokens (1: top-k
+// fused into the router kernel; >1: partial logits [splits][T][E] fp32 in
+// `partial`, then a top-k kernel).
+int router_waves(int T, int E);
+int router_splits(int T, int d, int E);
 
 // Outputs of the whole-batch routing path (T <= RT_TT): the router stage then
 // also writes counts, offsets, both tile lists and the placement.

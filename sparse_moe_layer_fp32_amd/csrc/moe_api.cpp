@@ -48,7 +48,7 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
     o = align256(o + bytes);
     return at;
   };
-  const int64_t ns = moe::router_splits((int)T, (int)d);
+  const int64_t ns = moe::router_splits((int)T, (int)d, (int)E);
   l.partial = put(ns > 1 ? 4 * ns * T * (16 * ceil_div((int)E, 16)) : 0);  // experts padded to 16
   l.topk_idx = put(4 * R);
   l.topk_w = put(4 * R);

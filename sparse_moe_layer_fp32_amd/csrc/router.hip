@@ -144,7 +144,9 @@ __device__ __forceinline__ void split3(float w, uint32_t& hi, uint32_t& mid, uin
 // experts, fewer rows for more experts (the three planes stay <= 61 KB).
 constexpr int w_fill(int nbw) { return nbw <= 4 ? kBlock : nbw <= 8 ? kBlock / 2 : kBlock / 4; }
 
-// grid = (token tiles of RT_TT, K splits); 4 waves x 16 tokens per workgroup.
+// grid = (token blocks of 16 WAVES tokens, K splits); WAVES waves x 16 tokens
+// per workgroup (4: one router tile; 8: two, for large batches, so that every
+// converted W_router fill serves twice the tokens).
 //
 // Logits l = x . W_router run on v_mfma_f32_16x16x32_bf16: x is bf16 and each
 // fp32 router weight is split into three bf16 parts (hi + mid + lo, exact),
@@ -156,8 +158,8 @@ constexpr int w_fill(int nbw) { return nbw <= 4 ? kBlock : nbw <= 8 ? kBlock / 2
 // memory.  The same registers feed the per-token e4m3 quantisation of x.
 // One split: top-k + softmax + tile histogram in place; several: partial
 // logits [split][T][E] for router_finish_kernel.
-template <int NBW>
-__global__ __launch_bounds__(256) void router_kernel(
+template <int NBW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void router_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ br,
     int T, int d, int E, int k, int gate_mode, int mx, int groups_per_split,
     float* __restrict__ partial, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -166,19 +168,21 @@ __global__ __launch_bounds__(256) void router_kernel(
   constexpr int KC = w_fill(NBW);                // W rows per fill
   constexpr int PITCH = 2 * KC + 16;             // bytes per expert row of a plane
   constexpr int UNITS = EP * KC / 8;             // (expert, 8 rows) conversion units
-  constexpr int UPT = (UNITS + 255) / 256;       // units per thread
+  constexpr int NTH = 64 * WAVES;                // threads
+  constexpr int TPW = WAVES / 4;                 // router tiles per workgroup
+  constexpr int UPT = (UNITS + NTH - 1) / NTH;   // units per thread
   constexpr int FILLS = kBlock / KC;             // fills per group
   __shared__ __attribute__((aligned(16))) uint8_t wl[3 * EP * PITCH];
-  __shared__ int shist[kMaxExperts];
+  __shared__ int shist[TPW][kMaxExperts];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
-  const int t0 = blockIdx.x * RT_TT + wave * 16;  // this wave's first token
+  const int t0 = blockIdx.x * (16 * WAVES) + wave * 16;  // this wave's first token
   const int ngroups = d / kBlock;
   const int g0 = blockIdx.y * groups_per_split;
   const int g1 = min(ngroups, g0 + groups_per_split);
   const bool fused = gridDim.y == 1;
   if (fused)
-    for (int i = tid; i < E; i += 256) shist[i] = 0;
+    for (int i = tid; i < TPW * kMaxExperts; i += NTH) shist[i / kMaxExperts][i % kMaxExperts] = 0;
 
   // x: lane holds token t0 + l16, the 8 bf16 at columns 32 c + 8 gq of a group
   const int xt = t0 + l16;
@@ -195,7 +199,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   auto load_w = [&](int row0) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = tid + 256 * j;
+      const int u = tid + NTH * j;
       const int e = u % EP, r8 = u / EP;
       const bool ok = u < UNITS && e < E;
 #pragma unroll
@@ -205,7 +209,7 @@ __global__ __launch_bounds__(256) void router_kernel(
   auto store_w = [&]() {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = tid + 256 * j;
+      const int u = tid + NTH * j;
       if (u >= UNITS) continue;
       const int e = u % EP, r8 = u / EP;
       uint32_t h[8], m[8], l[8];
@@ -328,13 +332,19 @@ __global__ __launch_bounds__(256) void router_kernel(
     }
     // the finish kernel adds its token blocks' picks into the tile histogram
     if (blockIdx.y == 0)
-      for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = 0;
+      for (int i = tid; i < TPW * E; i += NTH) {
+        const int rt = blockIdx.x * TPW + i / E;  // router tile
+        if (rt * RT_TT < T) hist[(size_t)rt * E + i % E] = 0;
+      }
     return;
   }
   __syncthreads();  // shist cleared
-  topk_emit<NBW>(tot, br, t0, T, E, k, gate_mode, topk_idx, topk_w, shist);
+  topk_emit<NBW>(tot, br, t0, T, E, k, gate_mode, topk_idx, topk_w, shist[wave >> 2]);
   __syncthreads();
-  for (int e = tid; e < E; e += 256) hist[(size_t)blockIdx.x * E + e] = shist[e];
+  for (int i = tid; i < TPW * E; i += NTH) {
+    const int rt = blockIdx.x * TPW + i / E;  // router tile
+    if (rt * RT_TT < T) hist[(size_t)rt * E + i % E] = shist[i / E][i % E];
+  }
 }
 
 // Lane exchanges inside the aligned group of eight lanes (half a DPP row):
@@ -476,30 +486,29 @@ __device__ void sum_partials(const float* __restrict__ partial, int nsplit, int 
   }
 }
 
-// Split-K finish for a block of kFinishTok tokens (a quarter of a router
-// tile, so that the partial reads of a tile spread over four CUs): the logit
-// of every (token, expert) is the sum of its partials in split order; then
-// top-k + softmax, and the block's picks are added to its router tile's
-// histogram (integer atomics: the counts do not depend on the order; the
-// router kernel zeroed the row).
-constexpr int kFinishTok = RT_TT / 4;
+// Split-K finish for a block of ntok tokens (a whole router tile, or a
+// quarter of one when the batch has few tiles, so that a tile's partial
+// reads spread over four CUs): the logit of every (token, expert) is the sum
+// of its partials in split order; then top-k + softmax, and the block's
+// picks are added to its router tile's histogram (integer atomics: the
+// counts do not depend on the order; the router kernel zeroed the row).
 template <int NBW>
 __global__ __launch_bounds__(512) void router_finish_kernel(const float* __restrict__ partial,
                                                              int nsplit, const float* __restrict__ br,
                                                              int T, int E, int k, int gate_mode,
                                                              int32_t* __restrict__ topk_idx,
                                                              float* __restrict__ topk_w,
-                                                             int32_t* __restrict__ hist) {
+                                                             int32_t* __restrict__ hist, int ntok) {
   constexpr int EP = NBW * 16;
   __shared__ float sl[RT_TT * (EP + 8)];
   __shared__ int shist[kMaxExperts];
   __shared__ float sbr[512];  // entries >= E are written but never read
   const int tid = threadIdx.x;
-  const int tt0 = blockIdx.x * kFinishTok;
-  const int tend = min(T, tt0 + kFinishTok);
+  const int tt0 = blockIdx.x * ntok;
+  const int tend = min(T, tt0 + ntok);
   const float brv = tid < E ? br[tid] : 0.f;
   if (tid < E) shist[tid] = 0;
-  sum_partials<EP>(partial, nsplit, T, tt0, sl, 512, kFinishTok);
+  sum_partials<EP>(partial, nsplit, T, tt0, sl, 512, ntok);
   sbr[tid] = brv;
   __syncthreads();  // the sums are in LDS, shist and sbr are set
   topk_group8<EP>(sl, sbr, tt0, tend, E, k, gate_mode, topk_idx, topk_w, shist, nullptr, nullptr,
@@ -656,27 +665,41 @@ hipError_t launch_router_nbw(const uint16_t* x, const float* Wr, const float* br
   const int ngroups = d / kBlock;
   const int gps = ceil_div(ngroups, nsplit);
   const int ns = ceil_div(ngroups, gps);
-  hipLaunchKernelGGL((router_kernel<NBW>), dim3(tiles, ns), dim3(256), 0, stream, x, Wr, br, T, d,
-                     E, k, gate_mode, mx ? 1 : 0, gps, partial, topk_idx, topk_w, hist, xq, xs);
+  const int waves = router_waves(T, E);
+  if constexpr (NBW <= 8) {
+    if (waves == 8) {
+      hipLaunchKernelGGL((router_kernel<NBW, 8>), dim3(ceil_div(T, 16 * 8), ns), dim3(64 * 8), 0, stream,
+                         x, Wr, br, T, d, E, k, gate_mode, mx ? 1 : 0, gps, partial, topk_idx, topk_w,
+                         hist, xq, xs);
+    }
+  }
+  if (waves == 4)
+    hipLaunchKernelGGL((router_kernel<NBW, 4>), dim3(tiles, ns), dim3(64 * 4), 0, stream, x, Wr, br, T,
+                       d, E, k, gate_mode, mx ? 1 : 0, gps, partial, topk_idx, topk_w, hist, xq, xs);
   if (sr != nullptr)
     hipLaunchKernelGGL((route_small_kernel<NBW>), dim3(1), dim3(512), 0, stream, partial, ns, ns == 1,
                        br, T, E, k, gate_mode, topk_idx, topk_w, sr->counts, sr->offsets, sr->tile_off0,
                        sr->tile_off1, reinterpret_cast<int4*>(sr->tiles0),
                        reinterpret_cast<int4*>(sr->tiles1), sr->bm0, sr->nt0, sr->max0, sr->bm1,
                        sr->nt1, sr->max1, sr->row_of, sr->row_token);
-  else if (ns > 1)
-    hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(ceil_div(T, kFinishTok)), dim3(512), 0, stream, partial, ns,
-                       br, T, E, k, gate_mode, topk_idx, topk_w, hist);
+  else if (ns > 1) {
+    // quarter tiles while the batch has fewer tiles than half the CUs
+    const int ntok = tiles < 128 ? RT_TT / 4 : RT_TT;
+    hipLaunchKernelGGL((router_finish_kernel<NBW>), dim3(ceil_div(T, ntok)), dim3(512), 0, stream,
+                       partial, ns, br, T, E, k, gate_mode, topk_idx, topk_w, hist, ntok);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-int router_splits(int T, int d) {
+int router_waves(int T, int E) { return (T >= 2048 && ceil_div(E, 16) <= 8) ? 8 : 4; }
+
+int router_splits(int T, int d, int E) {
   if (T <= 0) return 1;
-  const int tiles = ceil_div(T, RT_TT);
   const int ngroups = d / kBlock;
-  const int want = ceil_div(512, tiles);  // about two workgroups per CU
+  // about two 4-wave or one 8-wave workgroup per CU
+  const int want = router_waves(T, E) == 8 ? ceil_div(256, ceil_div(T, 16 * 8)) : ceil_div(512, ceil_div(T, RT_TT));
   const int ns = want < ngroups ? want : ngroups;
   if (ns <= 1) return 1;
   const int gps = ceil_div(ngroups, ns);
@@ -687,7 +710,7 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, in
                          int k, int gate_mode, bool mx, float* partial, int32_t* topk_idx,
                          float* topk_w, int32_t* hist, uint8_t* xq, void* xs, const SmallRoute* sr,
                          hipStream_t stream) {
-  const int nsplit = router_splits(T, d);
+  const int nsplit = router_splits(T, d, E);
   switch (ceil_div(E, 16)) {
 #define MOE_ROUTER_CASE(n)                                                                     \
   case n:                                                                                      \

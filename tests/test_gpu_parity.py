@@ -69,6 +69,9 @@ SMALL = [
     (50, 256, 256, 128, 5, 5),          # k = E (every expert)
     (130, 640, 640, 384, 3, 1),         # k = 1, down-projection column tail (640 = 2.5 x 256)
     (513, 384, 384, 512, 7, 3),         # odd expert count, T not a multiple of 16
+    (2100, 384, 384, 256, 20, 2),       # 128-token router workgroups, 3 K splits, ragged last block
+    (2048, 256, 256, 128, 128, 4),      # 128-token router workgroups with E = 128
+    (32800, 128, 128, 128, 8, 1),       # 128-token router workgroups, one split: top-k in the router
 ]
 
 
