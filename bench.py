@@ -68,23 +68,26 @@ ATTN_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "attention.hi
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c1": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 271558.412, "write_kib": 759.256,
-        "copy_fetch_kib": 524311.125, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 920012.425, "write_kib": 103914.719,
-        "copy_fetch_kib": 524305.6875, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 279949.713, "write_kib": 761.312,
-        "copy_fetch_kib": 524308.125, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 942775.488, "write_kib": 103719.781,
-        "copy_fetch_kib": 524307.75, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 144512.350, "write_kib": 759.256,
-        "copy_fetch_kib": 524314.25, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "cae94ab1c3d2c6ad67e1e02297828787ee620b8fae8562aaf5b530ba6e1ad187",
-        "fetch_kib": 579350.738, "write_kib": 103737.000,
+    "c4b": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 2807640.138, "write_kib": 215672.731,
+        "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 271558.513, "write_kib": 759.200,
+        "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 914708.075, "write_kib": 103844.750,
+        "copy_fetch_kib": 524306.9375, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 279948.675, "write_kib": 760.850,
+        "copy_fetch_kib": 524308.1875, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 941394.850, "write_kib": 103776.081,
+        "copy_fetch_kib": 524307.1875, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 144511.550, "write_kib": 759.156,
+        "copy_fetch_kib": 524312.0625, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
+        "fetch_kib": 575881.625, "write_kib": 103791.325,
         "copy_fetch_kib": 524305.875, "copy_write_kib": 1048576.0},
 }
 
