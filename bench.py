@@ -151,9 +151,10 @@ def calibration_copy(mib, dev):
 
 
 def sampled_steps(steps, every):
-    """Timed steps that carry the per-kernel events: every ``every``-th one (at
-    least one step).  A timing event costs a few microseconds of device time,
-    so the other steps run without them and the step time stays the call's."""
+    """Steps of the instrumented pass that carry the per-kernel events: one per
+    ``every`` timed steps (at least one).  A timing event costs a few
+    microseconds of device time, so the events run in an untimed pass of their
+    own and the timed region holds plain calls only."""
     every = max(1, every)
     picked = [i for i in range(steps) if i % every == every - 1]
     return picked or [steps - 1]
@@ -293,16 +294,15 @@ def attn_bench(args):
     torch.cuda.synchronize()
     sampled = sampled_steps(args.steps, args.event_every)
     evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for i in sampled}
+    for i in sampled:  # per-call times from an untimed instrumented pass
+        evs[i][0].record()
+        run()
+        evs[i][1].record()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        if i in evs:
-            evs[i][0].record()
-            run()
-            evs[i][1].record()
-        else:
-            run()
+        run()
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -318,7 +318,7 @@ def attn_bench(args):
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_attn_traffic(args.workload),
                 "kernel": "attn_decode_kernel + attn_combine_kernel (the whole call)",
                 "avg_ms": round(call_ms, 5), "algorithmic_bytes": work["bytes"]}
-    roof["timed_launches"] = len(sampled)
+    roof["event_launches"] = len(sampled)
     cfg = ({"workload": f"attn_prefill: causal GQA attention with sinks, S=8192, Hq=64, Hkv=8, D=64",
             "S": 8192} if prefill else
            {"workload": f"attn_decode: one query per sequence, B=64, KV up to 4096 (ragged, mean "
@@ -465,7 +465,9 @@ def peaks_bench(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50; 300 for decode-sized batches, whose steps take "
+                         "~0.1-0.5 ms, so that the timed region is not dominated by its edges)")
     # compute-bound kernels reach their steady clock after about 20 launches
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="c4b",
@@ -478,13 +480,12 @@ def main():
                     help="weight format: 128x128 block-scaled FP8, MXFP8 (E8M0 per 32) or MXFP4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=5,
-                    help="record the per-kernel timing events on every N-th timed step only (each "
-                         "event costs a few microseconds of device time; the other steps run the "
-                         "plain call)")
+                    help="one instrumented step (per-kernel timing events) per N timed steps, run in "
+                         "an untimed pass before the timed region: each event costs a few "
+                         "microseconds of device time, so the timed steps are plain calls")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding one forward (captured after the warm-up, "
-                         "as a serving loop replays it) instead of eager calls; the per-kernel times "
-                         "then come from an eager pass before the timed region")
+                         "as a serving loop replays it) instead of eager calls")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="read this many MiB between timed calls (outside the calls' events) so "
                          "that every call reads its weights from HBM; 0: back-to-back steps")
@@ -498,6 +499,8 @@ def main():
         sys.exit(2)
 
     if args.workload.startswith("attn"):
+        if args.steps is None:
+            args.steps = 50
         attn_bench(args)
         return
     if args.workload == "peaks":
@@ -512,6 +515,8 @@ def main():
     dev = torch.device("cuda:0")
     p = moe.device_inputs(inp, dev)
     T, d, f, E, k = inp["T"], inp["d"], inp["f"], inp["E"], inp["k"]
+    if args.steps is None:
+        args.steps = 300 if T * k <= 32 * E else 50   # decode-sized (the library's auto path rule)
     w_args = (p["W_router"], p["b_router"], k, p["W_gateup"], p["S_gateup"], p["b_gateup"],
               p["W_down"], p["S_down"], p["b_down"])
     ws = torch.empty(moe.workspace_bytes(T, d, f, E, k), dtype=torch.uint8, device=dev)
@@ -553,12 +558,13 @@ def main():
     torch.cuda.synchronize()
     sampled = sampled_steps(args.steps, args.event_every)
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
+    # per-kernel times from an untimed pass of instrumented steps
+    for i in sampled:
+        step(evs[i])
+    torch.cuda.synchronize()
     graph = None
     if args.graph:
-        # per-kernel times from eager steps, then one forward captured for the timed replays
-        for i in sampled:
-            step(evs[i])
-        torch.cuda.synchronize()
+        # one forward captured for the timed replays
         side = torch.cuda.Stream(dev)
         side.wait_stream(torch.cuda.current_stream(dev))
         with torch.cuda.stream(side):
@@ -574,12 +580,12 @@ def main():
     calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(args.steps)] if flush is not None else None
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {args.steps} steps (stage events on {len(sampled)} of them"
+    log(f"[bench] timing {args.steps} steps (stage events from {len(sampled)} untimed steps"
         + (f", {args.flush_mib} MiB flush before each)" if flush is not None else ")"))
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        run = graph.replay if graph is not None else (lambda: step(evs.get(i)))
+        run = graph.replay if graph is not None else step
         if flush is not None:
             flush_sink.copy_(flush.sum())   # untimed read: evicts L2 and the memory-side cache
             calls[i][0].record()
@@ -614,7 +620,7 @@ def main():
                       f"grouped_gemm_wide_kernel<true, {tf}>") + \
         " (gate/up + bias + SwiGLU + h quantisation)"
     roof["avg_ms"] = round(gate_ms, 5)
-    roof["timed_launches"] = len(sampled)
+    roof["event_launches"] = len(sampled)
     roof["algorithmic_bytes"] = ga["bytes"]
     roof["algorithmic_flops"] = ga["flops"]
 
