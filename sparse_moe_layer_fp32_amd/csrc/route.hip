@@ -60,9 +60,17 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   const int e = tid % EP, p = tid / EP;
   const int ch = ceil_div(nt, P);
   const int lo = min(nt, p * ch), hi = min(nt, lo + ch);
+  // the thread's chunk of its expert's column, 16 loads in flight at a time
+  constexpr int kBatch = 16;
   int s = 0;
   if (e < E)
-    for (int tl = lo; tl < hi; ++tl) s += hist[(size_t)tl * E + e];
+    for (int t0 = lo; t0 < hi; t0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = t0 + j < hi ? hist[(size_t)(t0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) s += v[j];
+    }
   spart[tid] = s;
   __syncthreads();
   if (p == 0 && e < E) {                 // exclusive scan over this expert's chunks
@@ -101,9 +109,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   }
   if (e < E) {                           // absolute first row of every (tile, expert)
     int run = soff[e] + spart[tid];
-    for (int tl = lo; tl < hi; ++tl) {
-      tile_base[(size_t)tl * E + e] = run;
-      run += hist[(size_t)tl * E + e];
+    for (int t0 = lo; t0 < hi; t0 += kBatch) {
+      int v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) v[j] = t0 + j < hi ? hist[(size_t)(t0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (t0 + j < hi) {
+          tile_base[(size_t)(t0 + j) * E + e] = run;
+          run += v[j];
+        }
     }
   }
 }
