@@ -164,6 +164,7 @@ __global__ __launch_bounds__(64 * WAVES) void router_kernel(
     int T, int d, int E, int k, int gate_mode, int mx, int groups_per_split,
     float* __restrict__ partial, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     int32_t* __restrict__ hist, uint8_t* __restrict__ xq, void* __restrict__ xs) {
+  static_assert(WAVES == 4 || WAVES == 8, "one or two router tiles per workgroup");
   constexpr int EP = NBW * 16;                   // experts padded to 16
   constexpr int KC = w_fill(NBW);                // W rows per fill
   constexpr int PITCH = 2 * KC + 16;             // bytes per expert row of a plane
