@@ -276,16 +276,43 @@ __global__ __launch_bounds__(64 * WAVES) void router_kernel(
         }
         if (xt < T && gq == 0)
           reinterpret_cast<uint32_t*>(xs)[(size_t)xt * ngroups + g] = codes;
-      } else if (xt < T) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          float q[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) q[i] = clamp_fp8(v[8 * c + i] / s);
+      } else {
+        // v / s for the 32 values of one scale.  With the correctly rounded
+        // reciprocal y, q0 = v y and the residual v - q0 s (exact by fma),
+        // q0 + residual * y is the IEEE quotient wherever |v / s| >= 2^-10,
+        // and smaller quotients get the same e4m3 code (a zero of v's sign):
+        // checked exhaustively over every bf16 group maximum with
+        // s >= 2^-64 and every bf16 value up to it.  A wave with a smaller,
+        // an infinite or a NaN scale divides.
+        const bool quick = __all(xt >= T || (s >= 0x1p-64f && s < __builtin_inff()));
+        const float y = 1.0f / s;
+        auto put = [&](int c, const float (&q)[8]) {
           *reinterpret_cast<uint2*>(xq + (size_t)xt * d + g * kBlock + 32 * c + 8 * gq) =
               make_uint2(f32x4_to_e4m3(q[0], q[1], q[2], q[3]), f32x4_to_e4m3(q[4], q[5], q[6], q[7]));
+        };
+        if (xt < T) {
+          if (quick) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float q[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) {
+                const float a = v[8 * c + i], q0 = a * y;
+                q[i] = clamp_fp8(copysignf(fmaf(fmaf(-q0, s, a), y, q0), a));
+              }
+              put(c, q);
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              float q[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) q[i] = clamp_fp8(v[8 * c + i] / s);
+              put(c, q);
+            }
+          }
+          if (gq == 0) reinterpret_cast<float*>(xs)[(size_t)xt * ngroups + g] = s;
         }
-        if (gq == 0) reinterpret_cast<float*>(xs)[(size_t)xt * ngroups + g] = s;
       }
     }
     v4f part[NBW];
