@@ -52,8 +52,9 @@
  *    launch failure returns MOE_ERR_HIP.  Device faults surface at the
  *    caller's next sync.  No C++ exception crosses the boundary.
  *  - T == 0 is a no-op returning MOE_OK (x and out may then be NULL).
- *  - Deterministic: the same inputs give the same output bits (no atomics
- *    on data paths; every reduction has a fixed order), so a replayed graph
+ *  - Deterministic: the same inputs give the same output bits (every
+ *    floating-point reduction has a fixed order; atomics only add integer
+ *    counts, whose sums do not depend on the order), so a replayed graph
  *    reproduces the eager call bit for bit.
  *  - `out` must not alias any input or the workspace.
  *  - NaN: a NaN in x makes every output of its token NaN; a NaN weight code,
