@@ -981,11 +981,17 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 
   auto compute = [&](const uint8_t* abase, const uint8_t* bbase) {
     if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
-    const float* sbs = reinterpret_cast<const float*>(abase + W_SA + W_SIDE_BS);
-    const v4f sl = *reinterpret_cast<const v4f*>(abase + s_pos);
-    const v2f sh = *reinterpret_cast<const v2f*>(abase + s_pos + 16);
-    const float sb0 = GATED ? sbs[0] : sbs[wn >> 1];
-    const float sb1 = GATED ? sbs[1] : sb0;
+    auto a_frag = [&](int mb) -> v8i {
+      const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
+      const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
+      const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
+      return v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    // LDS reads in the order of first use (LDS data returns in order): the
+    // first MFMA waits for its own two operands only, the scales come last
+    // (the first promotion follows the fourth MFMA)
+    v8i xf[2];
+    xf[0] = a_frag(0);
     v8i wf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -996,21 +1002,24 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
         wf[nb][2 * r] = t[0];
         wf[nb][2 * r + 1] = t[1];
       }
+    __builtin_amdgcn_sched_barrier(0);
+    const float* sbs = reinterpret_cast<const float*>(abase + W_SA + W_SIDE_BS);
+    const v4f sl = *reinterpret_cast<const v4f*>(abase + s_pos);
+    const v2f sh = *reinterpret_cast<const v2f*>(abase + s_pos + 16);
+    const float sb0 = GATED ? sbs[0] : sbs[wn >> 1];
+    const float sb1 = GATED ? sbs[1] : sb0;
+    __builtin_amdgcn_sched_barrier(0);
     // MB * NB MFMAs j = 4 mb + nb; the FMAs of MFMA j follow MFMA j + 3, by
-    // when its result is ready (two behind measured 1.4 % slower)
+    // when its result is ready (two behind measured 1.4 % slower).  The
+    // activation fragment of row block mb + 1 is read right after the first
+    // MFMA of block mb, three MFMAs before its use (two buffers).
     v4f pp[MB * NB];
-    v8i xf[MB];
 #pragma unroll
     for (int j = 0; j < MB * NB + 3; ++j) {
       if (j < MB * NB) {
         const int mb = j >> 2, nb = j & 3;
-        if (nb == 0) {
-          const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
-          const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
-          const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
-          xf[mb] = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-        }
-        pp[j] = mfma_fp8_16x16x128(wf[nb], xf[mb], v4f{0.f, 0.f, 0.f, 0.f});
+        pp[j] = mfma_fp8_16x16x128(wf[nb], xf[mb & 1], v4f{0.f, 0.f, 0.f, 0.f});
+        if (nb == 0 && mb + 1 < MB) xf[(mb + 1) & 1] = a_frag(mb + 1);
       }
       if (j >= 3) {
         const int q = j - 3, mb = q >> 2, nb = q & 3;
