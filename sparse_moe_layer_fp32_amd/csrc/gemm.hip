@@ -939,6 +939,17 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
     }
 
+  // activation fragment of row block mb (rows 96 wm + 16 mb + l16)
+  auto a_frag = [&](const uint8_t* abase, int mb) -> v8i {
+    const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
+    const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
+    const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
+    return v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+  };
+
+  // LDS reads in the order of first use (LDS data returns in order), and the
+  // activation fragment of row block mb + 1 read right after the first MFMA
+  // of block mb, three MFMAs before its use (two buffers)
   auto compute_mx = [&](const uint8_t* abase, const uint8_t* bbase) {
     if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
     // E8M0 scales: byte gq (K group) of the dwords of rows 96 wm + 16 mb + l16,
@@ -949,6 +960,8 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
       xsc[mb] = static_cast<int>((mb < 4 ? sl[mb] : (mb == 4 ? sh.x : sh.y)) >> (8 * gq));
+    v8i xf[2];
+    xf[0] = a_frag(abase, 0);
     const uint8_t* wsc = abase + W_SA + W_SIDE_BS + MX_PITCH * gq + l16;
     int wsv[NB];
     v8i wf[NB];
@@ -965,33 +978,25 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
         wf[nb][2 * r + 1] = t[1];
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
-      const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
-      const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
-      const v8i xf = v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (FP4) macc[mb][nb] = mfma_fp4_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
-        else macc[mb][nb] = mfma_fp8_16x16x128_mx(wf[nb], xf, macc[mb][nb], wsv[nb], xsc[mb]);
+        if constexpr (FP4) macc[mb][nb] = mfma_fp4_fp8_16x16x128_mx(wf[nb], xf[mb & 1], macc[mb][nb], wsv[nb], xsc[mb]);
+        else macc[mb][nb] = mfma_fp8_16x16x128_mx(wf[nb], xf[mb & 1], macc[mb][nb], wsv[nb], xsc[mb]);
+        if (nb == 0 && mb + 1 < MB) xf[(mb + 1) & 1] = a_frag(abase, mb + 1);
+        __builtin_amdgcn_sched_barrier(0);  // keeps the read ahead of its use
       }
     }
   };
 
   auto compute = [&](const uint8_t* abase, const uint8_t* bbase) {
     if (wm == 1 && tc.valid <= W_HALF) return;  // no rows in this wave's half
-    auto a_frag = [&](int mb) -> v8i {
-      const uint8_t* pa = abase + a_row + mb * 16 * kBlock;
-      const v4i lo4 = *reinterpret_cast<const v4i*>(pa + a_pos0);
-      const v4i hi4 = *reinterpret_cast<const v4i*>(pa + a_pos1);
-      return v8i{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    };
-    // LDS reads in the order of first use (LDS data returns in order): the
-    // first MFMA waits for its own two operands only, the scales come last
-    // (the first promotion follows the fourth MFMA)
+    // the first MFMA waits for its own two operands only; the scales come
+    // last (the first promotion follows the fourth MFMA)
     v8i xf[2];
-    xf[0] = a_frag(0);
+    xf[0] = a_frag(abase, 0);
     v8i wf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -1010,16 +1015,14 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     const float sb1 = GATED ? sbs[1] : sb0;
     __builtin_amdgcn_sched_barrier(0);
     // MB * NB MFMAs j = 4 mb + nb; the FMAs of MFMA j follow MFMA j + 3, by
-    // when its result is ready (two behind measured 1.4 % slower).  The
-    // activation fragment of row block mb + 1 is read right after the first
-    // MFMA of block mb, three MFMAs before its use (two buffers).
+    // when its result is ready (two behind measured 1.4 % slower)
     v4f pp[MB * NB];
 #pragma unroll
     for (int j = 0; j < MB * NB + 3; ++j) {
       if (j < MB * NB) {
         const int mb = j >> 2, nb = j & 3;
         pp[j] = mfma_fp8_16x16x128(wf[nb], xf[mb & 1], v4f{0.f, 0.f, 0.f, 0.f});
-        if (nb == 0 && mb + 1 < MB) xf[(mb + 1) & 1] = a_frag(mb + 1);
+        if (nb == 0 && mb + 1 < MB) xf[(mb + 1) & 1] = a_frag(abase, mb + 1);
       }
       if (j >= 3) {
         const int q = j - 3, mb = q >> 2, nb = q & 3;
