@@ -35,8 +35,11 @@ def sources():
 
 
 # per-source extra flags: the GEMMs keep MFMA results in VGPRs (the fp32
-# promotion reads them right away; the AGPR form would add one copy per value)
-EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# promotion reads them right away; the AGPR form would add one copy per value),
+# and their atomics stay as written: one lane adds and its result is used only
+# later (the wave-wide rewrite of the atomic optimizer would wait for the
+# result, and with it for every load in flight, right after the atomic)
+EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _compile(src):

@@ -132,12 +132,11 @@ __device__ __forceinline__ v4i dma_rsrc(const void* p, uint32_t bytes) {
 
 // Global -> LDS loads (buffer_load ... lds): lane i writes bytes [s*i, s*i+s)
 // at LDS address `lds` (uniform); offsets past the resource size read zeros.
-// Written as inline asm so that the compiler does not track them: its wait
-// analysis cannot tell the ring stages apart across the persistent loop and
-// would wait for every load in flight before each LDS read.  The kernel's own
-// s_waitcnt + s_barrier pairs order these loads against the reads; a wait
-// the compiler adds for its own memory operations only waits longer.  M0 is
-// restored.
+// Inline asm, which the compiler does not track, for the decode kernel: its
+// own s_waitcnt + s_barrier pairs order these loads against the reads, and a
+// wait the compiler adds for its own memory operations only waits longer.
+// (The prefill kernel uses the compiler's builtin instead; see lds_load.)  M0
+// is restored.
 // PIN: the descriptor is uniform, but in some kernels the register allocator
 // copies it to VGPRs, which the scalar asm operand cannot take; readfirstlane
 // pins it to SGPRs there (elsewhere it would only perturb the allocation).
@@ -723,6 +722,39 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 // about half a tile.  Persistent over the tile list; the loads run ahead
 // across tile boundaries (the next tile's first blocks load while the
 // current tile ends).
+//
+// Schedule: XCD x (workgroups b with b % 8 == x) owns the x-th of eight
+// ranges of the tile list, and workgroup b takes its slot's first two tiles
+// lo + b / 8 and lo + b / 8 + slots.  With g.sched the ranges have equal cost
+// (the scan stage sets them; a tile of at most 96 rows costs 2/3 of a full
+// one in the gate/up GEMM, 1/2 in the down GEMM) instead of equal length, and, with at least 4 K blocks per tile, the
+// rest of a range is handed out in order by an integer counter of its XCD.
+// Tiles take 29-44 us on the skewed prefill layer, and a fixed round robin
+// over equal lengths left the workgroups of an XCD up to five tiles apart at
+// the end and the XCDs up to 150 us apart (the range that holds only full
+// tiles of the hottest expert against one with 329 short tiles).  A tile
+// index is fetched two tiles ahead: wave 0 adds to the counter after the ring
+// barrier of a tile's first K block, stores the index in LDS in the second
+// (its ring wait covers the atomic) and every wave reads it in the third.
+// Which workgroup computes a tile does not change any result.  The last
+// workgroup to finish zeroes the counters again.
+// Global -> LDS loads through the compiler's builtin (the instruction of
+// dma16 / dma4), for the kernel below.  Every ring stage there is a
+// __shared__ array of its own, so the compiler's wait analysis tells the
+// stages apart and adds no wait inside a step; and it sees every load in
+// flight, so a value that an atomic returns is known to have arrived once
+// the ring wait that covers the atomic has passed.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+template <int SIZE>
+__device__ __forceinline__ void lds_load(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t voff) {
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4 loads");
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, voff, 0, 0, 0);
+}
+
 constexpr int WM_ROWS = 192, WN_COLS = 256, W_HALF = WM_ROWS / 2;
 constexpr int W_SA = WM_ROWS * kBlock, W_SIDE = 2048;
 constexpr int W_ASTAGE = W_SA + W_SIDE;
@@ -755,21 +787,43 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
 
   const int total = ((const const_i32*)g.tile_off)[g.E];
   const int nslots = gridDim.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int lo = (blockIdx.x & 7) * chunk;
-  const int hi = min(total, lo + chunk);
+  const int xcd = blockIdx.x & 7;
+  int32_t* const sched = g.sched;
+  int lo, hi;
+  if (sched != nullptr) {  // ranges of equal cost (clamped into the list)
+    const const_i32* bd = (const const_i32*)(sched + kSchedBounds);
+    lo = min(max(bd[xcd], 0), total);
+    hi = min(max(bd[xcd + 1], lo), total);
+  } else {
+    const int c = (total + 7) >> 3;
+    lo = min(xcd * c, total);
+    hi = min(total, lo + c);
+  }
+  const int chunk = hi - lo;
   const int L0 = lo + (blockIdx.x >> 3);
-  if (L0 >= hi) return;
+  const bool dyn = sched != nullptr && nkb >= 4;
+  // the last workgroup to finish (every fetch of every workgroup has returned
+  // by then) zeroes the counters for the next launch
+  auto finish = [&]() {
+    if (sched != nullptr && tid == 0 && atomicAdd(&sched[8], 1) == (int)gridDim.x - 1) {
+#pragma unroll
+      for (int i = 0; i < 9; ++i) atomicExch(&sched[i], 0);
+    }
+  };
+  if (L0 >= hi) {
+    finish();
+    return;
+  }
 
-  const v4i rA = dma_rsrc(g.A, g.A_bytes);
+  const __amdgpu_buffer_rsrc_t rA = buf_rsrc(g.A, g.A_bytes);
   // side loads: waves 0-3 the A row scales; block-scaled: waves 4, 5 the bias,
   // wave 6 the two weight-block scales; MX: waves 4-7 the E8M0 weight scales
   // of K groups 0-3 and waves 4, 5 the bias with a second load
-  const v4i rBias = dma_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N);
+  const __amdgpu_buffer_rsrc_t rBias = buf_rsrc(g.bias, 2u * (uint32_t)g.E * (uint32_t)N);
   const uint32_t bs_bytes = MX ? (uint32_t)g.E * (uint32_t)(K / 32) * (uint32_t)N
                                : 4u * (uint32_t)g.E * nkb * nsb;
-  const v4i rSide = wave < 4 ? dma_rsrc(g.As, g.As_bytes)
-                    : (wave < 6 && !MX) ? rBias : dma_rsrc(g.Bs, bs_bytes);
+  const __amdgpu_buffer_rsrc_t rSide = wave < 4 ? buf_rsrc(g.As, g.As_bytes)
+                                        : (wave < 6 && !MX) ? rBias : buf_rsrc(g.Bs, bs_bytes);
   const int side_step = wave < 4 ? 4 : MX ? 4 * N : (wave == 6 ? 4 * nsb : 0);
   const uint32_t side_dst = (MX && wave >= 4) ? W_SIDE_BS + MX_PITCH * (wave - 4) : 256 * wave;
 
@@ -783,13 +837,34 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   int Lb = L0, kbb = 0;
   DmaTile tb = ta;
   uint32_t boff[BQ];
-  v4i rB;
+  __amdgpu_buffer_rsrc_t rB;
+  // ---- dynamic schedule: in the first K block of every tile wave 0 fetches
+  // the tile after the next one (while the last index fetched was a tile),
+  // stores it in snext in the second K block (the ring wait of that block
+  // covers the atomic, so no further wait), and every wave reads it in the
+  // third, before the A cursor, one K block ahead, moves to the next tile at
+  // the end of block nkb - 2 (hence nkb >= 4)
+  __shared__ int32_t snext;
+  int tkt = 0, Lnext = L0;
+  // after the ring barrier
+  auto fetch_begin = [&](int kb) {
+    if (dyn && kb == 2 && Lnext < hi) Lnext = __builtin_amdgcn_readfirstlane(snext);
+    if (dyn && kb == 0 && Lnext < hi && wave == 0 && lane == 0) tkt = atomicAdd(&sched[xcd], 1);
+  };
+  // after the MFMAs
+  auto fetch_end = [&](int kb) {
+    if (dyn && kb == 1 && Lnext < hi && wave == 0) {
+      // a count outside [0, chunk) (counters not zeroed) reads as the end
+      if (lane == 0) snext = (tkt >= 0 && tkt < chunk) ? lo + 2 * nslots + tkt : hi;
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the store is done before the barrier
+    }
+  };
 
   auto rt_load = [&](const DmaTile& t, bool live, int buf) {
     if constexpr (GATED) {
       const int r = 64 * wave + lane;
       const uint32_t o = (live && wave < 3 && r < t.valid) ? 4u * (uint32_t)(t.row0 + r) : kOob;
-      dma4(dma_rsrc(g.row_token, g.rows_bytes), lds_addr(&rtok[buf][64 * wave]), o);
+      lds_load<4>(buf_rsrc(g.row_token, g.rows_bytes), reinterpret_cast<uint8_t*>(&rtok[buf][64 * wave]), o);
     }
   };
   auto setup_a = [&](const DmaTile& t, int buf) {
@@ -829,7 +904,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   };
   auto setup_b = [&](const DmaTile& t) {
     const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
-    rB = dma_rsrc(g.B + (size_t)t.e * KR * nkb * N, (uint32_t)(KR * nkb) * (uint32_t)N);
+    rB = buf_rsrc(g.B + (size_t)t.e * KR * nkb * N, (uint32_t)(KR * nkb) * (uint32_t)N);
 #pragma unroll
     for (int q = 0; q < BQ; ++q) {  // chunk BQ wave + q: stored rows 4 chunk + lane / 16
       const int kr = 4 * (BQ * wave + q) + (lane >> 4);
@@ -847,34 +922,39 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   // last tile (the offsets then point past the buffers and the loads land as
   // zeros in a stage no one reads), so the in-flight count is the same on
   // every path.
-  auto a_load = [&](uint32_t sbase, int q) {
-    dma16(rA, sbase + (W_AQ * wave + q) * 1024, aoff[q] + (uint32_t)kba * kBlock);
+  // The ring waits count this wave's loads in issue order (activation group,
+  // weight group, row tokens, epilogue stores): a scheduling barrier after
+  // each group keeps the compiler from moving loads across groups.
+  auto a_load = [&](uint8_t* base, int q) {
+    lds_load<16>(rA, base + (W_AQ * wave + q) * 1024, aoff[q] + (uint32_t)kba * kBlock);
   };
-  auto side_load = [&](uint32_t sbase) {
-    dma4(rSide, sbase + W_SA + side_dst, soff + (uint32_t)(kba * side_step));
-    if (MX && (wave == 4 || wave == 5)) dma4(rBias, sbase + W_SA + W_SIDE_BIAS + 256 * (wave - 4), soff2);
+  auto side_load = [&](uint8_t* base) {
+    lds_load<4>(rSide, base + W_SA + side_dst, soff + (uint32_t)(kba * side_step));
+    if (MX && (wave == 4 || wave == 5)) lds_load<4>(rBias, base + W_SA + W_SIDE_BIAS + 256 * (wave - 4), soff2);
   };
-  auto b_load = [&](uint32_t sbase, int q) {
-    dma16(rB, sbase + (BQ * wave + q) * 1024, boff[q] + (uint32_t)kbb * KR * (uint32_t)N);
+  auto b_load = [&](uint8_t* base, int q) {
+    lds_load<16>(rB, base + (BQ * wave + q) * 1024, boff[q] + (uint32_t)kbb * KR * (uint32_t)N);
   };
   auto issue_a = [&](uint8_t* base) {
-    const uint32_t sbase = lds_addr(base);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < W_AQ; ++q) a_load(sbase, q);
-    side_load(sbase);
+    for (int q = 0; q < W_AQ; ++q) a_load(base, q);
+    side_load(base);
+    __builtin_amdgcn_sched_barrier(0);
     ++kba;
   };
   auto issue_b = [&](uint8_t* base) {
-    const uint32_t sbase = lds_addr(base);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < BQ; ++q) b_load(sbase, q);
+    for (int q = 0; q < BQ; ++q) b_load(base, q);
+    __builtin_amdgcn_sched_barrier(0);
     ++kbb;
   };
   // Cursor moves after a tile's last K block has been issued.
   auto advance_b = [&]() {
     if (kbb < nkb) return;
     kbb = 0;
-    Lb += nslots;
+    Lb = dyn ? Lan : Lb + nslots;  // the A cursor is one K block behind: its next tile
     if (Lb < hi) {
       tb = dma_tile(g, Lb);
       setup_b(tb);
@@ -889,7 +969,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     La = Lan;
     ta = tan;
     rb ^= 1;
-    Lan += nslots;
+    Lan = dyn ? Lnext : Lan + nslots;
     if (Lan < hi) tan = dma_tile(g, Lan);
     if (nkb == 1) {  // the row tokens were loaded one K block ago: wait for them
       wait_vmcnt<0>();
@@ -1212,16 +1292,18 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   // block i + 1 and B of block i + 2.  Returns false after the last tile.
   auto step = [&](const uint8_t* ca, uint8_t* na, const uint8_t* cb, uint8_t* nb2) -> bool {
     wait_stage(pend);
+    fetch_begin(kbc);
     issue_a(na);
     if constexpr (MX) compute_mx(ca, cb);
     else compute(ca, cb);
+    fetch_end(kbc);
     issue_b(nb2);
     pend = advance_a();
     advance_b();
     if (++kbc < nkb) return true;
     epilogue(tc, ca);
     pend += ST;
-    Lc += nslots;
+    Lc = dyn ? La : Lc + nslots;  // the A cursor moved to the next tile one step ago
     if (Lc >= hi) return false;
     kbc = 0;
     tc = dma_tile(g, Lc);
@@ -1231,6 +1313,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
          step(sa1, sa0, sb0, sb2) && step(sa0, sa1, sb1, sb0) && step(sa1, sa0, sb2, sb1)) {
   }
   wait_vmcnt<0>();  // the loads past the last tile land before the workgroup ends
+  finish();
 }
 
 // ---------------------------------------------------------------------------

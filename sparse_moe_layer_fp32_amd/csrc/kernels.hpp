@@ -49,7 +49,17 @@ struct GemmArgs {
   int ksplit, kper, R;
   float* part;
   int part_bytes;
+  // prefill: the schedule block of this GEMM (kSchedInts ints, see below);
+  // nullptr: eight equal ranges of the tile list and a fixed round robin
+  int32_t* sched;
 };
+// Schedule block of a prefill GEMM: ints [0, 8) the tile counters of the
+// XCDs, [8] the count of finished workgroups (both zero before the launch
+// and zero again after it), [kSchedBounds, kSchedBounds + 9) the first tile
+// of every XCD's range of the tile list (ranges of equal cost) and the end.
+constexpr int kSchedInts = 32;
+constexpr int kSchedCounters = 16;  // the leading ints the place stage zeroes
+constexpr int kSchedBounds = 16;
 
 // K splits of a decode-path GEMM with at most max_tiles tiles of nkb K
 // blocks: with fewer tiles than the chip has workgroup slots (two per CU of
@@ -99,19 +109,27 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, in
                          float* topk_w, int32_t* hist, uint8_t* xq, void* xs, const SmallRoute* sr,
                          hipStream_t stream);
 
+// sched: both GEMMs' schedule blocks (kSchedInts ints each), whose XCD ranges
+// the scan writes: eight ranges of the tile list of equal cost, a tile whose
+// rows fill at most half of its row block counting 2/3 (gate/up) or 1/2
+// (down) of a full tile (half the row waves idle, all the weight loads).
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
-                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream);
+                             int32_t* tile_off0, int32_t* tile_off1, int32_t* sched,
+                             hipStream_t stream);
 
 // After the scan: the row of every (token, slot) pair (rank among the earlier
 // pairs of its router tile with the same expert), and the tile lists of both
 // grouped GEMMs from their per-expert tile offsets (row blocks of bm rows,
 // nt column tiles, grouped kTileGroup column tiles at a time), in one launch.
+// Also zeroes both GEMMs' schedule counters (the first kSchedCounters ints of
+// each schedule block at sched).
 hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
                                      int k, int32_t* row_of, int32_t* row_token, const int32_t* counts,
                                      const int32_t* offsets, const int32_t* tile_off0, int bm0,
                                      int nt0, int max0, int32_t* tiles0, const int32_t* tile_off1,
-                                     int bm1, int nt1, int max1, int32_t* tiles1, hipStream_t stream);
+                                     int bm1, int nt1, int max1, int32_t* tiles1, int32_t* sched,
+                                     hipStream_t stream);
 
 hipError_t launch_combine(const float* Y, const int32_t* row_of, const float* topk_w, int T, int d,
                           int k, uint16_t* out, hipStream_t stream);

@@ -19,7 +19,7 @@ constexpr int64_t kMaxBuffer = int64_t(1) << 31;
 
 struct Layout {
   size_t partial, topk_idx, topk_w, hist, counts, offsets, tile_base, tile_off0, tile_off1, tiles0,
-      tiles1, row_of, row_token, xq, xs, hq, hs, y, kpart, total;
+      tiles1, row_of, row_token, xq, xs, hq, hs, y, kpart, sched, total;
 };
 
 // Decode-path GEMM shapes for T*k = R rows: tile-count bounds and K splits
@@ -73,6 +73,8 @@ Layout make_layout(int64_t T, int64_t d, int64_t f, int64_t E, int64_t k) {
   const DecodeSplit ds = decode_split(R, d, f, E);
   const int64_t kp = ds.sg > 1 || ds.sp > 1 ? std::max<int64_t>(ds.sg * 2 * f, ds.sp * d) : 0;
   l.kpart = put(4 * R * kp);
+  // tile counters of the prefill GEMMs' dynamic schedule (gate/up, down)
+  l.sched = put(4 * 2 * moe::kSchedInts);
   l.total = o;
   return l;
 }
@@ -198,6 +200,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
   void* hs = at(l.hs);
   float* y = reinterpret_cast<float*>(at(l.y));
   float* kpart = reinterpret_cast<float*>(at(l.kpart));
+  int32_t* sched = reinterpret_cast<int32_t*>(at(l.sched));
 
   const int R = T * k;
   const int NT = ceil_div(T, moe::RT_TT);
@@ -230,13 +233,13 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
       case MOE_STAGE_SCAN:
         if (small) break;  // done by the router stage
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
-                                     tile_base, tile_off0, tile_off1, stream);
+                                     tile_base, tile_off0, tile_off1, sched, stream);
         break;
       case MOE_STAGE_PLACE:
         if (small) break;  // done by the router stage
         err = moe::launch_route_place_tables(topk_idx, tile_base, T, E, k, row_of, row_token, counts,
                                              offsets, tile_off0, gs.bm, nt_g, max_g, tiles0, tile_off1,
-                                             ps.bm, nt_p, max_p, tiles1, stream);
+                                             ps.bm, nt_p, max_p, tiles1, sched, stream);
         break;
       case MOE_STAGE_GATEUP: {
         moe::GemmArgs g{};
@@ -267,6 +270,10 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.R = R;
         g.part = kpart;
         g.part_bytes = (int)(4 * (int64_t)ks_g * R * 2 * f);
+        // the scan stage wrote the XCD ranges and the place stage zeroed the
+        // counters (batches of one router tile keep the static schedule: no
+        // scan or place stage)
+        g.sched = small ? nullptr : sched;
         err = moe::launch_gemm_gated(g, decode, fmt, max_g, stream);
         break;
       }
@@ -296,6 +303,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         p.R = R;
         p.part = kpart;
         p.part_bytes = (int)(4 * (int64_t)ks_p * R * d);
+        p.sched = small ? nullptr : sched + moe::kSchedInts;
         err = moe::launch_gemm_plain(p, decode, fmt, max_p, stream);
         break;
       }

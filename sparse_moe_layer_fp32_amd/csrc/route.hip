@@ -43,6 +43,17 @@ __device__ int wave0_exclusive_scan(int* s, int n) {
   return __shfl(incl, 63);
 }
 
+// Cost of an expert's row blocks in one column tile of a prefill GEMM:
+// `full` per row block, `part` for a last block of at most bm/2 rows (the
+// waves of the empty half skip their MFMAs and stores; every weight load
+// runs).  Fitted to the finishing times of the eight XCDs on the skewed
+// prefill layer: such a tile takes 0.67 of a full one in the gate/up GEMM,
+// 0.50 in the down GEMM (whose fp32 output stores halve too).
+__device__ __forceinline__ int tile_cost(int c, int bm, int full_cost, int part_cost) {
+  const int full = c / bm, tail = c - full * bm;
+  return full_cost * full + (tail == 0 ? 0 : 2 * tail <= bm ? part_cost : full_cost);
+}
+
 // One workgroup.  hist[nt][E] holds the expert counts of every router tile.
 __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ hist, int nt,
                                                           int E, int bm0, int ntile0, int bm1,
@@ -50,9 +61,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_base,
                                                           int32_t* __restrict__ tile_off0,
-                                                          int32_t* __restrict__ tile_off1) {
+                                                          int32_t* __restrict__ tile_off1,
+                                                          int32_t* __restrict__ sched) {
   __shared__ int spart[1024];
-  __shared__ int scnt[256], soff[256], st0[256], st1[256];
+  __shared__ int scnt[256], soff[256], st0[256], st1[256], sc0[256], sc1[256];
+  __shared__ int sbound[2][9], scost[2];
   const int tid = threadIdx.x;
   int EP = 1;
   while (EP < E) EP <<= 1;
@@ -89,16 +102,25 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     soff[tid] = c;
     st0[tid] = ceil_div(c, bm0) * ntile0;
     st1[tid] = ceil_div(c, bm1) * ntile1;
+    sc0[tid] = tile_cost(c, bm0, 3, 2) * ntile0;
+    sc1[tid] = tile_cost(c, bm1, 2, 1) * ntile1;
   }
   __syncthreads();
   if (tid < 64) {
     const int tot = wave0_exclusive_scan(soff, E);
     const int t0 = wave0_exclusive_scan(st0, E);
     const int t1 = wave0_exclusive_scan(st1, E);
+    const int c0 = wave0_exclusive_scan(sc0, E);
+    const int c1 = wave0_exclusive_scan(sc1, E);
     if (tid == 0) {
       offsets[E] = tot;
       tile_off0[E] = t0;
       tile_off1[E] = t1;
+      scost[0] = c0;
+      scost[1] = c1;
+      for (int x = 0; x < 8; ++x) sbound[0][x] = sbound[1][x] = 0;  // empty lists
+      sbound[0][8] = t0;
+      sbound[1][8] = t1;
     }
   }
   __syncthreads();
@@ -106,7 +128,26 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     offsets[tid] = soff[tid];
     tile_off0[tid] = st0[tid];
     tile_off1[tid] = st1[tid];
+    // XCD ranges of equal cost: range x starts at the tile where the cost
+    // before it reaches x/8 of the total, inside an expert in proportion to
+    // its tiles (the expert whose cost interval holds the target sets it)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int total = scost[g];
+      const int c0 = g == 0 ? sc0[tid] : sc1[tid];
+      const int ce = (tid + 1 < E ? (g == 0 ? sc0[tid + 1] : sc1[tid + 1]) : total) - c0;
+      const int n = g == 0 ? (tid + 1 < E ? st0[tid + 1] : sbound[0][8]) - st0[tid]
+                           : (tid + 1 < E ? st1[tid + 1] : sbound[1][8]) - st1[tid];
+      const int first = g == 0 ? st0[tid] : st1[tid];
+      for (int x = 1; x < 8; ++x) {
+        const int target = (int)((int64_t)x * total / 8);
+        if (ce > 0 && c0 <= target && target < c0 + ce)
+          sbound[g][x] = first + (int)((int64_t)(target - c0) * n / ce);
+      }
+    }
   }
+  __syncthreads();
+  if (tid < 18) sched[(tid / 9) * kSchedInts + kSchedBounds + tid % 9] = sbound[tid / 9][tid % 9];
   if (e < E) {                           // absolute first row of every (tile, expert)
     int run = soff[e] + spart[tid];
     for (int t0 = lo; t0 < hi; t0 += kBatch) {
@@ -182,10 +223,13 @@ __global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_tables_kernel(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ tile_off0, int bm0, int n_tiles0, int max0, int4* __restrict__ tiles0,
     int g0, const int32_t* __restrict__ tile_off1, int bm1, int n_tiles1, int max1,
-    int4* __restrict__ tiles1, int g1) {
+    int4* __restrict__ tiles1, int g1, int32_t* __restrict__ sched) {
   __shared__ int se[RT_TT * kMaxTopK];
   constexpr int NTH = RT_TT * kMaxTopK;
+  static_assert(2 * kSchedCounters <= NTH, "one counter per thread");
   const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x < 2 * kSchedCounters)
+    sched[(threadIdx.x / kSchedCounters) * kSchedInts + threadIdx.x % kSchedCounters] = 0;
   if (b < nt) {
     place_tile(topk_idx, tile_base, b, T, E, k, row_of, row_token, se);
   } else if (b < nt + g0) {
@@ -241,9 +285,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
-                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream) {
+                             int32_t* tile_off0, int32_t* tile_off1, int32_t* sched,
+                             hipStream_t stream) {
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, ntiles, E, bm0, nt0,
-                     bm1, nt1, counts, offsets, tile_base, tile_off0, tile_off1);
+                     bm1, nt1, counts, offsets, tile_base, tile_off0, tile_off1, sched);
   return hipGetLastError();
 }
 
@@ -251,7 +296,8 @@ hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* til
                                      int k, int32_t* row_of, int32_t* row_token, const int32_t* counts,
                                      const int32_t* offsets, const int32_t* tile_off0, int bm0,
                                      int nt0, int max0, int32_t* tiles0, const int32_t* tile_off1,
-                                     int bm1, int nt1, int max1, int32_t* tiles1, hipStream_t stream) {
+                                     int bm1, int nt1, int max1, int32_t* tiles1, int32_t* sched,
+                                     hipStream_t stream) {
   constexpr int NTH = RT_TT * kMaxTopK;
   const int nt = ceil_div(T, RT_TT);
   const int g0 = max0 > 0 ? std::min(1024, ceil_div(max0, NTH)) : 0;
@@ -259,7 +305,7 @@ hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* til
   hipLaunchKernelGGL(route_place_tables_kernel, dim3(nt + g0 + g1), dim3(NTH), 0, stream, topk_idx,
                      tile_base, T, E, k, row_of, row_token, nt, counts, offsets, tile_off0, bm0, nt0,
                      max0, reinterpret_cast<int4*>(tiles0), g0, tile_off1, bm1, nt1, max1,
-                     reinterpret_cast<int4*>(tiles1), g1);
+                     reinterpret_cast<int4*>(tiles1), g1, sched);
   return hipGetLastError();
 }
 
