@@ -726,7 +726,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 // Schedule: XCD x (workgroups b with b % 8 == x) owns the x-th of eight
 // ranges of the tile list, and workgroup b takes its slot's first two tiles
 // lo + b / 8 and lo + b / 8 + slots.  With g.sched the ranges have equal cost
-// (the scan stage sets them; a tile of at most 96 rows costs 2/3 of a full
+// (the place stage sets them; a tile of at most 96 rows costs 2/3 of a full
 // one in the gate/up GEMM, 1/2 in the down GEMM) instead of equal length, and, with at least 4 K blocks per tile, the
 // rest of a range is handed out in order by an integer counter of its XCD.
 // Tiles take 29-44 us on the skewed prefill layer, and a fixed round robin

@@ -109,21 +109,19 @@ hipError_t launch_router(const uint16_t* x, const float* Wr, const float* br, in
                          float* topk_w, int32_t* hist, uint8_t* xq, void* xs, const SmallRoute* sr,
                          hipStream_t stream);
 
-// sched: both GEMMs' schedule blocks (kSchedInts ints each), whose XCD ranges
-// the scan writes: eight ranges of the tile list of equal cost, a tile whose
-// rows fill at most half of its row block counting 2/3 (gate/up) or 1/2
-// (down) of a full tile (half the row waves idle, all the weight loads).
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
-                             int32_t* tile_off0, int32_t* tile_off1, int32_t* sched,
-                             hipStream_t stream);
+                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream);
 
 // After the scan: the row of every (token, slot) pair (rank among the earlier
 // pairs of its router tile with the same expert), and the tile lists of both
 // grouped GEMMs from their per-expert tile offsets (row blocks of bm rows,
 // nt column tiles, grouped kTileGroup column tiles at a time), in one launch.
-// Also zeroes both GEMMs' schedule counters (the first kSchedCounters ints of
-// each schedule block at sched).
+// Also, in one more workgroup, both GEMMs' schedule blocks at sched: the
+// counters zeroed, and the XCD ranges, eight ranges of the tile list of equal
+// cost, a tile whose rows fill at most half of its row block counting 2/3
+// (gate/up) or 1/2 (down) of a full tile (half the row waves idle, all the
+// weight loads run).
 hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* tile_base, int T, int E,
                                      int k, int32_t* row_of, int32_t* row_token, const int32_t* counts,
                                      const int32_t* offsets, const int32_t* tile_off0, int bm0,

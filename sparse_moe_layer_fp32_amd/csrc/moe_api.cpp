@@ -233,7 +233,7 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
       case MOE_STAGE_SCAN:
         if (small) break;  // done by the router stage
         err = moe::launch_route_scan(hist, NT, E, gs.bm, nt_g, ps.bm, nt_p, counts, offsets,
-                                     tile_base, tile_off0, tile_off1, sched, stream);
+                                     tile_base, tile_off0, tile_off1, stream);
         break;
       case MOE_STAGE_PLACE:
         if (small) break;  // done by the router stage
@@ -270,9 +270,8 @@ moe_status moe_forward_stages(const void* x, const float* W_router, const float*
         g.R = R;
         g.part = kpart;
         g.part_bytes = (int)(4 * (int64_t)ks_g * R * 2 * f);
-        // the scan stage wrote the XCD ranges and the place stage zeroed the
-        // counters (batches of one router tile keep the static schedule: no
-        // scan or place stage)
+        // the place stage wrote the XCD ranges and zeroed the counters
+        // (batches of one router tile keep the static schedule: no place stage)
         g.sched = small ? nullptr : sched;
         err = moe::launch_gemm_gated(g, decode, fmt, max_g, stream);
         break;

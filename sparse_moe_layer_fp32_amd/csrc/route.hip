@@ -17,7 +17,7 @@ namespace moe {
 
 namespace {
 
-// Exclusive scan of n <= 256 ints in LDS by wave 0 (4 per lane); returns the total.
+// Exclusive scan of n <= 256 ints in LDS by one wave (4 per lane); returns the total.
 __device__ int wave0_exclusive_scan(int* s, int n) {
   const int lane = threadIdx.x & 63;
   int v[4], run = 0;
@@ -61,11 +61,9 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ tile_base,
                                                           int32_t* __restrict__ tile_off0,
-                                                          int32_t* __restrict__ tile_off1,
-                                                          int32_t* __restrict__ sched) {
+                                                          int32_t* __restrict__ tile_off1) {
   __shared__ int spart[1024];
-  __shared__ int scnt[256], soff[256], st0[256], st1[256], sc0[256], sc1[256];
-  __shared__ int sbound[2][9], scost[2];
+  __shared__ int scnt[256], soff[256], st0[256], st1[256];
   const int tid = threadIdx.x;
   int EP = 1;
   while (EP < E) EP <<= 1;
@@ -102,25 +100,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     soff[tid] = c;
     st0[tid] = ceil_div(c, bm0) * ntile0;
     st1[tid] = ceil_div(c, bm1) * ntile1;
-    sc0[tid] = tile_cost(c, bm0, 3, 2) * ntile0;
-    sc1[tid] = tile_cost(c, bm1, 2, 1) * ntile1;
   }
   __syncthreads();
   if (tid < 64) {
     const int tot = wave0_exclusive_scan(soff, E);
     const int t0 = wave0_exclusive_scan(st0, E);
     const int t1 = wave0_exclusive_scan(st1, E);
-    const int c0 = wave0_exclusive_scan(sc0, E);
-    const int c1 = wave0_exclusive_scan(sc1, E);
     if (tid == 0) {
       offsets[E] = tot;
       tile_off0[E] = t0;
       tile_off1[E] = t1;
-      scost[0] = c0;
-      scost[1] = c1;
-      for (int x = 0; x < 8; ++x) sbound[0][x] = sbound[1][x] = 0;  // empty lists
-      sbound[0][8] = t0;
-      sbound[1][8] = t1;
     }
   }
   __syncthreads();
@@ -128,26 +117,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
     offsets[tid] = soff[tid];
     tile_off0[tid] = st0[tid];
     tile_off1[tid] = st1[tid];
-    // XCD ranges of equal cost: range x starts at the tile where the cost
-    // before it reaches x/8 of the total, inside an expert in proportion to
-    // its tiles (the expert whose cost interval holds the target sets it)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int total = scost[g];
-      const int c0 = g == 0 ? sc0[tid] : sc1[tid];
-      const int ce = (tid + 1 < E ? (g == 0 ? sc0[tid + 1] : sc1[tid + 1]) : total) - c0;
-      const int n = g == 0 ? (tid + 1 < E ? st0[tid + 1] : sbound[0][8]) - st0[tid]
-                           : (tid + 1 < E ? st1[tid + 1] : sbound[1][8]) - st1[tid];
-      const int first = g == 0 ? st0[tid] : st1[tid];
-      for (int x = 1; x < 8; ++x) {
-        const int target = (int)((int64_t)x * total / 8);
-        if (ce > 0 && c0 <= target && target < c0 + ce)
-          sbound[g][x] = first + (int)((int64_t)(target - c0) * n / ce);
-      }
-    }
   }
-  __syncthreads();
-  if (tid < 18) sched[(tid / 9) * kSchedInts + kSchedBounds + tid % 9] = sbound[tid / 9][tid % 9];
   if (e < E) {                           // absolute first row of every (tile, expert)
     int run = soff[e] + spart[tid];
     for (int t0 = lo; t0 < hi; t0 += kBatch) {
@@ -214,9 +184,58 @@ __device__ void tile_entries(const int32_t* __restrict__ tile_off, const int32_t
   }
 }
 
+// The XCD ranges of both GEMMs' tile lists (sched, kSchedInts ints per
+// GEMM): range x starts at the tile where the cost before it reaches x/8 of
+// the total, inside an expert in proportion to its tiles; and the tile
+// counters zeroed.  One workgroup of >= 256 threads; sc: 512 ints of LDS.
+__device__ void xcd_ranges(const int32_t* __restrict__ counts, const int32_t* __restrict__ tile_off0,
+                           int bm0, int nt0, const int32_t* __restrict__ tile_off1, int bm1, int nt1,
+                           int E, int32_t* __restrict__ sched, int* sc) {
+  __shared__ int sbound[2][9], scost[2];
+  const int tid = threadIdx.x;
+  if (tid < 2 * kSchedCounters)
+    sched[(tid / kSchedCounters) * kSchedInts + tid % kSchedCounters] = 0;
+  if (tid < E) {
+    const int c = counts[tid];
+    sc[tid] = tile_cost(c, bm0, 3, 2) * nt0;
+    sc[256 + tid] = tile_cost(c, bm1, 2, 1) * nt1;
+  }
+  __syncthreads();
+  if (tid < 128) {  // one cost scan per wave
+    const int g = tid >> 6;
+    const int total = wave0_exclusive_scan(sc + 256 * g, E);
+    if ((tid & 63) == 0) {
+      scost[g] = total;
+      for (int x = 0; x < 8; ++x) sbound[g][x] = 0;  // empty lists
+      sbound[g][8] = (g == 0 ? tile_off0 : tile_off1)[E];
+    }
+  }
+  __syncthreads();
+  if (tid < E) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int32_t* toff = g == 0 ? tile_off0 : tile_off1;
+      const int total = scost[g];
+      const int c0 = sc[256 * g + tid];
+      const int ce = (tid + 1 < E ? sc[256 * g + tid + 1] : total) - c0;
+      const int first = toff[tid], n = toff[tid + 1] - first;
+      for (int x = 1; x < 8; ++x) {
+        const int target = x * (total >> 3) + ((x * (total & 7)) >> 3);  // x * total / 8
+        // in float: a range start needs no more than tile precision, and any
+        // start inside the expert's tiles keeps every tile in one range
+        if (ce > 0 && c0 <= target && target < c0 + ce)
+          sbound[g][x] = first + min(n - 1, (int)((float)(target - c0) * (float)n / (float)ce));
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < 18) sched[(tid / 9) * kSchedInts + kSchedBounds + tid % 9] = sbound[tid / 9][tid % 9];
+}
+
 // After the scan, in one launch: workgroups [0, nt) place router tile
-// blockIdx.x, the next g0 build the gate/up GEMM's tile list and the last g1
-// the down GEMM's (the three only read the scan's results).
+// blockIdx.x, the next g0 build the gate/up GEMM's tile list, the next g1 the
+// down GEMM's, and the last one the GEMMs' XCD ranges (all only read the
+// scan's results).
 __global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_tables_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ tile_base, int T, int E, int k,
     int32_t* __restrict__ row_of, int32_t* __restrict__ row_token, int nt,
@@ -226,18 +245,18 @@ __global__ __launch_bounds__(RT_TT * kMaxTopK) void route_place_tables_kernel(
     int4* __restrict__ tiles1, int g1, int32_t* __restrict__ sched) {
   __shared__ int se[RT_TT * kMaxTopK];
   constexpr int NTH = RT_TT * kMaxTopK;
-  static_assert(2 * kSchedCounters <= NTH, "one counter per thread");
+  static_assert(2 * kSchedCounters <= NTH && NTH >= kMaxExperts && NTH >= 512, "xcd_ranges");
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x < 2 * kSchedCounters)
-    sched[(threadIdx.x / kSchedCounters) * kSchedInts + threadIdx.x % kSchedCounters] = 0;
   if (b < nt) {
     place_tile(topk_idx, tile_base, b, T, E, k, row_of, row_token, se);
   } else if (b < nt + g0) {
     tile_entries(tile_off0, counts, offsets, E, bm0, n_tiles0, max0, tiles0, (b - nt) * NTH + threadIdx.x,
                  g0 * NTH);
-  } else {
+  } else if (b < nt + g0 + g1) {
     tile_entries(tile_off1, counts, offsets, E, bm1, n_tiles1, max1, tiles1,
                  (b - nt - g0) * NTH + threadIdx.x, g1 * NTH);
+  } else {
+    xcd_ranges(counts, tile_off0, bm0, n_tiles0, tile_off1, bm1, n_tiles1, E, sched, se);
   }
 }
 
@@ -285,10 +304,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 hipError_t launch_route_scan(const int32_t* hist, int ntiles, int E, int bm0, int nt0, int bm1,
                              int nt1, int32_t* counts, int32_t* offsets, int32_t* tile_base,
-                             int32_t* tile_off0, int32_t* tile_off1, int32_t* sched,
-                             hipStream_t stream) {
+                             int32_t* tile_off0, int32_t* tile_off1, hipStream_t stream) {
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, ntiles, E, bm0, nt0,
-                     bm1, nt1, counts, offsets, tile_base, tile_off0, tile_off1, sched);
+                     bm1, nt1, counts, offsets, tile_base, tile_off0, tile_off1);
   return hipGetLastError();
 }
 
@@ -302,7 +320,7 @@ hipError_t launch_route_place_tables(const int32_t* topk_idx, const int32_t* til
   const int nt = ceil_div(T, RT_TT);
   const int g0 = max0 > 0 ? std::min(1024, ceil_div(max0, NTH)) : 0;
   const int g1 = max1 > 0 ? std::min(1024, ceil_div(max1, NTH)) : 0;
-  hipLaunchKernelGGL(route_place_tables_kernel, dim3(nt + g0 + g1), dim3(NTH), 0, stream, topk_idx,
+  hipLaunchKernelGGL(route_place_tables_kernel, dim3(nt + g0 + g1 + 1), dim3(NTH), 0, stream, topk_idx,
                      tile_base, T, E, k, row_of, row_token, nt, counts, offsets, tile_off0, bm0, nt0,
                      max0, reinterpret_cast<int4*>(tiles0), g0, tile_off1, bm1, nt1, max1,
                      reinterpret_cast<int4*>(tiles1), g1, sched);
