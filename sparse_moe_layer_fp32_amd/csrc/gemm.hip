@@ -1042,12 +1042,16 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
       xsc[mb] = static_cast<int>((mb < 4 ? sl[mb] : (mb == 4 ? sh.x : sh.y)) >> (8 * gq));
     v8i xf[2];
     xf[0] = a_frag(abase, 0);
-    const uint8_t* wsc = abase + W_SA + W_SIDE_BS + MX_PITCH * gq + l16;
     int wsv[NB];
     v8i wf[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      wsv[nb] = wsc[16 * b_tseg(nb)];
+      {  // the byte through its aligned dword: byte loads lost their LDS alias scope
+         // in code generation, and with it the compiler waited for every stage load
+        const int o = 16 * b_tseg(nb) + (int)(MX_PITCH * gq + l16);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(abase + W_SA + W_SIDE_BS + (o & ~3));
+        wsv[nb] = (int)((w >> (8 * (o & 3))) & 0xffu);
+      }
       wf[nb] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int r = 0; r < (FP4 ? 2 : 4); ++r) {  // FP4: stored rows 16gq + 8r + l16/2
