@@ -68,27 +68,27 @@ ATTN_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "attention.hi
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c4b": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 2807640.138, "write_kib": 215672.731,
-        "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
-    "c1": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 271558.513, "write_kib": 759.200,
+    "c4b": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 2277340.792, "write_kib": 210405.859,
+        "copy_fetch_kib": 524317.0, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 271558.375, "write_kib": 759.406,
         "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 914708.075, "write_kib": 103844.750,
-        "copy_fetch_kib": 524306.9375, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 279948.675, "write_kib": 760.850,
-        "copy_fetch_kib": 524308.1875, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 941394.850, "write_kib": 103776.081,
-        "copy_fetch_kib": 524307.1875, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 144511.550, "write_kib": 759.156,
-        "copy_fetch_kib": 524312.0625, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "e8e4fe01dfc16991a6691715f051c850590b869686a6e6088052e7d4d163489d",
-        "fetch_kib": 575881.625, "write_kib": 103791.325,
-        "copy_fetch_kib": 524305.875, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 865696.698, "write_kib": 104167.776,
+        "copy_fetch_kib": 524306.6875, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 279948.448, "write_kib": 761.302,
+        "copy_fetch_kib": 524306.8125, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 888787.688, "write_kib": 104099.245,
+        "copy_fetch_kib": 524307.5, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 144511.385, "write_kib": 759.177,
+        "copy_fetch_kib": 524311.4375, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "1292381fdcc2aa660cf374da7de9740a3e157e0b5b56454a7c920cdd4ff2f26a",
+        "fetch_kib": 526596.115, "write_kib": 104071.953,
+        "copy_fetch_kib": 524304.375, "copy_write_kib": 1048576.0},
 }
 
 
