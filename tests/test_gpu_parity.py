@@ -97,6 +97,33 @@ def test_small_shapes_vs_oracle(shape, path, fmt):
          f"down-stage err/bound {worst:.3f}")
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_tile_counter_schedule_vs_oracle(fmt):
+    """Prefill GEMMs whose tile lists outgrow the static first two tiles of
+    every workgroup (2 x 256), with at least 4 K blocks per tile: the rest is
+    handed out by the per-XCD tile counters, inside XCD ranges of equal cost.
+    A Zipf-skewed 256-expert layer gives 272 row blocks, most of them short
+    (1088 gate/up and 816 down tiles); the down GEMM has exactly 4 K blocks,
+    where a fetched tile index is read in the step that uses it.  Every token
+    against the oracle: a tile computed twice or never would show."""
+    layer = gen.custom_layer(768, 512, 256, 8, layer_id=7000, router="zipf")
+    inp = gen.make_inputs(layer, T=1024, fmt=fmt)
+    ref = parity.oracle_ref(inp)
+    rows = np.diff(ref["offsets"])
+    blocks = int(sum(-(-int(c) // 192) for c in rows))
+    assert blocks * (512 // 128) > 512 and blocks * (768 // 256) > 512, blocks
+    _say(f"[schedule] fmt={fmt} row blocks {blocks}")
+    dbg = run_debug(inp, "prefill")
+    parity.check_routing(dbg, ref, inp["T"], inp["k"])
+    parity.check_xquant(dbg, ref["xq"], ref["xs"])
+    nflip, ncodes = parity.check_h_decisions(dbg, ref, fmt)
+    worst = parity.check_down_stage(dbg, ref, inp, inp["d_real"])
+    parity.check_combine_stage(dbg)
+    g = parity.bf16_to_f64(dbg["out"])
+    m = parity.check_end_to_end(g, dbg, ref, inp, inp["d_real"])
+    _say(f"   out {m}\n   h flips {nflip}/{ncodes}; down-stage err/bound {worst:.3f}")
+
+
 # Decode batches with fewer GEMM tiles than the chip's workgroup slots: both
 # decode GEMMs cut every tile into K ranges (split K), write fp32 partial sums
 # and a finish kernel adds them in split order before the epilogue.
