@@ -35,18 +35,28 @@ def _bits(t):
     return t.view(torch.int16)
 
 
-@pytest.mark.parametrize("cfg", ["c0", "c1"])
+def _graph_inputs(case, fmt):
+    if case == "schedule":  # prefill tile lists that go through the per-XCD tile counters
+        layer = gen.custom_layer(768, 512, 256, 8, layer_id=7000, router="zipf")
+        return gen.make_inputs(layer, T=1024, fmt=fmt), "prefill"
+    return gen.make_inputs(case, fmt=fmt), "auto"
+
+
+@pytest.mark.parametrize("cfg", ["c0", "c1", "schedule"])
 @pytest.mark.parametrize("fmt", ["block128", "mx"])
 def test_graph_capture_replays_bit_equal(cfg, fmt):
+    """c0 and c1: one-router-tile batches; "schedule": a prefill batch whose
+    GEMM tile counters the place stage zeroes and the last workgroup zeroes
+    again in every replay."""
     _say(f"[graph] {cfg} {fmt}")
-    inp = gen.make_inputs(cfg, fmt=fmt)
+    inp, path = _graph_inputs(cfg, fmt)
     p = moe.device_inputs(inp)
     blk = moe.MoeBlock(p)
     T, d = inp["T"], inp["d"]
     x = p["x"].clone()
     ws = blk.workspace(T)
     out_eager = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
-    blk(x, out=out_eager)                       # eager warm-up
+    blk(x, out=out_eager, path=path)            # eager warm-up
     torch.cuda.synchronize()
     ref = out_eager.clone()
 
@@ -55,11 +65,11 @@ def test_graph_capture_replays_bit_equal(cfg, fmt):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        blk(x, out=out_g)                       # warm-up on the capture stream's side
+        blk(x, out=out_g, path=path)            # warm-up on the capture stream's side
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        blk(x, out=out_g)
+        blk(x, out=out_g, path=path)
     assert blk.workspace(T) is ws               # the captured workspace is the one in use
 
     for rep in range(3):
@@ -69,13 +79,13 @@ def test_graph_capture_replays_bit_equal(cfg, fmt):
         torch.cuda.synchronize()
         assert torch.equal(_bits(out_g), _bits(ref)), f"replay {rep} differs from the eager call"
         out_eager.fill_(0)
-        blk(x, out=out_eager)                   # eager work between replays
+        blk(x, out=out_eager, path=path)        # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(_bits(out_eager), _bits(ref))
 
     # new token values in the captured input buffer: the replay recomputes
     x2 = torch.roll(p["x"], shifts=1, dims=0).contiguous()
-    ref2 = blk(x2, out=torch.empty_like(out_eager)).clone()
+    ref2 = blk(x2, out=torch.empty_like(out_eager), path=path).clone()
     torch.cuda.synchronize()
     x.copy_(x2)
     graph.replay()
