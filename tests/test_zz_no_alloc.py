@@ -58,6 +58,18 @@ def test_noalloc_decode_and_prefill_paths():
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), path
 
 
+def test_noalloc_prefill_tile_counters():
+    """A prefill batch whose GEMM tile lists go through the per-XCD tile
+    counters (35 MiB of workspace): the counters sit in the shared array and
+    must start every call at zero; two calls in a row, the second smaller."""
+    layer = gen.custom_layer(768, 512, 256, 8, layer_id=7000, router="zipf")
+    for T in (1024, 600):
+        _say(f"[noalloc] tile counters T={T}")
+        p = moe.device_inputs(gen.make_inputs(layer, T=T))
+        ref, out, _, _ = _pair(p, "block128", "prefill")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), T
+
+
 def test_noalloc_refuses_sizes_beyond_the_scratch():
     # the prefill-shaped layer needs far more than 64 MiB of workspace: refused on the host
     T, d, f, E, k = 8192, 2944, 2944, 32, 4
