@@ -727,16 +727,18 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 // ranges of the tile list, and workgroup b takes its slot's first two tiles
 // lo + b / 8 and lo + b / 8 + slots.  With g.sched the ranges have equal cost
 // (the place stage sets them; a tile of at most 96 rows costs 2/3 of a full
-// one in the gate/up GEMM, 1/2 in the down GEMM) instead of equal length, and, with at least 4 K blocks per tile, the
-// rest of a range is handed out in order by an integer counter of its XCD.
+// one in the gate/up GEMM, 1/2 in the down GEMM) instead of equal length,
+// and, with at least 3 K blocks per tile, the rest of a range is handed out
+// in order by an integer counter of its XCD.
 // Tiles take 29-44 us on the skewed prefill layer, and a fixed round robin
 // over equal lengths left the workgroups of an XCD up to five tiles apart at
 // the end and the XCDs up to 150 us apart (the range that holds only full
 // tiles of the hottest expert against one with 329 short tiles).  A tile
-// index is fetched two tiles ahead: wave 0 adds to the counter after the ring
-// barrier of a tile's first K block, stores the index in LDS in the second
-// (its ring wait covers the atomic) and every wave reads it in the third.
-// Which workgroup computes a tile does not change any result.  The last
+// index is fetched two tiles ahead, only where a cursor changes tiles (no
+// per-step state): wave 0 adds to the counter as the compute cursor enters a
+// tile, stores the index in LDS as the weight cursor leaves it and every wave
+// reads it as the activation cursor does.  Which workgroup computes a tile
+// does not change any result.  The last
 // workgroup to finish zeroes the counters again.
 // Global -> LDS loads through the compiler's builtin (the instruction of
 // dma16 / dma4), for the kernel below.  Every ring stage there is a
@@ -801,7 +803,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   }
   const int chunk = hi - lo;
   const int L0 = lo + (blockIdx.x >> 3);
-  const bool dyn = sched != nullptr && nkb >= 4;
+  const bool dyn = sched != nullptr && nkb >= 3;
   // the last workgroup to finish (every fetch of every workgroup has returned
   // by then) zeroes the counters for the next launch
   auto finish = [&]() {
@@ -838,22 +840,21 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   DmaTile tb = ta;
   uint32_t boff[BQ];
   __amdgpu_buffer_rsrc_t rB;
-  // ---- dynamic schedule: in the first K block of every tile wave 0 fetches
-  // the tile after the next one (while the last index fetched was a tile),
-  // stores it in snext in the second K block (the ring wait of that block
-  // covers the atomic, so no further wait), and every wave reads it in the
-  // third, before the A cursor, one K block ahead, moves to the next tile at
-  // the end of block nkb - 2 (hence nkb >= 4)
+  // ---- dynamic schedule, in the cursors' tile moves only.  When the compute
+  // cursor enters tile Y (in the prologue: the first tile) and Y's successor
+  // Z is a tile, wave 0 adds to its XCD's counter for the tile after Z.  When
+  // the B cursor moves from Y to Z, at least one step later (nkb >= 3), wave 0
+  // stores the index in snext: the compiler's wait for the atomic there asks
+  // less than the ring wait that follows (the atomic is older than the step's
+  // own loads).  One step later, past a ring barrier, the A cursor moves from
+  // Y to Z and every wave reads snext as the tile after Z.
   __shared__ int32_t snext;
-  int tkt = 0, Lnext = L0;
-  // after the ring barrier
-  auto fetch_begin = [&](int kb) {
-    if (dyn && kb == 2 && Lnext < hi) Lnext = __builtin_amdgcn_readfirstlane(snext);
-    if (dyn && kb == 0 && Lnext < hi && wave == 0 && lane == 0) tkt = atomicAdd(&sched[xcd], 1);
+  int tkt = 0;
+  auto fetch = [&]() {
+    if (dyn && Lan < hi && wave == 0 && lane == 0) tkt = atomicAdd(&sched[xcd], 1);
   };
-  // after the MFMAs
-  auto fetch_end = [&](int kb) {
-    if (dyn && kb == 1 && Lnext < hi && wave == 0) {
+  auto fetch_store = [&]() {
+    if (dyn && Lan < hi && wave == 0) {
       // a count outside [0, chunk) (counters not zeroed) reads as the end
       if (lane == 0) snext = (tkt >= 0 && tkt < chunk) ? lo + 2 * nslots + tkt : hi;
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the store is done before the barrier
@@ -954,6 +955,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   auto advance_b = [&]() {
     if (kbb < nkb) return;
     kbb = 0;
+    fetch_store();
     Lb = dyn ? Lan : Lb + nslots;  // the A cursor is one K block behind: its next tile
     if (Lb < hi) {
       tb = dma_tile(g, Lb);
@@ -969,7 +971,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     La = Lan;
     ta = tan;
     rb ^= 1;
-    Lan = dyn ? Lnext : Lan + nslots;
+    Lan = __builtin_amdgcn_readfirstlane(!dyn ? Lan + nslots : La < hi ? snext : hi);
     if (Lan < hi) tan = dma_tile(g, Lan);
     if (nkb == 1) {  // the row tokens were loaded one K block ago: wait for them
       wait_vmcnt<0>();
@@ -1274,8 +1276,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     asm volatile("" ::: "memory");
   };
 
-  // ---- prologue: row tokens of the first two tiles, then B of K blocks 0
-  // and 1 and A of K block 0 (the B stages are older than the A stage)
+  // ---- prologue: the successor of the second tile, row tokens of the first
+  // two tiles, then B of K blocks 0 and 1 and A of K block 0 (the B stages
+  // are older than the A stage)
+  fetch();
   rt_load(ta, true, 0);
   rt_load(tan, Lan < hi, 1);
   if constexpr (GATED) {
@@ -1296,11 +1300,9 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   // block i + 1 and B of block i + 2.  Returns false after the last tile.
   auto step = [&](const uint8_t* ca, uint8_t* na, const uint8_t* cb, uint8_t* nb2) -> bool {
     wait_stage(pend);
-    fetch_begin(kbc);
     issue_a(na);
     if constexpr (MX) compute_mx(ca, cb);
     else compute(ca, cb);
-    fetch_end(kbc);
     issue_b(nb2);
     pend = advance_a();
     advance_b();
@@ -1309,6 +1311,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     pend += ST;
     Lc = dyn ? La : Lc + nslots;  // the A cursor moved to the next tile one step ago
     if (Lc >= hi) return false;
+    fetch();
     kbc = 0;
     tc = dma_tile(g, Lc);
     return true;

@@ -97,22 +97,25 @@ def test_small_shapes_vs_oracle(shape, path, fmt):
          f"down-stage err/bound {worst:.3f}")
 
 
+@pytest.mark.parametrize("d,f", [(768, 512), (384, 384)])
 @pytest.mark.parametrize("fmt", FMTS)
-def test_tile_counter_schedule_vs_oracle(fmt):
+def test_tile_counter_schedule_vs_oracle(fmt, d, f):
     """Prefill GEMMs whose tile lists outgrow the static first two tiles of
-    every workgroup (2 x 256), with at least 4 K blocks per tile: the rest is
+    every workgroup (2 x 256), with at least 3 K blocks per tile: the rest is
     handed out by the per-XCD tile counters, inside XCD ranges of equal cost.
-    A Zipf-skewed 256-expert layer gives 272 row blocks, most of them short
-    (1088 gate/up and 816 down tiles); the down GEMM has exactly 4 K blocks,
-    where a fetched tile index is read in the step that uses it.  Every token
-    against the oracle: a tile computed twice or never would show."""
-    layer = gen.custom_layer(768, 512, 256, 8, layer_id=7000, router="zipf")
+    A Zipf-skewed 256-expert layer gives about 270 row blocks, most of them
+    short.  With d = 768, f = 512 the gate/up GEMM has 6 K blocks and the down
+    GEMM 4; with d = f = 384 both have 3, the fewest the counters serve, where
+    the index fetched for a tile is stored one step after the atomic and read
+    in the next (and the down GEMM's last column tile is half wide).  Every
+    token against the oracle: a tile computed twice or never would show."""
+    layer = gen.custom_layer(d, f, 256, 8, layer_id=7000, router="zipf")
     inp = gen.make_inputs(layer, T=1024, fmt=fmt)
     ref = parity.oracle_ref(inp)
     rows = np.diff(ref["offsets"])
     blocks = int(sum(-(-int(c) // 192) for c in rows))
-    assert blocks * (512 // 128) > 512 and blocks * (768 // 256) > 512, blocks
-    _say(f"[schedule] fmt={fmt} row blocks {blocks}")
+    assert blocks * (f // 128) > 512 and blocks * -(-d // 256) > 512, blocks
+    _say(f"[schedule] fmt={fmt} d={d} f={f} row blocks {blocks}")
     dbg = run_debug(inp, "prefill")
     parity.check_routing(dbg, ref, inp["T"], inp["k"])
     parity.check_xquant(dbg, ref["xq"], ref["xs"])
