@@ -16,7 +16,8 @@ codes and scales are compared on every token and are bit-identical on every
 row below.  The expert math is compared on `tokens` sampled tokens: 160 seeded
 random ones, the first and last token, and the tokens of the first and last
 row of every expert's last row tile for 32- and 192-row tiles (the ragged
-tails of both GEMMs' tile lists).
+tails of both GEMMs' tile lists).  A row whose token count is the config's T
+checks the expert math on every row and token.
 
 Columns, with o the oracle's unrounded fp64 output and g the GPU's bf16 output
 over the real columns of the sampled tokens:
