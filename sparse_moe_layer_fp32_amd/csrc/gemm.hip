@@ -771,7 +771,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   constexpr int BQ = SB / 1024 / DMA_WAVES;          // B chunks (1 KB) per wave
   constexpr int MB = W_HALF / 16, NB = 4;            // 16 x 16 blocks per wave: 6 x 4
   constexpr int RT = GATED ? 1 : 0;                  // row-token loads per A-cursor tile move
-  constexpr int ST = GATED ? MB * 3 : MB * NB;       // epilogue stores per wave
+  constexpr int ST = GATED ? MB * 3 : MB * NB;       // epilogue stores per wave with rows
   constexpr int ASTAGE = MX ? W_SA + W_SIDE_BS + 4 * MX_PITCH : W_ASTAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[ASTAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[ASTAGE];
@@ -1125,7 +1125,20 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
   };
 
   // lane -> rows 96 wm + 16 mb + l16, columns 4 gq.. of each 16-column block
-  auto epilogue = [&](const DmaTile& t, const uint8_t* abase) {
+  // Returns the number of stores issued (the ring waits count them).
+  auto epilogue = [&](const DmaTile& t, const uint8_t* abase) -> int {
+    // A wave whose row half holds no valid row (a tile of at most 96 rows)
+    // has nothing to write: its MFMAs were skipped, so its accumulators are
+    // still zero.  It only joins the row-maximum barrier of the block-scaled
+    // gated epilogue, which every wave passes once per tile.
+    if (wm == 1 && t.valid <= W_HALF) {
+      if constexpr (GATED && !MX) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      return 0;
+    }
     const int n0 = t.nt * (GATED ? kBlock : WN_COLS);
     const uint8_t* sbias = abase + W_SA + W_SIDE_BIAS;
     if constexpr (MX) {
@@ -1260,11 +1273,13 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
           for (int i = 0; i < 4; ++i) acc[mb][nb][i] = 0.f;
         }
       }
+    return ST;
   };
 
   // Ring wait: this wave's loads of the A stage about to be read (and, older,
   // of the B stage) are done; younger are the next B stage's BQ loads and
-  // `pend` row-token loads and epilogue stores.  Then a bare s_barrier.
+  // `pend` row-token loads and epilogue stores (none from a wave without
+  // rows in the tile).  Then a bare s_barrier.
   auto wait_stage = [&](int pend) {
     if (pend == 0) wait_vmcnt<BQ>();
     else if (pend == RT) wait_vmcnt<BQ + RT>();
@@ -1307,8 +1322,7 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_wide_kernel(Ge
     pend = advance_a();
     advance_b();
     if (++kbc < nkb) return true;
-    epilogue(tc, ca);
-    pend += ST;
+    pend += epilogue(tc, ca);
     Lc = dyn ? La : Lc + nslots;  // the A cursor moved to the next tile one step ago
     if (Lc >= hi) return false;
     fetch();
