@@ -68,27 +68,27 @@ ATTN_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "attention.hi
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c4b": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 2290148.875, "write_kib": 210732.458,
-        "copy_fetch_kib": 524311.9375, "copy_write_kib": 1048576.0},
-    "c1": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 271558.292, "write_kib": 759.297,
-        "copy_fetch_kib": 524308.25, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 883622.396, "write_kib": 104177.219,
-        "copy_fetch_kib": 524308.125, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 279948.469, "write_kib": 761.714,
-        "copy_fetch_kib": 524307.4375, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 885083.312, "write_kib": 104213.396,
-        "copy_fetch_kib": 524306.3125, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 144511.344, "write_kib": 759.177,
-        "copy_fetch_kib": 524312.1875, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "5cd8755238bdb35fa1fd9780e2eff18d9954e5b1017f600a3b77e57adf60295f",
-        "fetch_kib": 538280.667, "write_kib": 104171.458,
-        "copy_fetch_kib": 524305.625, "copy_write_kib": 1048576.0},
+    "c4b": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 2348308.521, "write_kib": 210638.406,
+        "copy_fetch_kib": 524315.3125, "copy_write_kib": 1048576.0},
+    "c1": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 271558.396, "write_kib": 759.208,
+        "copy_fetch_kib": 524307.5, "copy_write_kib": 1048576.0},
+    "c2": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 905262.146, "write_kib": 104102.63,
+        "copy_fetch_kib": 524307.0, "copy_write_kib": 1048576.0},
+    "c1-mx": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 279948.531, "write_kib": 761.156,
+        "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
+    "c2-mx": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 909948.875, "write_kib": 104154.87,
+        "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
+    "c1-mxfp4": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 144511.323, "write_kib": 759.156,
+        "copy_fetch_kib": 524313.125, "copy_write_kib": 1048576.0},
+    "c2-mxfp4": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+        "fetch_kib": 552645.885, "write_kib": 104099.526,
+        "copy_fetch_kib": 524305.375, "copy_write_kib": 1048576.0},
 }
 
 
