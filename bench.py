@@ -68,25 +68,25 @@ ATTN_SRC = os.path.join(ROOT, "sparse_moe_layer_fp32_amd", "csrc", "attention.hi
 # kernels reports null until they are measured again.  Keys: workload, or
 # workload-mx for the MXFP8 format.
 TRAFFIC = {
-    "c4b": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c4b": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 2348308.521, "write_kib": 210638.406,
         "copy_fetch_kib": 524315.3125, "copy_write_kib": 1048576.0},
-    "c1": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c1": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 271558.396, "write_kib": 759.208,
         "copy_fetch_kib": 524307.5, "copy_write_kib": 1048576.0},
-    "c2": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c2": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 905262.146, "write_kib": 104102.63,
         "copy_fetch_kib": 524307.0, "copy_write_kib": 1048576.0},
-    "c1-mx": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c1-mx": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 279948.531, "write_kib": 761.156,
         "copy_fetch_kib": 524307.6875, "copy_write_kib": 1048576.0},
-    "c2-mx": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c2-mx": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 909948.875, "write_kib": 104154.87,
         "copy_fetch_kib": 524307.625, "copy_write_kib": 1048576.0},
-    "c1-mxfp4": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c1-mxfp4": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 144511.323, "write_kib": 759.156,
         "copy_fetch_kib": 524313.125, "copy_write_kib": 1048576.0},
-    "c2-mxfp4": {"gemm_sha256": "bd8cfa7f1d7ed668e848c4f43e11673102bfb445ac62649191bc11f6a8c91796",
+    "c2-mxfp4": {"gemm_sha256": "376c0a3adadda0ea029a814fc7ac8d4b51cf7e183117f09f550855471b4b7dc7",
         "fetch_kib": 552645.885, "write_kib": 104099.526,
         "copy_fetch_kib": 524305.375, "copy_write_kib": 1048576.0},
 }

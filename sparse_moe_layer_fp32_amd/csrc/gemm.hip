@@ -718,10 +718,10 @@ __global__ __launch_bounds__(DMA_WAVES * 64, 1) void grouped_gemm_dma_kernel(Gem
 // rounding).
 //
 // Rows: waves wm = 0 / 1 own tile rows 0-95 / 96-191; a wave whose half has
-// no valid row skips its MFMAs, so a ragged tail tile of <= 96 rows costs
-// about half a tile.  Persistent over the tile list; the loads run ahead
-// across tile boundaries (the next tile's first blocks load while the
-// current tile ends).
+// no valid row skips its MFMAs and its epilogue, so a ragged tail tile of
+// <= 96 rows costs about half a tile.  Persistent over the tile list; the
+// loads run ahead across tile boundaries (the next tile's first blocks load
+// while the current tile ends).
 //
 // Schedule: XCD x (workgroups b with b % 8 == x) owns the x-th of eight
 // ranges of the tile list, and workgroup b takes its slot's first two tiles
