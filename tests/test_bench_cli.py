@@ -91,3 +91,18 @@ def test_prefill_attention_writes_each_output_once():
     assert t["write_kib"] * 1024 == out
     read = t["fetch_kib"] * (1 << 20) / t["copy_fetch_kib"] * 1024
     assert read >= out + 2 * 8192 * 8 * 64 * 2
+
+
+def test_stored_counters_are_keyed_to_the_present_sources():
+    """The bench line reports stored HBM counters only while the kernel source
+    they were taken on is unchanged, so every committed entry must be keyed to
+    the present source: a change to the GEMM or attention source (a comment
+    included) needs the counter runs again, or, for a byte-identical build,
+    the entries moved to the new hash."""
+    b = _bench()
+    gemm = b.gemm_src_sha()
+    for key, t in b.TRAFFIC.items():
+        assert t["gemm_sha256"] == gemm, key
+    attn = b.src_sha(b.ATTN_SRC)
+    for key, t in b.ATTN_TRAFFIC.items():
+        assert t["attn_sha256"] == attn, key
